@@ -1,0 +1,300 @@
+/*
+ * qgemm_oracle.c -- plain CPU oracle for the quantized GEMM / conv path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It
+ * shares no code, header or table with the HIP library and includes no HIP
+ * header.
+ *
+ * Sources of the definitions (web pages; section numbers are the pages' own):
+ *   [INT4-GEMM]  "DeepGEMM" INT4 GEMM article, www.cf-1.com/news/6060138
+ *                  §2.1 (two signed nibbles per byte), §3.2 (C = A*B with
+ *                  packed INT4 in, INT32 out), §4.3 (B stored column-major).
+ *   [MCU-CONV]   smart-speaker MCU conv front-end article,
+ *                news.rkmt.cn/news/16638
+ *                  §2.1 (output geometry and MAC count), §2.3 (Q31
+ *                  requantize: 64-bit product, add half an LSB, arithmetic
+ *                  shift, saturate; symmetric zero point 0; padding equals
+ *                  the zero point), §3.1 (NHWC activations, weights
+ *                  [out][kh][kw][in]), §3.2 (conv as C = A x B over an
+ *                  im2col matrix), §3.3 (bias enters the requantize step).
+ *
+ * Readings where the pages are silent or contradict themselves:
+ *   - packed INT4: element 2i is the LOW nibble of byte i, element 2i+1 the
+ *     high nibble; codes are 4-bit two's complement (0x8 = -8).
+ *   - bias is added to the int32 accumulator before the Q31 multiply.
+ *   - ">>" on a negative int64 is an arithmetic (flooring) shift.  GCC
+ *     documents this for signed right shifts; the oracle is built with gcc.
+ *   - requant domain: acc + bias fits int32, mult in [0, 2^31-1],
+ *     shift in [1, 63]; outside it the oracle reports ORC_E_DOMAIN/RANGE
+ *     instead of producing a value.
+ *   - GEMM layouts: A is [M][lda] row-major, B is [N][ldb] (K contiguous,
+ *     i.e. column-major K x N); packed operands count lda/ldb in nibbles.
+ *   - conv: NHWC input, OHWI weights, dilation 1, one group, symmetric
+ *     padding filled with 0, floor output-size formula.
+ *
+ * Every entry point can compute a subset of output rows (GEMM) or output
+ * pixels (conv) so that full-size problems can be checked on samples; the
+ * selected results are written compactly, row r of the output holding the
+ * r-th requested row/pixel.  OpenMP only spreads independent output rows
+ * over threads; every dot product is summed in one thread, in k order.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <omp.h>
+
+#define ORC_OK 0
+#define ORC_E_RANGE 1   /* an int32 intermediate does not fit in int32 */
+#define ORC_E_DOMAIN 2  /* shift or multiplier outside the stated domain */
+
+/* ---- O1: packed INT4 element access ([INT4-GEMM] §2.1, §3.2) ---- */
+int orc_int4_at(const uint8_t *row, int64_t i)
+{
+    uint8_t byte = row[i / 2];
+    int code = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return code < 8 ? code : code - 16;
+}
+
+/* ---- O3: Q31 requantize ([MCU-CONV] §2.3, bias per §3.3) ---- */
+int orc_requant(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int8_t *out)
+{
+    int64_t x = acc + (int64_t)bias;
+    if (x < INT32_MIN || x > INT32_MAX)
+        return ORC_E_RANGE;
+    if (shift < 1 || shift > 63 || mult < 0)
+        return ORC_E_DOMAIN;
+    int64_t t = x * (int64_t)mult;          /* |t| < 2^62 */
+    t = t + ((int64_t)1 << (shift - 1));    /* half an LSB */
+    t = t >> shift;                         /* arithmetic shift (gcc) */
+    if (t > 127)
+        t = 127;
+    if (t < -128)
+        t = -128;
+    *out = (int8_t)t;
+    return ORC_OK;
+}
+
+/* ---- O2: plain dot products over K, int64 sums ---- */
+static int64_t dot_s8_s8(const int8_t *a, const int8_t *b, int64_t K)
+{
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += (int64_t)a[k] * (int64_t)b[k];
+    return acc;
+}
+
+static int64_t dot_s4_s4(const uint8_t *a, const uint8_t *b, int64_t K)
+{
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += (int64_t)orc_int4_at(a, k) * (int64_t)orc_int4_at(b, k);
+    return acc;
+}
+
+static int64_t dot_s8_s4(const int8_t *a, const uint8_t *b, int64_t K)
+{
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += (int64_t)a[k] * (int64_t)orc_int4_at(b, k);
+    return acc;
+}
+
+/* kinds of operand: 8 = int8 bytes, 4 = packed signed int4 (ld in nibbles) */
+static int64_t dot_any(int ka, const void *A, int64_t lda, int64_t m,
+                       int kb, const void *B, int64_t ldb, int64_t n, int64_t K)
+{
+    if (ka == 8 && kb == 8)
+        return dot_s8_s8((const int8_t *)A + m * lda, (const int8_t *)B + n * ldb, K);
+    if (ka == 4 && kb == 4)
+        return dot_s4_s4((const uint8_t *)A + m * (lda / 2), (const uint8_t *)B + n * (ldb / 2), K);
+    /* ka == 8 && kb == 4 */
+    return dot_s8_s4((const int8_t *)A + m * lda, (const uint8_t *)B + n * (ldb / 2), K);
+}
+
+/*
+ * Raw accumulators acc[r][n] = sum_k A[m_r][k] * B[n][k] as int64
+ * ([INT4-GEMM] §3.2 with C zeroed first; [MCU-CONV] §3.2).
+ * rows == NULL means rows 0..nrows-1.  out is [nrows][N].
+ */
+int orc_gemm_acc(int ka, const void *A, int64_t lda, int kb, const void *B, int64_t ldb,
+                 int64_t N, int64_t K, const int64_t *rows, int64_t nrows, int64_t *out)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n)
+            out[r * N + n] = dot_any(ka, A, lda, m, kb, B, ldb, n, K);
+    }
+    return ORC_OK;
+}
+
+/* GEMM followed by the per-output-channel requantize; out is [nrows][ldc]. */
+static int gemm_requant(int ka, const void *A, int64_t lda, int kb, const void *B, int64_t ldb,
+                        const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                        int8_t *C, int64_t ldc, int64_t N, int64_t K,
+                        const int64_t *rows, int64_t nrows)
+{
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = dot_any(ka, A, lda, m, kb, B, ldb, n, K);
+            if (acc < INT32_MIN || acc > INT32_MAX)
+                status |= ORC_E_RANGE;
+            int8_t y = 0;
+            status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[n], &y);
+            C[r * ldc + n] = y;
+        }
+    }
+    return status;
+}
+
+/* int8 x int8 -> int32 -> requantized int8 */
+int orc_gemm_s8s8_requant(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                          const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                          int8_t *C, int64_t ldc, int64_t N, int64_t K,
+                          const int64_t *rows, int64_t nrows)
+{
+    return gemm_requant(8, A, lda, 8, B, ldb, bias, mult, shift, C, ldc, N, K, rows, nrows);
+}
+
+/* int8 activations x packed int4 weights -> requantized int8 */
+int orc_gemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                          const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                          int8_t *C, int64_t ldc, int64_t N, int64_t K,
+                          const int64_t *rows, int64_t nrows)
+{
+    return gemm_requant(8, A, lda, 4, B, ldb, bias, mult, shift, C, ldc, N, K, rows, nrows);
+}
+
+/* packed int4 x packed int4 -> raw int32 ([INT4-GEMM] §3.2) */
+int orc_gemm_s4s4_i32(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                      int32_t *C, int64_t ldc, int64_t N, int64_t K,
+                      const int64_t *rows, int64_t nrows)
+{
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = dot_any(4, A, lda, m, 4, B, ldb, n, K);
+            if (acc < INT32_MIN || acc > INT32_MAX)
+                status |= ORC_E_RANGE;
+            C[r * ldc + n] = (int32_t)acc;
+        }
+    }
+    return status;
+}
+
+/* ---- O4/O5: NHWC conv geometry and MAC count ([MCU-CONV] §2.1) ---- */
+int64_t orc_conv_out_size(int64_t in, int64_t k, int64_t stride, int64_t pad)
+{
+    int64_t span = in + 2 * pad - k;
+    if (span < 0)
+        return 0;
+    return span / stride + 1;
+}
+
+/* MACs = out_w * out_h * out_c * in_c * k_w * k_h (per image), taps over
+ * padding included, times the batch. */
+int64_t orc_conv_macs(int64_t batch, int64_t H, int64_t W, int64_t C_in, int64_t C_out,
+                      int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    return batch * Ho * Wo * C_out * C_in * KH * KW;
+}
+
+/* Accumulator of one output element: the sum over taps and input channels,
+ * with positions outside the image contributing the zero point 0. */
+static int64_t conv_acc_at(const int8_t *X, const int8_t *Wt,
+                           int64_t H, int64_t W, int64_t C_in,
+                           int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                           int64_t ph, int64_t pw,
+                           int64_t b, int64_t oh, int64_t ow, int64_t oc)
+{
+    int64_t acc = 0;
+    for (int64_t kh = 0; kh < KH; ++kh) {
+        for (int64_t kw = 0; kw < KW; ++kw) {
+            int64_t ih = oh * sh - ph + kh;
+            int64_t iw = ow * sw - pw + kw;
+            if (ih < 0 || ih >= H || iw < 0 || iw >= W)
+                continue; /* padded tap: input value is the zero point 0 */
+            for (int64_t ci = 0; ci < C_in; ++ci) {
+                int64_t x = X[((b * H + ih) * W + iw) * C_in + ci];
+                int64_t w = Wt[((oc * KH + kh) * KW + kw) * C_in + ci];
+                acc += x * w;
+            }
+        }
+    }
+    return acc;
+}
+
+/* Raw conv accumulators for the selected output pixels; out is [npix][C_out].
+ * Pixel index p = (b * H_out + oh) * W_out + ow.  pix == NULL means 0..npix-1. */
+int orc_conv2d_acc(const int8_t *X, const int8_t *Wt,
+                   int64_t batch, int64_t H, int64_t W, int64_t C_in, int64_t C_out,
+                   int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                   const int64_t *pix, int64_t npix, int64_t *out)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    (void)batch;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t oc = 0; oc < C_out; ++oc)
+            out[r * C_out + oc] = conv_acc_at(X, Wt, H, W, C_in, KH, KW, sh, sw, ph, pw,
+                                              b, oh, ow, oc);
+    }
+    return ORC_OK;
+}
+
+/* Conv followed by the per-output-channel requantize; Y is [npix][C_out]. */
+int orc_conv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
+                               const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                               int8_t *Y,
+                               int64_t batch, int64_t H, int64_t W, int64_t C_in, int64_t C_out,
+                               int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                               int64_t ph, int64_t pw,
+                               const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    int status = ORC_OK;
+    (void)batch;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(| : status)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t oc = 0; oc < C_out; ++oc) {
+            int64_t acc = conv_acc_at(X, Wt, H, W, C_in, KH, KW, sh, sw, ph, pw, b, oh, ow, oc);
+            if (acc < INT32_MIN || acc > INT32_MAX)
+                status |= ORC_E_RANGE;
+            int8_t y = 0;
+            status |= orc_requant(acc, bias ? bias[oc] : 0, mult[oc], shift[oc], &y);
+            Y[r * C_out + oc] = y;
+        }
+    }
+    return status;
+}
+
+/* ---- threading controls, so a caller can state the cores it used ---- */
+void orc_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
+}

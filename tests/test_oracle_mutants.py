@@ -1,0 +1,75 @@
+"""Plants plausible mistakes in a copy of the oracle (on the CPU) and checks
+that the oracle's pins fail for each one: evidence that the pins are tight
+enough to catch a dropped term, a wrong sign or index, or a transposed
+operand."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_FILES = ["tests/test_oracle_int4.py", "tests/test_oracle_requant.py",
+             "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py"]
+
+MUTANTS = {
+    "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
+                     "(i % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
+    "no_sign_extension": ("return code < 8 ? code : code - 16;", "return code;"),
+    "no_rounding_term": ("t = t + ((int64_t)1 << (shift - 1));", "t = t;"),
+    "rounding_off_by_one": ("((int64_t)1 << (shift - 1))", "((int64_t)1 << shift)"),
+    "saturation_low": ("if (t < -128)\n        t = -128;", "if (t < -127)\n        t = -127;"),
+    "bias_dropped": ("int64_t x = acc + (int64_t)bias;", "int64_t x = acc;"),
+    "bias_after_multiply": ("int64_t t = x * (int64_t)mult; ",
+                            "int64_t t = acc * (int64_t)mult + bias; "),
+    "k_reversed": ("acc += (int64_t)a[k] * (int64_t)b[k];",
+                   "acc += (int64_t)a[k] * (int64_t)b[K - 1 - k];"),
+    "k_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n        acc += (int64_t)a[k] * (int64_t)b[k];",
+                       "for (int64_t k = 0; k + 1 < K; ++k)\n        acc += (int64_t)a[k] * (int64_t)b[k];"),
+    "conv_pad_offset": ("int64_t ih = oh * sh - ph + kh;", "int64_t ih = oh * sh + kh;"),
+    "conv_weight_transposed": ("Wt[((oc * KH + kh) * KW + kw) * C_in + ci]",
+                               "Wt[((oc * KW + kw) * KH + kh) * C_in + ci]"),
+    "conv_out_size": ("return span / stride + 1;", "return span / stride;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(tmp_path, name):
+    src = open(os.path.join(ROOT, "oracle", "qgemm_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    msrc = tmp_path / "qgemm_oracle.c"
+    msrc.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(msrc),
+                    "-o", str(lib)], check=True)
+    env = dict(os.environ, QG_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 1, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    lib = tmp_path / "liboracle_copy.so"
+    oracle.build(out=str(lib))
+    env = dict(os.environ, QG_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+def test_ubsan_build_runs_clean(tmp_path):
+    """The oracle built with UBSan (trap on any undefined behaviour, e.g. a
+    signed int64 overflow in the requantize) passes the pins."""
+    lib = tmp_path / "liboracle_ubsan.so"
+    oracle.build(extra_flags=["-fsanitize=undefined", "-fno-sanitize-recover=all"],
+                 out=str(lib))
+    env = dict(os.environ, QG_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_requant.py", "tests/test_oracle_conv.py"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
