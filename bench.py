@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized GEMM / conv hot path on one MI355X.
+
+One step is one call of every entry point on its workload:
+  pointwise  qgemm_s8s8_requant  M=320 N=64 K=64 (1x1 conv, 20x16 pixels)
+  s4s4       qgemm_s4s4_i32      M=N=K=4096, raw int32 out
+  conv3x3    qconv2d_nhwc_s8_requant  batch 32, 56x56, 64->64, 3x3 s1 p1
+  w4a8       qgemm_w4a8_requant  M=16 tokens, K=8192, N=28672 (skinny)
+  s8s8       qgemm_s8s8_requant  M=N=K=8192
+Inputs are seeded synthetic arrays resident in HBM before timing starts.
+Each workload rotates through enough copies of its buffers that every call
+reads HBM rather than the 256 MB Infinity Cache (the pointwise case is
+L2-sized and reported hot).
+
+Prints ONE JSON line: whole-step int TOPS as `value`, per-workload times,
+TOPS, GB/s and fractions of the INT8 MFMA and HBM peaks, the roofline of the
+dominant kernel (per-launch HIP events on the launch stream), and the CPU
+oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
+METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
+ORDER = ["pointwise", "s4s4", "conv3x3", "w4a8", "s8s8"]
+# buffer sets per workload so that the rotation exceeds the Infinity Cache
+ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "w4a8": 5, "s8s8": 3}
+KERNEL_SOURCES = {
+    "s8s8": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "s4s4": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "pointwise": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "conv3x3": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
+}
+
+
+def shape_of(name):
+    from conv_qgemm_amd import datagen
+    return datagen.WORKLOADS[name]
+
+
+def ops_and_bytes(name):
+    """(int ops = 2 * MACs, algorithmic bytes: inputs once, outputs once,
+    plus 12 bytes per output channel of bias / multiplier / shift)."""
+    w = shape_of(name)
+    if w["kind"] == "conv":
+        Ho, Wo = w["H"], w["W"]  # 3x3 s1 p1 keeps the size
+        pix = w["batch"] * Ho * Wo
+        K = w["KH"] * w["KW"] * w["C_in"]
+        macs = pix * w["C_out"] * K
+        by = w["batch"] * w["H"] * w["W"] * w["C_in"] + w["C_out"] * K + 12 * w["C_out"] + \
+            pix * w["C_out"]
+        return 2 * macs, by
+    M, N, K = w["M"], w["N"], w["K"]
+    macs = M * N * K
+    if w["kind"] == "s8s8":
+        by = M * K + N * K + M * N + 12 * N
+    elif w["kind"] == "s4s4":
+        by = M * K // 2 + N * K // 2 + 4 * M * N
+    else:  # w4a8
+        by = M * K + N * K // 2 + M * N + 12 * N
+    return 2 * macs, by
+
+
+def src_sha(path):
+    h = hashlib.sha256()
+    for p in (path, "conv_qgemm_amd/csrc/dev_common.hpp"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    or None when it is absent or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if not line.startswith("traffic "):
+            continue
+        kv = dict(x.split("=", 1) for x in line.split()[1:])
+        if kv.get("workload") != name:
+            continue
+        if kv.get("src_sha") != src_sha(KERNEL_SOURCES[name]):
+            return None
+        return int(float(kv["bytes_per_launch"]))
+    return None
+
+
+class Case:
+    """Device buffers (rotated copies) and the call of one workload."""
+
+    def __init__(self, name, torch, qgemm, datagen):
+        self.name = name
+        self.q = qgemm
+        d = datagen.workload(name)
+        self.host = d
+        nrot = ROTATE[name]
+        dev = lambda a: torch.from_numpy(a).cuda()
+        base = {k: dev(v) for k, v in d.items()}
+        self.sets = []
+        for r in range(nrot):
+            s = {k: (v if r == 0 else v.clone()) for k, v in base.items()}
+            w = shape_of(name)
+            if w["kind"] == "conv":
+                s["Y"] = torch.empty((w["batch"], w["H"], w["W"], w["C_out"]), dtype=torch.int8,
+                                     device="cuda")
+            elif w["kind"] == "s4s4":
+                s["C"] = torch.empty((w["M"], w["N"]), dtype=torch.int32, device="cuda")
+            else:
+                s["C"] = torch.empty((w["M"], w["N"]), dtype=torch.int8, device="cuda")
+            self.sets.append(s)
+        self.ops, self.bytes = ops_and_bytes(name)
+
+    def __call__(self, i):
+        s = self.sets[i % len(self.sets)]
+        q = self.q
+        if self.name == "s4s4":
+            return q.qgemm_s4s4_i32(s["A"], s["B"], C=s["C"])
+        if self.name == "w4a8":
+            return q.qgemm_w4a8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
+        if self.name == "conv3x3":
+            return q.qconv2d_nhwc_s8_requant(s["X"], s["W"], s["bias"], s["mult"], s["shift"],
+                                             stride=(1, 1), pad=(1, 1), Y=s["Y"])
+        return q.qgemm_s8s8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
+
+
+def cpu_baseline(names, frac=16):
+    """The CPU oracle, as it stands, on 1/frac of every workload of the step:
+    every frac-th output row (GEMMs), pixel (conv) or weight row (w4a8)."""
+    import numpy as np
+
+    import oracle
+    from conv_qgemm_amd import datagen
+
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    total_ops, total_t, parts = 0, 0.0, []
+    for name in names:
+        d = datagen.workload(name)
+        w = shape_of(name)
+        ops, _ = ops_and_bytes(name)
+        t0 = time.perf_counter()
+        if w["kind"] == "s8s8":
+            rows = np.arange(0, w["M"], frac)
+            oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
+            part = len(rows) / w["M"]
+        elif w["kind"] == "s4s4":
+            rows = np.arange(0, w["M"], frac)
+            oracle.gemm_s4s4_i32(d["A"], d["B"], rows=rows)
+            part = len(rows) / w["M"]
+        elif w["kind"] == "w4a8":
+            cols = np.arange(0, w["N"], frac)
+            oracle.gemm_w4a8_requant(d["A"], d["B"][cols], d["bias"][cols], d["mult"][cols],
+                                     d["shift"][cols])
+            part = len(cols) / w["N"]
+        else:
+            npix = w["batch"] * w["H"] * w["W"]
+            pix = np.arange(0, npix, frac)
+            oracle.conv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                          pix=pix)
+            part = len(pix) / npix
+        dt = time.perf_counter() - t0
+        total_ops += ops * part
+        total_t += dt
+        parts.append(f"{name}:{part:.4f}")
+    return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(total_t, 2),
+            "sample": f"every {frac}th output row/pixel/weight row of each workload of one "
+                      f"step ({', '.join(parts)} of the outputs)"}
+
+
+def hbm_copy_gbs(torch, nbytes=1 << 30, iters=10):
+    """Achieved bandwidth of a plain device-to-device copy (read + write)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="all", help="all, or a comma list of " + ",".join(ORDER))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-frac", type=int, default=2)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; runs on more than one GPU are not "
+              "part of it (the path shards by output channel, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from conv_qgemm_amd import datagen
+    if not os.path.exists(os.path.join(ROOT, "conv_qgemm_amd", "libqgemm.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    from conv_qgemm_amd import qgemm
+
+    names = ORDER if args.config == "all" else args.config.split(",")
+    torch.cuda.set_device(0)
+    cases = [Case(n, torch, qgemm, datagen) for n in names]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        for c in cases:
+            c(i)
+    torch.cuda.synchronize()
+
+    ev = {c.name: [] for c in cases}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for c in cases:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            c(i)
+            b.record()
+            ev[c.name].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    total_ops = 0
+    for c in cases:
+        times = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev[c.name])
+        avg = sum(times) / len(times)
+        med = times[len(times) // 2]
+        p99 = times[min(len(times) - 1, int(0.99 * len(times)))]
+        tops = c.ops / avg / 1e12
+        gbs = c.bytes / avg / 1e9
+        per[c.name] = {"us_avg": round(avg * 1e6, 2), "us_median": round(med * 1e6, 2),
+                       "us_p99": round(p99 * 1e6, 2), "tops": round(tops, 2),
+                       "gb_s": round(gbs, 1),
+                       "pct_int8_mfma_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
+                       "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                       "ops": c.ops, "alg_bytes": c.bytes,
+                       "buffer_sets": ROTATE[c.name]}
+        total_ops += c.ops
+    ms_per_step = wall / args.steps * 1e3
+    value = total_ops / (wall / args.steps) / 1e12
+
+    dom = max(per, key=lambda n: per[n]["us_avg"])
+    mfma_bound = dom in ("s8s8", "s4s4", "conv3x3", "pointwise")
+    if mfma_bound:
+        achieved = per[dom]["tops"]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": round(achieved / PEAK_INT8_TOPS, 4)}
+    else:
+        achieved = per[dom]["gb_s"]
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "qgemm step: " + " + ".join(
+            {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
+             "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
+             "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
+                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..5"},
+        "per_config": per,
+        "roofline": roof,
+    }
+    try:
+        out["hbm_copy_gb_s"] = round(hbm_copy_gbs(torch), 1)
+    except RuntimeError:
+        out["hbm_copy_gb_s"] = None
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(names, args.cpu_frac)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,95 @@
+// dev_common.hpp -- device helpers shared by the gfx950 kernels of libqgemm.
+//
+// Operand encodings (INT4 GEMM article, www.cf-1.com/news/6060138, §2.1):
+// packed int4 holds element 2i in the low nibble of byte i and element 2i+1
+// in the high nibble, 4-bit two's complement.
+//
+// CDNA4 has no int4 matrix instruction, so int4 operands are widened to int8
+// in registers before the int8 MFMA.  The widening places each nibble in the
+// TOP half of its byte:
+//     lo = (p << 4) & 0xF0F0F0F0   -> bytes 16*v[2i]
+//     hi =  p       & 0xF0F0F0F0   -> bytes 16*v[2i+1]
+// A byte whose top nibble is the code and bottom nibble is 0 reads, as a
+// signed int8, exactly 16 times the nibble's signed value.  Products of two
+// widened operands are therefore 256*a*b and products with an int8 operand
+// 16*a*b; the epilogue shifts the exact int32 sum right by 8 or 4, which is
+// exact because the sum is a multiple of 256 or 16 and stays inside int32
+// for the K bounds the API enforces.
+//
+// The widening splits even and odd elements into separate dwords, so the
+// matrix instruction sees K in a permuted order.  A sum over K does not
+// depend on the order as long as both operands use the same one: an int4 x
+// int4 product widens both sides identically, and an int8 operand facing an
+// int4 one is permuted the same way with v_perm_b32 (even_odd_split).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// 8 packed bytes (16 int4 values, dwords p.x = values 0..7, p.y = 8..15)
+// -> 16 int8 bytes in the order [0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15],
+// each value scaled by 16.
+__device__ __forceinline__ v4i widen_int4_x16(v2u p)
+{
+    v4i r;
+    r[0] = (int)((p.x << 4) & 0xF0F0F0F0u);
+    r[1] = (int)(p.x & 0xF0F0F0F0u);
+    r[2] = (int)((p.y << 4) & 0xF0F0F0F0u);
+    r[3] = (int)(p.y & 0xF0F0F0F0u);
+    return r;
+}
+
+// 16 int8 bytes in natural order -> the same permutation widen_int4_x16
+// produces: [0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15].
+// v_perm_b32 picks bytes of the 64-bit {src0, src1} (src1 = bytes 0..3).
+__device__ __forceinline__ v4i even_odd_split(v4i q)
+{
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], 0x06040200u);
+    r[1] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], 0x07050301u);
+    r[2] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], 0x06040200u);
+    r[3] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], 0x07050301u);
+    return r;
+}
+
+// Q31 requantize of one accumulator (MCU conv front-end article,
+// news.rkmt.cn/news/16638, §2.3): x = acc + bias, t = x * mult (64-bit),
+// t += 2^(shift-1), t >>= shift (arithmetic), saturate to int8.
+// `rnd` is 2^(shift-1), computed once per channel by the caller.
+__device__ __forceinline__ int requant_one(int acc, int bias, int mult, int shift, long long rnd)
+{
+    int x = acc + bias;
+    long long t = (long long)x * (long long)mult + rnd;
+    long long y = t >> shift;
+    y = y < -128 ? -128 : y;
+    y = y > 127 ? 127 : y;
+    return (int)y;
+}
+
+__device__ __forceinline__ unsigned pack4_i8(int a, int b, int c, int d)
+{
+    return (unsigned)(a & 0xFF) | ((unsigned)(b & 0xFF) << 8) | ((unsigned)(c & 0xFF) << 16) |
+           ((unsigned)(d & 0xFF) << 24);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X, each
+// with its own L2.  Renumber them so that consecutive tile ids land on the
+// same XCD: XCD x runs ids [x * per, (x + 1) * per) (the first nwg % 8 XCDs
+// take one more).  Neighbouring tiles then share A/B panels in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg)
+{
+    constexpr int NXCD = 8;
+    int xcd = bid % NXCD;
+    int slot = bid / NXCD;
+    int per = nwg / NXCD;
+    int rem = nwg % NXCD;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace qg

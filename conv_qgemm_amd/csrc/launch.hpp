@@ -1,0 +1,46 @@
+// launch.hpp -- host-side descriptors and kernel launchers inside libqgemm.
+// Internal to the library; the public ABI is include/qgemm.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace qg {
+
+// One GEMM: C[m][n] = epilogue(sum_k A[m][k] * B[n][k]).  Strides in bytes
+// for A/B (packed int4 rows are K/2 bytes), in elements for C.
+struct GemmDesc {
+    const void *A;
+    int64_t lda_b;
+    const void *B;
+    int64_t ldb_b;
+    const int32_t *bias;  // may be null
+    const int32_t *mult;
+    const int32_t *shift;
+    void *C;
+    int64_t ldc;
+    int64_t M, N, K;  // K in values
+};
+
+// One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,
+// K = KH*KW*C_in, B = OHWI weights viewed as [C_out][K].
+struct ConvDesc {
+    const int8_t *X;
+    const int8_t *W;
+    const int32_t *bias;
+    const int32_t *mult;
+    const int32_t *shift;
+    int8_t *Y;
+    int batch, H, Wd, C_in, C_out, KH, KW, sh, sw, ph, pw, Ho, Wo;
+};
+
+hipError_t launch_s8s8_requant(const GemmDesc &d, hipStream_t s);
+hipError_t launch_s4s4_i32(const GemmDesc &d, hipStream_t s);
+hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s);
+hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s);
+hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s);
+
+// Largest M the weight-streaming W4A8 kernel takes; larger M is tiled.
+constexpr int64_t kSkinnyMaxM = 64;
+
+}  // namespace qg

@@ -1,0 +1,197 @@
+"""Python binding of libqgemm (ctypes), with the C ABI's names.
+
+Argument marshalling only: torch tensors on the GPU give device pointers,
+leading dimensions and the current stream; every step of the computation runs
+in the library's HIP kernels.  If ``libqgemm.so`` is missing or cannot be
+loaded, importing this module raises -- there is no fallback path.
+
+Layouts follow ``include/qgemm.h``: A ``[M][K]`` row-major, B ``[N][K]``
+(column-major K x N), packed int4 operands as ``uint8`` ``[rows][K/2]`` with
+element 2i in the low nibble of byte i, per-output-channel int32 bias /
+Q31 multiplier / shift, NHWC activations and OHWI weights for the conv.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
+
+QG_OK = 0
+QG_ERR_NULLPTR = 1
+QG_ERR_INVALID = 2
+QG_ERR_NO_DEVICE = 3
+QG_ERR_LAUNCH = 4
+
+QG_S4S4_MAX_K = 131040
+QG_W4A8_MAX_K = 131040
+
+
+class QGemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(or python conv_qgemm_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.qgemm_s8s8_requant.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
+    lib.qgemm_s8s8_requant.restype = S
+    lib.qgemm_s4s4_i32.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.qgemm_s4s4_i32.restype = S
+    lib.qgemm_w4a8_requant.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
+    lib.qgemm_w4a8_requant.restype = S
+    lib.qconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 11 + [P]
+    lib.qconv2d_nhwc_s8_requant.restype = S
+    lib.qg_status_string.argtypes = [S]
+    lib.qg_status_string.restype = ctypes.c_char_p
+    lib.qg_version.argtypes = []
+    lib.qg_version.restype = S
+    return lib
+
+
+lib = _load()
+EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
+           "qconv2d_nhwc_s8_requant", "qg_status_string", "qg_version")
+
+
+def status_string(status: int) -> str:
+    return lib.qg_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib.qg_version())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, what: str):
+    if status != QG_OK:
+        raise QGemmError(status, what)
+
+
+def _mat(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t
+
+
+def _vec(t, n, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < n or t.stride(0) != 1:
+        raise ValueError(f"{name} must be a contiguous int32 vector of length >= {n}")
+    return t
+
+
+def qgemm_s8s8_requant(A, B, bias, mult, shift, C=None, stream=None):
+    """C[m][n] = requant(sum_k A[m][k] * B[n][k]); A int8 [M, K], B int8 [N, K]."""
+    _mat(A, torch.int8, "A")
+    _mat(B, torch.int8, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.int8, device=A.device)
+    _mat(C, torch.int8, "C")
+    st = lib.qgemm_s8s8_requant(_ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                _ptr(_vec(bias, N, "bias")), _ptr(_vec(mult, N, "mult")),
+                                _ptr(_vec(shift, N, "shift")), _ptr(C), C.stride(0), M, N, K,
+                                _stream(stream))
+    _check(st, "qgemm_s8s8_requant")
+    return C
+
+
+def qgemm_s4s4_i32(A, B, C=None, K=None, stream=None):
+    """C = A * B^T over packed int4 rows; A uint8 [M, K/2], B uint8 [N, K/2]."""
+    _mat(A, torch.uint8, "A")
+    _mat(B, torch.uint8, "B")
+    M = A.shape[0]
+    N = B.shape[0]
+    if K is None:
+        K = 2 * A.shape[1]
+    if 2 * A.shape[1] < K or 2 * B.shape[1] < K:
+        raise ValueError("packed rows shorter than K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    _mat(C, torch.int32, "C")
+    st = lib.qgemm_s4s4_i32(_ptr(A), 2 * A.stride(0), _ptr(B), 2 * B.stride(0), _ptr(C),
+                            C.stride(0), M, N, K, _stream(stream))
+    _check(st, "qgemm_s4s4_i32")
+    return C
+
+
+def qgemm_w4a8_requant(A, B, bias, mult, shift, C=None, K=None, stream=None):
+    """int8 activations A [M, K] x packed int4 weights B uint8 [N, K/2] -> int8."""
+    _mat(A, torch.int8, "A")
+    _mat(B, torch.uint8, "B")
+    M = A.shape[0]
+    N = B.shape[0]
+    if K is None:
+        K = A.shape[1]
+    if A.shape[1] < K or 2 * B.shape[1] < K:
+        raise ValueError("rows shorter than K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.int8, device=A.device)
+    _mat(C, torch.int8, "C")
+    st = lib.qgemm_w4a8_requant(_ptr(A), A.stride(0), _ptr(B), 2 * B.stride(0),
+                                _ptr(_vec(bias, N, "bias")), _ptr(_vec(mult, N, "mult")),
+                                _ptr(_vec(shift, N, "shift")), _ptr(C), C.stride(0), M, N, K,
+                                _stream(stream))
+    _check(st, "qgemm_w4a8_requant")
+    return C
+
+
+def conv_out_hw(H, W, KH, KW, stride, pad):
+    sh, sw = stride
+    ph, pw = pad
+    return (H + 2 * ph - KH) // sh + 1, (W + 2 * pw - KW) // sw + 1
+
+
+def qconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1), Y=None,
+                            stream=None):
+    """NHWC int8 conv with zero-point-0 padding and the fused requantize.
+
+    X int8 [batch, H, W, C_in] and W int8 [C_out, KH, KW, C_in], both
+    contiguous; returns Y int8 [batch, H_out, W_out, C_out].
+    """
+    if X.dtype != torch.int8 or W.dtype != torch.int8:
+        raise TypeError("X and W must be int8")
+    if X.dim() != 4 or W.dim() != 4 or not X.is_contiguous() or not W.is_contiguous():
+        raise ValueError("X [B,H,W,C_in] and W [C_out,KH,KW,C_in] must be contiguous 4-D")
+    batch, H, Wd, C_in = X.shape
+    C_out, KH, KW, C_in2 = W.shape
+    if C_in2 != C_in:
+        raise ValueError("X and W disagree on C_in")
+    Ho, Wo = conv_out_hw(H, Wd, KH, KW, stride, pad)
+    if Y is None:
+        Y = torch.empty((batch, max(Ho, 0), max(Wo, 0), C_out), dtype=torch.int8,
+                        device=X.device)
+    if not Y.is_contiguous() or Y.dtype != torch.int8 or tuple(Y.shape) != (batch, Ho, Wo, C_out):
+        raise ValueError("Y must be a contiguous int8 [batch, H_out, W_out, C_out] tensor")
+    st = lib.qconv2d_nhwc_s8_requant(_ptr(X), _ptr(W), _ptr(_vec(bias, C_out, "bias")),
+                                     _ptr(_vec(mult, C_out, "mult")),
+                                     _ptr(_vec(shift, C_out, "shift")), _ptr(Y),
+                                     batch, H, Wd, C_in, C_out, KH, KW, stride[0], stride[1],
+                                     pad[0], pad[1], _stream(stream))
+    _check(st, "qconv2d_nhwc_s8_requant")
+    return Y

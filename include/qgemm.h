@@ -1,0 +1,153 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) quantized GEMM / conv library.
+ *
+ * The computation: low-bit integer matrix products with INT32 accumulation,
+ * and a fused per-output-channel fixed-point requantize back to INT8.
+ *
+ * Definitions followed (web pages; section numbers are the pages' own):
+ *   - INT4 operands are signed 4-bit two's complement, two per byte
+ *     ("DeepGEMM" INT4 GEMM article, www.cf-1.com/news/6060138, §2.1).
+ *     Element 2i is the LOW nibble of byte i, element 2i+1 the high nibble.
+ *   - C = A * B with INT4 or INT8 inputs and INT32 accumulation (same
+ *     article, §3.2); B is stored column-major, i.e. as [N][K] with K
+ *     contiguous (same article, §4.3).
+ *   - Requantize (MCU conv front-end article, news.rkmt.cn/news/16638,
+ *     §2.3, with the bias of §3.3):
+ *         x = acc + bias[n]                       (int32)
+ *         t = x * mult[n]                         (int64)
+ *         t = t + 2^(shift[n] - 1)                (half an LSB)
+ *         y = t >> shift[n]                       (arithmetic shift)
+ *         out = min(127, max(-128, y))            (int8)
+ *     Symmetric quantization: zero point 0, so there is no zero-point
+ *     argument and conv padding reads 0 (same article, §2.3).
+ *   - Conv: NHWC activations, OHWI weights [C_out][KH][KW][C_in] (same
+ *     article, §3.1), computed as an implicit GEMM over the im2col matrix
+ *     of §3.2 with K index (kh * KW + kw) * C_in + ci; output size
+ *     floor((H + 2*pad - KH) / stride) + 1 (same article, §2.1).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is DEVICE memory owned by the caller.  The library never
+ *     allocates, frees or synchronizes, and keeps no mutable state.
+ *   - stream: a hipStream_t (NULL = default stream).  A call validates its
+ *     arguments on the host, enqueues its kernels on `stream` and returns;
+ *     the result is ready when the stream reaches that point.  A fault in a
+ *     kernel surfaces at the caller's next synchronization.
+ *   - Leading dimensions are in ELEMENTS.  For packed int4 operands they
+ *     count nibbles and must be even; the byte stride is ld / 2.
+ *   - Alignment: every base pointer must be 16-byte aligned, and the row
+ *     strides of the operands (lda, ldb in bytes) multiples of 16 bytes.
+ *     The output row stride ldc may be any value >= N; when ldc is a
+ *     multiple of 4 the kernels store four results per instruction.
+ *   - Outputs must not overlap inputs.
+ *   - Results are deterministic: integer sums are exact, so repeated calls
+ *     give identical bytes.
+ *   - Device-resident preconditions, not checked by the library:
+ *     shift[n] in [1, 63]; mult[n] in [0, 2^31 - 1]; acc + bias[n] fits in
+ *     int32.  Outside them the output bytes are unspecified (no fault).
+ *
+ * Status codes (checked in this order; every argument check happens on the
+ * host before any HIP call, so it is testable without a GPU):
+ *   QG_ERR_NULLPTR   a required pointer is NULL (bias may be NULL = zero)
+ *   QG_ERR_INVALID   a size, stride or alignment rule is broken
+ *   QG_ERR_NO_DEVICE no HIP device is current, or it is not gfx950
+ *   QG_ERR_LAUNCH    the kernel launch reported an error
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULLPTR = 1,
+    QG_ERR_INVALID = 2,
+    QG_ERR_NO_DEVICE = 3,
+    QG_ERR_LAUNCH = 4
+} qg_status;
+
+/* Largest K accepted by the int4 entry points.  The library computes on
+ * 16x-scaled nibbles; this bound keeps the scaled int32 sums exact:
+ * s4s4: 256 * 64 * K < 2^31;  w4a8: 16 * 128 * 8 * K < 2^31 (|a| <= 128). */
+#define QG_S4S4_MAX_K 131040
+#define QG_W4A8_MAX_K 131040
+
+/*
+ * qgemm_s8s8_requant -- C[m][n] = requant(sum_k A[m][k] * B[n][k]).
+ *   A     int8  [M][lda], row-major, lda >= K
+ *   B     int8  [N][ldb] (column-major K x N), ldb >= K
+ *   bias  int32 [N] or NULL;  mult int32 [N] (Q31);  shift int32 [N]
+ *   C     int8  [M][ldc], ldc >= N
+ *   M, N, K >= 1; K % 16 == 0 (16-byte rows); lda, ldb % 16 == 0.
+ * MCU conv front-end article §2.3 (requantize), §3.2 (C = A x B);
+ * INT4 GEMM article §4.3 (B column-major).
+ */
+qg_status qgemm_s8s8_requant(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                             const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                             int8_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             void *stream);
+
+/*
+ * qgemm_s4s4_i32 -- C[m][n] = sum_k A[m][k] * B[n][k], raw int32, no requant.
+ *   A     packed int4 [M][lda/2 bytes], lda >= K (nibbles)
+ *   B     packed int4 [N][ldb/2 bytes], ldb >= K
+ *   C     int32 [M][ldc], ldc >= N
+ *   M, N >= 1; K >= 1, K % 32 == 0 (16-byte packed rows), K <= QG_S4S4_MAX_K;
+ *   lda, ldb % 32 == 0 (nibbles).
+ * INT4 GEMM article §2.1 (packing), §3.2 (C = A*B into a zeroed C).
+ */
+qg_status qgemm_s4s4_i32(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                         int32_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                         void *stream);
+
+/*
+ * qgemm_w4a8_requant -- int8 activations x packed int4 weights, requantized.
+ *   A     int8  [M][lda], lda >= K
+ *   B     packed int4 [N][ldb/2 bytes], ldb >= K (nibbles)
+ *   bias/mult/shift as for qgemm_s8s8_requant
+ *   C     int8  [M][ldc], ldc >= N
+ *   M, N >= 1; K % 32 == 0, K <= QG_W4A8_MAX_K; lda % 16 == 0, ldb % 32 == 0.
+ * Small M (a few tokens) runs a weight-streaming kernel; larger M runs the
+ * tiled kernel.  Same definitions as above.
+ */
+qg_status qgemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                             const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                             int8_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             void *stream);
+
+/*
+ * qconv2d_nhwc_s8_requant -- int8 NHWC conv, zero-point-0 padding, requant.
+ *   X     int8 [batch][H][Wd][C_in]  (NHWC, dense)
+ *   W     int8 [C_out][KH][KW][C_in] (OHWI, dense)
+ *   bias/mult/shift int32 [C_out] (bias may be NULL)
+ *   Y     int8 [batch][H_out][W_out][C_out] (NHWC, dense)
+ *   H_out = (H + 2*pad_h - KH) / stride_h + 1, W_out likewise; both >= 1.
+ *   batch, H, Wd, KH, KW, stride >= 1; pad >= 0; C_in % 16 == 0 and
+ *   C_out % 16 == 0 (pad channels with zeros, as the MCU article's §3.1
+ *   pads input channels); dilation 1, one group.
+ * MCU conv front-end article §2.1, §2.3, §3.1, §3.2; 3x3 taps walked as
+ * shifted 1x1 products (Groq TSP ResNet50 article, www.pwwt.cn/news/1982903,
+ * §2.1).
+ */
+qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W,
+                                  const int32_t *bias, const int32_t *mult,
+                                  const int32_t *shift, int8_t *Y,
+                                  int32_t batch, int32_t H, int32_t Wd, int32_t C_in,
+                                  int32_t C_out, int32_t KH, int32_t KW,
+                                  int32_t stride_h, int32_t stride_w,
+                                  int32_t pad_h, int32_t pad_w, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qg_status_string(qg_status s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

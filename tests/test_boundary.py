@@ -1,0 +1,159 @@
+"""The C-ABI library on the host: it loads, exports every function declared in
+include/qgemm.h, and rejects every invalid argument before any HIP call (so
+these run with no GPU).  Pointers here are fake, aligned addresses: a call
+that passes validation is only made where no GPU is present, where it must
+stop at the device check."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+
+@pytest.fixture(scope="module")
+def qg():
+    from conv_qgemm_amd import qgemm
+    return qgemm
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(qg):
+    names = _declared_functions()
+    assert set(names) >= {"qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
+                          "qconv2d_nhwc_s8_requant", "qg_status_string", "qg_version"}
+    raw = ctypes.CDLL(qg._LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(qg.EXPORTS) == set(names)
+
+
+def test_status_strings(qg):
+    for code in range(5):
+        s = qg.status_string(code)
+        assert s.startswith("QG_")
+    assert qg.status_string(99) == "unknown qg_status"
+    assert qg.version() >= 100
+
+
+def test_header_constants_match_binding(qg):
+    text = open(HEADER).read()
+    assert int(re.search(r"QG_S4S4_MAX_K (\d+)", text).group(1)) == qg.QG_S4S4_MAX_K
+    assert int(re.search(r"QG_W4A8_MAX_K (\d+)", text).group(1)) == qg.QG_W4A8_MAX_K
+    # 256 * 64 * K and 16 * 1024 * K stay below 2^31 at the bound
+    assert 256 * 64 * qg.QG_S4S4_MAX_K < 2 ** 31
+    assert 16 * 128 * 8 * qg.QG_W4A8_MAX_K < 2 ** 31
+    assert qg.QG_S4S4_MAX_K % 32 == 0
+
+
+P = 0x10000  # fake, 16-byte aligned device addresses
+NULL = None
+
+
+def s8(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=32, N=64, K=64):
+    return qg.lib.qgemm_s8s8_requant(A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, None)
+
+
+def s4(qg, A=P, lda=64, B=P, ldb=64, C=P, ldc=64, M=32, N=64, K=64):
+    return qg.lib.qgemm_s4s4_i32(A, lda, B, ldb, C, ldc, M, N, K, None)
+
+
+def w4(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=16, N=64, K=64):
+    return qg.lib.qgemm_w4a8_requant(A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, None)
+
+
+def cv(qg, X=P, W=P, bias=P, mult=P, shift=P, Y=P, batch=1, H=8, Wd=8, C_in=16, C_out=16,
+       KH=3, KW=3, sh=1, sw=1, ph=1, pw=1):
+    return qg.lib.qconv2d_nhwc_s8_requant(X, W, bias, mult, shift, Y, batch, H, Wd, C_in, C_out,
+                                          KH, KW, sh, sw, ph, pw, None)
+
+
+def test_nullptr(qg):
+    E = qg.QG_ERR_NULLPTR
+    for kw in ("A", "B", "C", "mult", "shift"):
+        assert s8(qg, **{kw: NULL}) == E, kw
+        assert w4(qg, **{kw: NULL}) == E, kw
+    for kw in ("A", "B", "C"):
+        assert s4(qg, **{kw: NULL}) == E, kw
+    for kw in ("X", "W", "Y", "mult", "shift"):
+        assert cv(qg, **{kw: NULL}) == E, kw
+
+
+def test_invalid_gemm_sizes(qg):
+    E = qg.QG_ERR_INVALID
+    for f in (s8, s4, w4):
+        assert f(qg, M=0) == E
+        assert f(qg, N=0) == E
+        assert f(qg, K=0) == E
+        assert f(qg, M=-1) == E
+        assert f(qg, M=2 ** 31) == E        # rows past the int32 headroom
+        assert f(qg, lda=32, K=64) == E     # lda < K
+        assert f(qg, ldb=32, K=64) == E     # ldb < K
+        assert f(qg, ldc=48, N=64) == E     # ldc < N
+    # K must fill whole 16-byte rows: K % 16 for int8, K % 32 with any int4 operand
+    assert s8(qg, K=40, lda=64, ldb=64) == E
+    assert s4(qg, K=48, lda=64, ldb=64) == E
+    assert w4(qg, K=48, lda=64, ldb=64) == E
+    # row strides: multiples of 16 bytes
+    assert s8(qg, lda=72) == E
+    assert s4(qg, lda=80) == E              # 80 nibbles = 40 bytes
+    assert w4(qg, ldb=80) == E
+    # int4 K bounds keep the scaled int32 sums exact
+    big = qg.QG_S4S4_MAX_K + 32
+    assert s4(qg, K=big, lda=big, ldb=big) == E
+    assert w4(qg, K=big, lda=big, ldb=big) == E
+
+
+def test_invalid_alignment(qg):
+    E = qg.QG_ERR_INVALID
+    for kw in ("A", "B", "C"):
+        assert s8(qg, **{kw: P + 8}) == E, kw
+        assert s4(qg, **{kw: P + 4}) == E, kw
+        assert w4(qg, **{kw: P + 1}) == E, kw
+    for kw in ("bias", "mult", "shift"):
+        assert s8(qg, **{kw: P + 4}) == E, kw
+        assert w4(qg, **{kw: P + 4}) == E, kw
+    for kw in ("X", "W", "Y", "mult"):
+        assert cv(qg, **{kw: P + 4}) == E, kw
+
+
+def test_invalid_conv(qg):
+    E = qg.QG_ERR_INVALID
+    for kw in ("batch", "H", "Wd", "C_in", "C_out", "KH", "KW", "sh", "sw"):
+        assert cv(qg, **{kw: 0}) == E, kw
+    assert cv(qg, ph=-1) == E
+    assert cv(qg, pw=-1) == E
+    assert cv(qg, C_in=24) == E             # C_in % 16
+    assert cv(qg, C_out=8) == E             # C_out % 16
+    assert cv(qg, H=2, KH=5, ph=1) == E     # H_out < 1
+    assert cv(qg, Wd=1, KW=4, pw=1) == E    # W_out < 1
+    assert cv(qg, batch=2 ** 20, H=2 ** 10, Wd=2 ** 10) == E  # too many pixels
+
+
+def test_valid_call_without_gpu_reports_no_device(qg):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case is only meaningful without one")
+    assert s8(qg) == qg.QG_ERR_NO_DEVICE
+    assert s4(qg) == qg.QG_ERR_NO_DEVICE
+    assert w4(qg) == qg.QG_ERR_NO_DEVICE
+    assert cv(qg) == qg.QG_ERR_NO_DEVICE
+
+
+def test_binding_rejects_bad_tensors(qg):
+    import torch
+    A = torch.zeros((4, 32), dtype=torch.int16)
+    with pytest.raises(TypeError):
+        qg.qgemm_s8s8_requant(A, A, None, None, None)
+    X = torch.zeros((1, 4, 4, 16), dtype=torch.int8)
+    W = torch.zeros((16, 3, 3, 32), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        qg.qconv2d_nhwc_s8_requant(X, W, None, torch.zeros(16, dtype=torch.int32),
+                                   torch.zeros(16, dtype=torch.int32))

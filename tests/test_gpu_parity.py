@@ -1,0 +1,299 @@
+"""Parity of the HIP path with the CPU oracle, byte for byte.
+
+Every case draws seeded inputs, runs the library through its C ABI (via the
+ctypes binding) on the GPU and compares with the oracle on the same inputs.
+Integer results are unique, so the bar is exact equality.  Small cases span
+several tiles with ragged tails in M, N and K; the full-size workloads are
+checked in full where the oracle finishes in seconds (the conv, the skinny
+W4A8) and on sampled output rows otherwise (the 4096^3 and 8192^3 GEMMs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from conv_qgemm_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def qg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from conv_qgemm_amd import qgemm
+    return qgemm
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _sample_rows(M, n, seed):
+    g = np.random.default_rng(seed)
+    rows = set(g.choice(M, size=min(n, M), replace=False).tolist())
+    rows |= {0, M - 1, max(M - 2, 0)}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# ---------------------------------------------------------------- s8s8
+
+S8_SHAPES = [
+    (1, 1, 16), (7, 5, 16), (33, 17, 48), (64, 64, 64), (129, 65, 144), (320, 64, 64),
+    (300, 260, 512), (517, 389, 272), (1500, 1500, 96),
+]
+
+
+@pytest.mark.parametrize("M,N,K", S8_SHAPES)
+@pytest.mark.parametrize("unsat", [False, True])
+def test_s8s8_small(qg, M, N, K, unsat):
+    _say("s8s8", M, N, K, unsat)
+    d = datagen.gemm_s8s8(M, N, K, seed=M + N + K, shift=(38, 44) if unsat else (31, 40))
+    C = qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]))
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(host(C), want)
+
+
+def test_s8s8_large_tile_sampled(qg):
+    # enough 256x256 tiles to select the largest tile, ragged in M and N
+    M, N, K = 4100, 4130, 160
+    _say("s8s8 large tile", M, N, K)
+    d = datagen.gemm_s8s8(M, N, K, seed=77, shift=(36, 42))
+    C = host(qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    rows = _sample_rows(M, 200, 1)
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
+    assert np.array_equal(C[rows], want)
+
+
+def test_s8s8_no_bias_and_strided(qg):
+    M, N, K = 96, 80, 128
+    d = datagen.gemm_s8s8(M, N, K, seed=3, shift=(36, 40))
+    Aw = np.zeros((M, K + 48), np.int8)
+    Aw[:, :K] = d["A"]
+    Bw = np.zeros((N, K + 16), np.int8)
+    Bw[:, :K] = d["B"]
+    At, Bt = dev(Aw), dev(Bw)
+    Cw = torch.full((M, N + 32), 99, dtype=torch.int8, device="cuda")
+    qg.qgemm_s8s8_requant(At[:, :K], Bt[:, :K], None, dev(d["mult"]), dev(d["shift"]),
+                          C=Cw[:, :N])
+    got = host(Cw)
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], None, d["mult"], d["shift"])
+    assert np.array_equal(got[:, :N], want)
+    assert np.all(got[:, N:] == 99)  # nothing written past N
+
+
+@pytest.mark.parametrize("ldc_extra", [1, 3])
+def test_unaligned_output_stride(qg, ldc_extra):
+    # an output row stride that is not a multiple of 4 takes the scalar stores
+    M, N, K = 70, 36, 64
+    d = datagen.gemm_s8s8(M, N, K, seed=31, shift=(36, 40))
+    Cw = torch.zeros((M, N + ldc_extra), dtype=torch.int8, device="cuda")
+    qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                          dev(d["shift"]), C=Cw[:, :N])
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    got = host(Cw)
+    assert np.array_equal(got[:, :N], want) and np.all(got[:, N:] == 0)
+    s = datagen.gemm_s4s4(M, N, K, seed=32)
+    Ci = torch.zeros((M, N + ldc_extra), dtype=torch.int32, device="cuda")
+    qg.qgemm_s4s4_i32(dev(s["A"]), dev(s["B"]), C=Ci[:, :N])
+    goti = host(Ci)
+    assert np.array_equal(goti[:, :N], oracle.gemm_s4s4_i32(s["A"], s["B"]))
+    assert np.all(goti[:, N:] == 0)
+    w = datagen.gemm_w4a8(9, N, 128, seed=33, shift=(37, 43))
+    Cs = torch.zeros((9, N + ldc_extra), dtype=torch.int8, device="cuda")
+    qg.qgemm_w4a8_requant(dev(w["A"]), dev(w["B"]), dev(w["bias"]), dev(w["mult"]),
+                          dev(w["shift"]), C=Cs[:, :N])
+    gots = host(Cs)
+    assert np.array_equal(gots[:, :N], oracle.gemm_w4a8_requant(w["A"], w["B"], w["bias"],
+                                                                w["mult"], w["shift"]))
+
+
+def test_s8s8_extremes(qg):
+    # -128 operands, large K, shifts at both ends of the domain
+    M, N, K = 64, 48, 1024
+    A = np.full((M, K), -128, np.int8)
+    B = np.full((N, K), -128, np.int8)
+    B[1::2] = 127
+    bias = np.zeros(N, np.int32)
+    mult = np.full(N, 2 ** 31 - 1, np.int32)
+    shift = np.array([1, 63, 31, 44] * (N // 4), np.int32)
+    C = qg.qgemm_s8s8_requant(dev(A), dev(B), dev(bias), dev(mult), dev(shift))
+    assert np.array_equal(host(C), oracle.gemm_s8s8_requant(A, B, bias, mult, shift))
+
+
+# ---------------------------------------------------------------- s4s4
+
+S4_SHAPES = [(1, 1, 32), (16, 64, 32), (37, 29, 96), (130, 70, 288), (300, 200, 544),
+             (1500, 1500, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", S4_SHAPES)
+def test_s4s4_small(qg, M, N, K):
+    _say("s4s4", M, N, K)
+    d = datagen.gemm_s4s4(M, N, K, seed=M * 3 + K)
+    C = qg.qgemm_s4s4_i32(dev(d["A"]), dev(d["B"]))
+    assert np.array_equal(host(C), oracle.gemm_s4s4_i32(d["A"], d["B"]))
+
+
+def test_s4s4_hello_world(qg):
+    # the INT4 GEMM article's example: A all 0x11, B all 0x22, K = 32 -> 64
+    A = np.full((16, 16), 0x11, np.uint8)
+    B = np.full((64, 16), 0x22, np.uint8)
+    C = host(qg.qgemm_s4s4_i32(dev(A), dev(B)))
+    assert np.all(C == 64)
+
+
+def test_s4s4_extremes(qg):
+    M, N, K = 64, 64, 4096
+    A = np.full((M, K // 2), 0x88, np.uint8)  # all -8
+    B = np.full((N, K // 2), 0x88, np.uint8)
+    B[::3] = 0x77                              # all 7
+    C = host(qg.qgemm_s4s4_i32(dev(A), dev(B)))
+    assert np.array_equal(C, oracle.gemm_s4s4_i32(A, B))
+    assert C[0, 1] == 64 * K and C[0, 0] == -56 * K
+
+
+# ---------------------------------------------------------------- w4a8
+
+W4_SHAPES = [
+    (1, 16, 32), (5, 100, 544), (16, 64, 8192), (16, 1000, 8224), (16, 48, 16416),
+    (33, 77, 256), (64, 32, 512), (65, 130, 160), (300, 260, 640),
+]
+
+
+@pytest.mark.parametrize("M,N,K", W4_SHAPES)
+def test_w4a8_small(qg, M, N, K):
+    _say("w4a8", M, N, K)
+    d = datagen.gemm_w4a8(M, N, K, seed=M + 7 * N + K, shift=(37, 43))
+    C = qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]))
+    want = oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(host(C), want)
+
+
+# ---------------------------------------------------------------- conv
+
+CONV_GEOMS = [
+    # batch, H, W, C_in, C_out, KH, KW, stride, pad
+    (1, 7, 6, 16, 16, 3, 3, (1, 1), (1, 1)),
+    (2, 9, 8, 16, 32, 3, 3, (2, 2), (1, 1)),
+    (1, 10, 7, 32, 16, 3, 3, (1, 1), (0, 0)),
+    (1, 8, 8, 16, 48, 5, 5, (1, 1), (2, 2)),
+    (2, 6, 11, 16, 16, 1, 3, (1, 2), (0, 1)),
+    (1, 5, 5, 16, 16, 3, 3, (2, 1), (2, 0)),
+    (3, 20, 16, 64, 64, 1, 1, (1, 1), (0, 0)),
+    (2, 14, 14, 64, 64, 3, 3, (1, 1), (1, 1)),
+    (1, 12, 13, 32, 128, 3, 3, (1, 1), (1, 1)),
+    (1, 11, 9, 48, 80, 3, 3, (2, 2), (1, 1)),
+    (1, 40, 32, 16, 16, 3, 3, (2, 2), (1, 1)),  # first layer of the MCU front-end, C_in padded to 16
+]
+
+
+@pytest.mark.parametrize("geom", CONV_GEOMS)
+def test_conv_small(qg, geom):
+    b, H, Wd, Ci, Co, KH, KW, stride, pad = geom
+    _say("conv", geom)
+    d = datagen.conv_nhwc(b, H, Wd, Ci, Co, KH, KW, seed=H * Wd + Ci, shift=(35, 41))
+    Y = qg.qconv2d_nhwc_s8_requant(dev(d["X"]), dev(d["W"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"]), stride=stride, pad=pad)
+    want = oracle.conv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                         stride=stride, pad=pad)
+    assert np.array_equal(host(Y), want)
+
+
+def test_conv_pointwise_equals_gemm(qg):
+    d = datagen.workload("pointwise", unsaturated=True)
+    X = dev(d["A"].reshape(1, 20, 16, 64))
+    W = dev(d["B"].reshape(64, 1, 1, 64))
+    Y = qg.qconv2d_nhwc_s8_requant(X, W, dev(d["bias"]), dev(d["mult"]), dev(d["shift"]),
+                                   stride=(1, 1), pad=(0, 0))
+    C = qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]))
+    assert np.array_equal(host(Y).reshape(320, 64), host(C))
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_pointwise(qg, unsat):
+    d = datagen.workload("pointwise", unsaturated=unsat)
+    C = qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]))
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(host(C), want)
+
+
+def test_workload_s4s4_sampled(qg):
+    _say("workload s4s4 4096^3")
+    d = datagen.workload("s4s4")
+    C = host(qg.qgemm_s4s4_i32(dev(d["A"]), dev(d["B"])))
+    rows = _sample_rows(4096, 48, 2)
+    assert np.array_equal(C[rows], oracle.gemm_s4s4_i32(d["A"], d["B"], rows=rows))
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_conv3x3_full(qg, unsat):
+    _say("workload conv3x3 full", unsat)
+    d = datagen.workload("conv3x3", unsaturated=unsat)
+    Y = host(qg.qconv2d_nhwc_s8_requant(dev(d["X"]), dev(d["W"]), dev(d["bias"]),
+                                        dev(d["mult"]), dev(d["shift"]), stride=(1, 1),
+                                        pad=(1, 1)))
+    want = oracle.conv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                         stride=(1, 1), pad=(1, 1))
+    assert np.array_equal(Y, want)
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_w4a8_full(qg, unsat):
+    _say("workload w4a8 full", unsat)
+    d = datagen.workload("w4a8", unsaturated=unsat)
+    C = host(qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    want = oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(C, want)
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_s8s8_sampled(qg, unsat):
+    _say("workload s8s8 8192^3", unsat)
+    d = datagen.workload("s8s8", unsaturated=unsat)
+    C = host(qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    rows = _sample_rows(8192, 48, 3)
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
+    assert np.array_equal(C[rows], want)
+
+
+# ---------------------------------------------------------------- runtime behaviour
+
+def test_deterministic_and_side_stream(qg):
+    d = datagen.gemm_s8s8(700, 300, 256, seed=12, shift=(36, 42))
+    args = [dev(d[k]) for k in ("A", "B", "bias", "mult", "shift")]
+    ref = host(qg.qgemm_s8s8_requant(*args))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs = [qg.qgemm_s8s8_requant(*args, stream=s) for _ in range(3)]
+    s.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy(), ref)
+
+
+def test_invalid_call_on_gpu_raises(qg):
+    A = torch.zeros((32, 40), dtype=torch.int8, device="cuda")  # K = 40 breaks K % 16
+    B = torch.zeros((16, 40), dtype=torch.int8, device="cuda")
+    p = torch.zeros(16, dtype=torch.int32, device="cuda")
+    with pytest.raises(qg.QGemmError) as e:
+        qg.qgemm_s8s8_requant(A, B, p, p, p)
+    assert e.value.status == qg.QG_ERR_INVALID
