@@ -62,14 +62,39 @@ __device__ __forceinline__ v4i even_odd_split(v4i q)
 // news.rkmt.cn/news/16638, §2.3): x = acc + bias, t = x * mult (64-bit),
 // t += 2^(shift-1), t >>= shift (arithmetic), saturate to int8.
 // `rnd` is 2^(shift-1), computed once per channel by the caller.
+// The 64-bit quotient is saturated from its two halves: when the high word is
+// not the sign extension of the low word, |y| >= 2^31 and the result is the
+// bound on y's side.
 __device__ __forceinline__ int requant_one(int acc, int bias, int mult, int shift, long long rnd)
 {
-    int x = acc + bias;
-    long long t = (long long)x * (long long)mult + rnd;
-    long long y = t >> shift;
-    y = y < -128 ? -128 : y;
-    y = y > 127 ? 127 : y;
-    return (int)y;
+    const int x = acc + bias;
+    const long long y = ((long long)x * (long long)mult + rnd) >> shift;
+    const int lo = (int)y, hi = (int)(y >> 32);
+    const int c = min(max(lo, -128), 127);
+    return hi == (lo >> 31) ? c : ((hi >> 31) ^ 127);
+}
+
+// The same when shift >= 31: |x * mult| < 2^62 then keeps y inside int32, so
+// the low word of the 64-bit shift is y itself.
+__device__ __forceinline__ int requant_one_s31(int acc, int bias, int mult, int shift,
+                                               long long rnd)
+{
+    const int x = acc + bias;
+    const int y = (int)(((long long)x * (long long)mult + rnd) >> shift);
+    return min(max(y, -128), 127);
+}
+
+// The same when shift >= 33: with x * mult = H * 2^32 + L (0 <= L < 2^32,
+// H the high word of the signed product), t / 2^shift =
+// (H + 2^(shift-33) + L / 2^32) / 2^(shift-32), and the fraction L / 2^32
+// never changes the floor, so y = (H + 2^(shift-33)) >> (shift-32) exactly.
+// |H| <= 2^30, so the sum stays inside int32.
+__device__ __forceinline__ int requant_one_s33(int acc, int bias, int mult, int shift)
+{
+    const int x = acc + bias;
+    const int h = __mulhi(x, mult);
+    const int y = (h + (1 << ((shift - 33) & 31))) >> ((shift - 32) & 31);
+    return min(max(y, -128), 127);
 }
 
 __device__ __forceinline__ unsigned pack4_i8(int a, int b, int c, int d)

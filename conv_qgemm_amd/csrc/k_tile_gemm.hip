@@ -365,11 +365,15 @@ static hipError_t run_gemm(const GemmDesc &d, hipStream_t s)
 
 hipError_t launch_s8s8_requant(const GemmDesc &d, hipStream_t s)
 {
+    if (dma_gemm_fits(d, false))
+        return launch_s8s8_requant_dma(d, s);
     return run_gemm<OP_S8, OP_S8, EPI_REQUANT, 128>(d, s);
 }
 
 hipError_t launch_s4s4_i32(const GemmDesc &d, hipStream_t s)
 {
+    if (dma_gemm_fits(d, true))
+        return launch_s4s4_i32_dma(d, s);
     return run_gemm<OP_S4, OP_S4, EPI_I32, 256>(d, s);
 }
 

@@ -40,6 +40,11 @@ hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s);
 hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s);
 hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s);
 
+// 256x256 ring kernel for large GEMMs (k_gemm_dma.hip)
+bool dma_gemm_fits(const GemmDesc &d, bool int4);
+hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s);
+hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
+
 // Largest M the weight-streaming W4A8 kernel takes; larger M is tiled.
 constexpr int64_t kSkinnyMaxM = 64;
 

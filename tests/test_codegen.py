@@ -1,0 +1,72 @@
+"""Guards on the generated gfx950 code of the large-GEMM kernel (compiled
+here to AMD assembly; no GPU needed).  Two silent regressions these catch:
+the accumulator array demoted to scratch memory (private segment), and the
+compiler waiting for every direct-to-LDS load (vmcnt(0)) inside the main
+loop, which serialises the 4-stage ring."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "conv_qgemm_amd", "csrc", "k_gemm_dma.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "k_gemm_dma.s"
+    from conv_qgemm_amd import build
+    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(asm):
+    """name -> body text for each k_gemm_dma instantiation."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*k_gemm_dma\S*):", asm, re.M):
+        end = asm.index(".Lfunc_end", m.end())
+        out[m.group(1)] = asm[m.end():end]
+    return out
+
+
+def _nonempty(ks):
+    assert len(ks) == 2, list(ks)
+    return ks
+
+
+def _main_loop(body):
+    lines = [ln.strip() for ln in body.splitlines() if ln.strip() and not ln.strip().startswith(";")]
+    mf = [i for i, ln in enumerate(lines) if "v_mfma" in ln]
+    start = max(i for i in range(mf[0]) if lines[i].startswith(".LBB"))
+    return lines[start:mf[-1] + 1]
+
+
+def test_no_scratch(asm):
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
+    assert sizes
+    ks = _kernels(asm)
+    assert len(ks) == 2
+    for name, body in ks.items():
+        loop = _main_loop(body)
+        assert not any("scratch_" in ln for ln in loop), name
+
+
+def test_main_loop_shape(asm):
+    for name, body in _nonempty(_kernels(asm)).items():
+        loop = _main_loop(body)
+        waits = [ln for ln in loop if ln.startswith("s_waitcnt")]
+        assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (name, waits)
+        assert sum("s_barrier" in ln for ln in loop) == 1, name
+        assert sum("global_load_lds_dwordx4" in ln for ln in loop) == 8, name
+        kind = 8 if "ILi8E" in name else 4
+        assert sum("v_mfma_i32_32x32x32_i8" in ln for ln in loop) == (32 if kind == 8 else 64), name
+
+
+def test_accumulators_not_spilled(asm):
+    for name, body in _nonempty(_kernels(asm)).items():
+        # every accumulator stays in registers: no acc-sized private segment
+        m = re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", body)
+        if m:
+            assert int(m.group(1)) < 256, name
