@@ -21,24 +21,29 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxGrid = (int64_t)1 << 24;
-// per-device verdict of the architecture check: 0 unknown, 1 gfx950, 2 other
+// per-device facts, filled once: architecture verdict (0 unknown, 1 gfx950,
+// 2 other) and compute-unit count
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-qg_status check_device()
+qg_status check_device(int *cus)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return QG_ERR_NO_DEVICE;
-    int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+    int v = g_arch_ok[dev].load(std::memory_order_acquire);
     if (v == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return QG_ERR_NO_DEVICE;
         v = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-        g_arch_ok[dev].store(v, std::memory_order_relaxed);
+        g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                         std::memory_order_relaxed);
+        g_arch_ok[dev].store(v, std::memory_order_release);
     }
+    *cus = g_cus[dev].load(std::memory_order_relaxed);
     return v == 1 ? QG_OK : QG_ERR_NO_DEVICE;
 }
 
@@ -97,9 +102,10 @@ qg_status qgemm_s8s8_requant(const int8_t *A, int64_t lda, const int8_t *B, int6
         st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if ((st = check_device()) != QG_OK)
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
         return st;
-    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K};
+    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, cus};
     return launched(qg::launch_s8s8_requant(d, (hipStream_t)stream));
 }
 
@@ -111,9 +117,10 @@ qg_status qgemm_s4s4_i32(const uint8_t *A, int64_t lda, const uint8_t *B, int64_
     qg_status st = check_gemm(A, lda, true, B, ldb, true, C, ldc, 4, M, N, K, QG_S4S4_MAX_K);
     if (st != QG_OK)
         return st;
-    if ((st = check_device()) != QG_OK)
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
         return st;
-    qg::GemmDesc d{A, lda / 2, B, ldb / 2, nullptr, nullptr, nullptr, C, ldc, M, N, K};
+    qg::GemmDesc d{A, lda / 2, B, ldb / 2, nullptr, nullptr, nullptr, C, ldc, M, N, K, cus};
     return launched(qg::launch_s4s4_i32(d, (hipStream_t)stream));
 }
 
@@ -129,9 +136,10 @@ qg_status qgemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int
         st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if ((st = check_device()) != QG_OK)
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
         return st;
-    qg::GemmDesc d{A, lda, B, ldb / 2, bias, mult, shift, C, ldc, M, N, K};
+    qg::GemmDesc d{A, lda, B, ldb / 2, bias, mult, shift, C, ldc, M, N, K, cus};
     if (M <= qg::kSkinnyMaxM)
         return launched(qg::launch_w4a8_skinny(d, (hipStream_t)stream));
     return launched(qg::launch_w4a8_tiled(d, (hipStream_t)stream));
@@ -166,7 +174,8 @@ qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_
     qg_status st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if ((st = check_device()) != QG_OK)
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
         return st;
     qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C_in, C_out, KH, KW,
                    stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo};

@@ -8,19 +8,32 @@
 // article §2.3; packed int4 operands: INT4 GEMM article,
 // www.cf-1.com/news/6060138, §2.1.)
 //
-// Layout of the work:
-//   * a workgroup is 8 waves; K is cut into 8 slices, one per wave, of up
-//     to 16 steps of 64 values, and the loop over K chunks of 8 slices
-//     covers any K;
-//   * each wave keeps its slice of the 16 activation rows in registers as
-//     v_mfma_i32_16x16x64_i8 operands, loaded once per chunk (once in total
-//     when K <= 8192) and byte-permuted to match the widened int4 order;
-//   * the workgroup walks a strided list of 16-column groups; for each, every
-//     wave streams its slice of the 16 weight rows with 16-byte loads (the
-//     next group's loads are issued before this group's MFMAs), widens the
-//     nibbles in registers and multiplies;
-//   * the 8 partial 16x16 sums meet in LDS; one wave (rotating) adds them,
-//     requantizes 4 adjacent columns per lane and stores one dword.
+// What the memory system wants, measured on MI355X: every wave-wide load
+// should cover 1 KB of contiguous bytes, and a CU should keep about one
+// 64 KB burst in flight -- deeper rings of outstanding loads run slower, not
+// faster (each XCD's L2 has to hold the lines in flight).  The MFMA operand
+// layout wants the opposite (one lane per weight row), so the weights pass
+// through LDS:
+//   * one workgroup of 8 waves per CU walks a strided list of 16-row column
+//     groups; a unit is one group times one K chunk of 8192 values
+//     (16 rows x 4 KB), and units alternate between two 64 KB LDS slots;
+//   * the direct-to-LDS load (global_load_lds_dwordx4) writes lane L's 16
+//     bytes at LDS offset 16*L of a 1 KB piece, so every load reads one
+//     contiguous KB of one weight row; lane L fetches granule L ^ row of that
+//     KB, which makes the reads below bank-conflict free;
+//   * wave w multiplies K values [1024w, 1024w+1024) of the chunk: per
+//     64-value step a lane needs 8 packed bytes of weight row lane%16, read
+//     from LDS 16 bytes (two steps) at a time, widened in registers
+//     (dev_common.hpp) and fed to v_mfma_i32_16x16x64_i8 with the
+//     activations as the second operand;
+//   * activations live in registers, loaded once when K <= 8192 and double-
+//     buffered per unit otherwise; values past the end of K are zeroed, so
+//     whatever sits in LDS there (clamped or stale bytes) adds nothing;
+//   * one barrier per unit: after it, this unit's bytes have landed for every
+//     wave and the other slot is free, so the next unit's loads go out at
+//     once; the 8 partial 16x16 sums of a finished group are added by one
+//     wave (rotating) behind the same barrier, requantized and kept in LDS
+//     until the end.
 #include "dev_common.hpp"
 #include "launch.hpp"
 
@@ -28,10 +41,24 @@ namespace qg {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 constexpr int kWaves = 8;
-constexpr int kSteps = 16;               // MFMA K steps (64 values) per wave slice
-constexpr int kLoads = kSteps / 2;       // 16-byte weight loads per lane per group
-constexpr int kChunk = kWaves * kSteps * 64;  // K values per chunk (8192)
+constexpr int kSteps = 16;                     // MFMA K steps (64 values) per wave per unit
+constexpr int kChunk = kWaves * kSteps * 64;   // K values per unit (8192)
+constexpr int kRowBytes = kChunk / 2;          // packed bytes per weight row per unit (4 KB)
+constexpr int kSlot = 16 * kRowBytes;          // 64 KB
+constexpr int kPieces = kRowBytes / 1024;      // 1 KB pieces per row per unit
+constexpr int kLoads = 16 * kPieces / kWaves;  // direct-to-LDS loads per wave per unit (8)
+constexpr int kMaxGroups = 32;                 // column groups per workgroup (LDS staging)
+
+// LDS map, one object so that the compiler sees one buffer
+constexpr int kRedOff = 2 * kSlot;                          // v4i red[2][kWaves][64]
+constexpr int kPrmOff = kRedOff + 2 * kWaves * 64 * 16;     // int prm[3][kMaxGroups*16]
+constexpr int kOutOff = kPrmOff + 3 * kMaxGroups * 16 * 4;  // unsigned outb[kMaxGroups][64]
+constexpr int kLdsBytes = kOutOff + kMaxGroups * 64 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 struct SkinnyArgs {
     const int8_t *A;
@@ -47,131 +74,186 @@ struct SkinnyArgs {
     int ngroups;  // ceil(N / 16)
 };
 
+// Wait until this wave's vector memory operations (the direct-to-LDS loads
+// included) and LDS operations are done, then meet the other waves.
+__device__ __forceinline__ void drain_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ONE: K fits one chunk, so the activations are loaded once.
+template <bool ONE>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
 {
-    __shared__ __attribute__((aligned(16))) v4i red[2][kWaves][64];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    v4i(*red)[kWaves][64] = (v4i(*)[kWaves][64])(lds + kRedOff);
+    int(*prm)[kMaxGroups * 16] = (int(*)[kMaxGroups * 16])(lds + kPrmOff);
+    unsigned(*outb)[64] = (unsigned(*)[64])(lds + kOutOff);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;  // weight row within the group / token index
     const int g = lane >> 4;    // 16-value group within a 64-value K step
-    const int t0 = blockIdx.y * 16;
-    const int tok = t0 + col;
-    const bool tok_ok = tok < p.M;
-    const int nchunks = (p.K + kChunk - 1) / kChunk;
+    const int tok = blockIdx.y * 16 + col;
+    const int nchunks = ONE ? 1 : (p.K + kChunk - 1) / kChunk;
     const int KbB = p.K / 2;
-    const v4i zero4 = {0, 0, 0, 0};
 
-    // value offset of (step s, group g) inside a wave slice: loads cover two
-    // steps, lane group g reading 32 consecutive values per load.
+    // groups of this workgroup: blockIdx.x + i * gridDim.x, i < ng
+    const int ng = (p.ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int nunits = ng * nchunks;  // (group, chunk) units, group-major
+
+    // ---- per-column parameters of this workgroup's columns into LDS ----
+    for (int c = tid; c < ng * 16; c += kWaves * 64) {
+        const int n = min(((int)blockIdx.x + (c >> 4) * (int)gridDim.x) * 16 + (c & 15), p.N - 1);
+        prm[0][c] = p.bias ? p.bias[n] : 0;
+        prm[1][c] = p.mult[n];
+        prm[2][c] = p.shift[n];
+    }
+
+    // ---- activations: token rows past M read row M-1 (never stored) ----
+    // value offset of (step s, lane group g) inside a wave's 1024 values: a
+    // 16-byte weight read covers two steps, lane group g taking 32 values
     auto kofs = [&](int s) { return (s >> 1) * 128 + g * 32 + (s & 1) * 16; };
-
-    v4i af[kSteps];
-    auto load_acts = [&](int chunk) {
+    const int8_t *arow = p.A + (int64_t)min(tok, p.M - 1) * p.lda;
+    auto load_acts = [&](int chunk, v4i(&af)[kSteps]) {
         const int kbase = chunk * kChunk + wave * (kSteps * 64);
-        const int8_t *arow = p.A + (int64_t)(tok_ok ? tok : 0) * p.lda;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            af[s] = *(const v4i *)(arow + min(kbase + kofs(s), p.K - 16));
+    };
+    // zero the values at or past K, then match the widened int4 order
+    auto fix_acts = [&](int chunk, v4i(&af)[kSteps]) {
+        const int kbase = chunk * kChunk + wave * (kSteps * 64);
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            const int k = kbase + kofs(s);
-            v4i q = (tok_ok && k < p.K) ? *(const v4i *)(arow + k) : zero4;
+            const int keep = kbase + kofs(s) < p.K ? -1 : 0;
+            v4i q = af[s];
+            for (int e = 0; e < 4; ++e)
+                q[e] &= keep;
             af[s] = even_odd_split(q);
         }
     };
 
-    // weights of the group being multiplied, and of the next one in flight
-    v4i wcur[kLoads], wnext[kLoads];
-    auto load_weights = [&](int grp, int chunk, v4i (&dst)[kLoads]) {
-        const int n = min(grp * 16 + col, p.N - 1);  // clamped columns are never stored
-        const uint8_t *brow = p.B + (int64_t)n * p.ldb_b;
-        const int kbase = chunk * kChunk + wave * (kSteps * 64);
+    // ---- direct-to-LDS loads of unit u into slot `slot` ----
+    // wave w loads rows 2w and 2w+1, kPieces KB each; a piece lying wholly
+    // past the end of the row is skipped (its LDS bytes meet zero
+    // activations), a piece crossing it reads clamped in-bounds addresses
+    auto issue = [&](int u, int slot) {
+        const int i = u / nchunks, c = u - i * nchunks;
+        const int grp = (int)blockIdx.x + i * (int)gridDim.x;
 #pragma unroll
         for (int l = 0; l < kLoads; ++l) {
-            const int kb = (kbase + l * 128 + g * 32) / 2;  // packed byte offset
-            dst[l] = kb < KbB ? *(const v4i *)(brow + kb) : zero4;
+            const int r = 2 * wave + l / kPieces, piece = l % kPieces;
+            const int kb0 = c * kRowBytes + piece * 1024;  // packed byte offset in the row
+            if (kb0 >= KbB)
+                continue;
+            const int n = min(grp * 16 + r, p.N - 1);  // clamped rows are never stored
+            const int kb = min(kb0 + ((lane ^ r) << 4), KbB - 16);
+            uint8_t *dst = lds + slot * kSlot + (r * kPieces + piece) * 1024;
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(p.B + (int64_t)n * p.ldb_b + kb),
+                                             (lds_void_t *)dst, 16, 0, 0);
         }
     };
 
-    if (nchunks == 1)
-        load_acts(0);
+    // ---- LDS read addresses of this lane's 8 16-byte weight fragments ----
+    // the fragment of steps 2l, 2l+1 is byte 512w + 64l + 16g of row `col`:
+    // piece w/2, granule 32(w&1) + 4l + g, stored at granule ^ col
+    int rd[kSteps / 2];
+#pragma unroll
+    for (int l = 0; l < kSteps / 2; ++l)
+        rd[l] = (col * kPieces + (wave >> 1)) * 1024 + ((((wave & 1) * 32 + 4 * l + g) ^ col) << 4);
 
-    int it = 0;
-    int grp = blockIdx.x;
-    if (grp < p.ngroups)
-        load_weights(grp, 0, wcur);
-    for (; grp < p.ngroups; grp += gridDim.x, ++it) {
-        v4i acc = zero4;
-        for (int chunk = 0; chunk < nchunks; ++chunk) {
-            if (nchunks > 1)
-                load_acts(chunk);
-            // prefetch the next (group, chunk) pair's weights
-            int ngrp = grp, nchunk = chunk + 1;
-            if (nchunk == nchunks) {
-                ngrp = grp + gridDim.x;
-                nchunk = 0;
-            }
-            if (ngrp < p.ngroups)
-                load_weights(ngrp, nchunk, wnext);
+    v4i acc = {0, 0, 0, 0};
+    auto consume = [&](int slot, const v4i(&af)[kSteps]) {
 #pragma unroll
-            for (int l = 0; l < kLoads; ++l) {
-                const v4i w = wcur[l];
-                v2u lo = {(unsigned)w[0], (unsigned)w[1]};
-                v2u hi = {(unsigned)w[2], (unsigned)w[3]};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(lo), af[2 * l], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(hi), af[2 * l + 1], acc, 0, 0, 0);
-            }
-#pragma unroll
-            for (int l = 0; l < kLoads; ++l)
-                wcur[l] = wnext[l];
+        for (int l = 0; l < kSteps / 2; ++l) {
+            const v4i wl = *(const v4i *)(lds + slot * kSlot + rd[l]);
+            const v2u lo = {(unsigned)wl[0], (unsigned)wl[1]};
+            const v2u hi = {(unsigned)wl[2], (unsigned)wl[3]};
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(lo), af[2 * l], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(hi), af[2 * l + 1], acc, 0,
+                                                        0, 0);
         }
-        // lane holds token t0 + lane%16 and columns grp*16 + 4*(lane/16) + e
-        red[it & 1][wave][lane] = acc;
-        __syncthreads();
-        if (wave == (it % kWaves)) {
-            v4i sum = red[it & 1][0][lane];
+    };
+
+    // one wave adds the 8 partial sums of group i and requantizes; the lane
+    // holds token lane%16 and columns 4*(lane/16) + e of the group
+    auto reduce = [&](int i) {
+        if (wave != i % kWaves)
+            return;
+        v4i sum = red[i & 1][0][lane];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) {
-                v4i v = red[it & 1][w][lane];
-                for (int e = 0; e < 4; ++e)
-                    sum[e] += v[e];
-            }
-            const int n = grp * 16 + 4 * g;
-            const bool vec = n + 3 < p.N && (p.ldc & 3) == 0;
-            int y[4];
-            for (int e = 0; e < 4; ++e) {
-                const int nn = min(n + e, p.N - 1);
-                const int b = p.bias ? p.bias[nn] : 0;
-                const int m = p.mult[nn];
-                const int s = p.shift[nn];
-                y[e] = requant_one(sum[e] >> 4, b, m, s, 1ll << ((s - 1) & 63));
-            }
-            if (tok_ok && n < p.N) {
-                int8_t *dst = p.C + (int64_t)tok * p.ldc + n;
-                if (vec) {
-                    *(unsigned *)dst = pack4_i8(y[0], y[1], y[2], y[3]);
-                } else {
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N)
-                            dst[e] = (int8_t)y[e];
-                }
-            }
+        for (int v = 1; v < kWaves; ++v) {
+            const v4i x = red[i & 1][v][lane];
+            for (int e = 0; e < 4; ++e)
+                sum[e] += x[e];
+        }
+        const v4i b4 = *(const v4i *)&prm[0][i * 16 + 4 * g];
+        const v4i m4 = *(const v4i *)&prm[1][i * 16 + 4 * g];
+        const v4i s4 = *(const v4i *)&prm[2][i * 16 + 4 * g];
+        int y[4];
+        for (int e = 0; e < 4; ++e)
+            y[e] = requant_one(sum[e] >> 4, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+        outb[i][lane] = pack4_i8(y[0], y[1], y[2], y[3]);
+    };
+
+    // unit u: its bytes are in slot u&1 and its activations in `af`; the
+    // next unit's loads (and activations, when K has several chunks) go out
+    // right after the barrier
+    v4i af0[kSteps], af1[kSteps];
+    auto step = [&](int u, int slot, v4i(&af)[kSteps], v4i(&af_next)[kSteps]) {
+        drain_and_barrier();
+        if (u + 1 < nunits) {
+            issue(u + 1, slot ^ 1);
+            if (!ONE)
+                load_acts((u + 1) % nchunks, af_next);
+        }
+        const int i = u / nchunks, c = u - i * nchunks;
+        if (!ONE)
+            fix_acts(c, af);
+        if (c == 0 && i > 0)
+            reduce(i - 1);
+        if (c == 0)
+            acc = (v4i){0, 0, 0, 0};
+        consume(slot, af);
+        if (c == nchunks - 1)
+            red[i & 1][wave][lane] = acc;
+    };
+
+    load_acts(0, af0);
+    if (ONE)
+        fix_acts(0, af0);
+    issue(0, 0);
+    for (int u = 0; u < nunits; u += 2) {
+        step(u, 0, af0, af1);
+        if (u + 1 < nunits) {
+            if (ONE)
+                step(u + 1, 1, af0, af1);
+            else
+                step(u + 1, 1, af1, af0);
         }
     }
-}
+    drain_and_barrier();
+    reduce(ng - 1);
 
-int num_cus()
-{
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cached = n;
-        else
-            return 256;
+    // ---- results: 16 tokens x 16 columns per group, one dword per lane ----
+    drain_and_barrier();
+    const bool tok_ok = tok < p.M;
+    for (int i = wave; i < ng; i += kWaves) {
+        const int n = ((int)blockIdx.x + i * (int)gridDim.x) * 16 + 4 * g;
+        if (!tok_ok || n >= p.N)
+            continue;
+        const unsigned v = outb[i][lane];
+        int8_t *dst = p.C + (int64_t)tok * p.ldc + n;
+        if (n + 3 < p.N && (p.ldc & 3) == 0) {
+            *(unsigned *)dst = v;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (n + e < p.N)
+                    dst[e] = (int8_t)(v >> (8 * e));
+        }
     }
-    return cached;
 }
 
 }  // namespace
@@ -192,9 +274,18 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
     a.N = (int)d.N;
     a.K = (int)d.K;
     a.ngroups = (int)((d.N + 15) / 16);
-    const int grid_x = a.ngroups < num_cus() ? a.ngroups : num_cus();
+    // one workgroup per CU, but never more than kMaxGroups groups each
+    int grid_x = d.cus;
+    if (grid_x * kMaxGroups < a.ngroups)
+        grid_x = (a.ngroups + kMaxGroups - 1) / kMaxGroups;
+    if (grid_x > a.ngroups)
+        grid_x = a.ngroups;
     const int grid_y = (int)((d.M + 15) / 16);
-    hipLaunchKernelGGL(k_skinny_w4a8, dim3(grid_x, grid_y), dim3(kWaves * 64), 0, s, a);
+    const dim3 grid(grid_x, grid_y), block(kWaves * 64);
+    if (d.K <= kChunk)
+        hipLaunchKernelGGL((k_skinny_w4a8<true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_skinny_w4a8<false>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

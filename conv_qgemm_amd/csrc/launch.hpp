@@ -20,6 +20,7 @@ struct GemmDesc {
     void *C;
     int64_t ldc;
     int64_t M, N, K;  // K in values
+    int cus;          // compute units of the current device
 };
 
 // One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,
