@@ -32,12 +32,12 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
-ORDER = ["pointwise", "s4s4", "conv3x3", "w4a8", "s8s8"]
+ORDER = ["pointwise", "w4a8", "conv3x3", "s4s4", "s8s8"]
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
 ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "w4a8": 5, "s8s8": 3}
 KERNEL_SOURCES = {
-    "s8s8": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
-    "s4s4": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
+    "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "pointwise": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "conv3x3": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
@@ -144,7 +144,7 @@ def cpu_baseline(names, frac=16):
     import oracle
     from conv_qgemm_amd import datagen
 
-    cores = len(os.sched_getaffinity(0))
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
     total_ops, total_t, parts = 0, 0.0, []
     for name in names:
@@ -196,7 +196,63 @@ def hbm_copy_gbs(torch, nbytes=1 << 30, iters=10):
     return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def _csv_rows(path):
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
+    for f in files:
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def summarize_trace(stats_csv, title, cmd):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel summary."""
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in _csv_rows(stats_csv):
+        if "AverageNs" not in r:
+            continue
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_pmc(name, fetch_dir, write_dir, copy_bytes=1 << 30):
+    """One traffic line for `name` from two rocprofv3 --pmc runs of
+    `bench.py --config name` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Every dispatch that is not a copy kernel belongs to the workload; the
+    1 GiB device copy of hbm_copy_gbs() in the same run calibrates the
+    counter (factor = known bytes / what the counter reads for that copy)."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        work, copies = [], []
+        for r in _csv_rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            (copies if "copy" in r["Kernel_Name"].lower() else work).append(v)
+        if not work or not copies:
+            raise SystemExit(f"no {counter} rows for the workload or the copy kernel in {d}")
+        calib = copy_bytes / max(copies)
+        out[counter] = (sum(work) / len(work), calib)
+    (f, cf), (w, cw) = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    total = f * cf + w * cw
+    return (f"traffic workload={name} src_sha={src_sha(KERNEL_SOURCES[name])} "
+            f"bytes_per_launch={int(total)} fetch_bytes_raw={int(f)} write_bytes_raw={int(w)} "
+            f"calib_fetch={cf:.4f} calib_write={cw:.4f}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        print(summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        print(summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -225,43 +281,61 @@ def main():
     cases = [Case(n, torch, qgemm, datagen) for n in names]
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        for c in cases:
-            c(i)
+    # Timed region: each workload runs as its own phase of W warm-up calls and
+    # K timed back-to-back calls on one stream (lightest workload first), so a
+    # workload is not measured in the power state that a previous, heavier
+    # one leaves behind.  A pair of HIP events on the launch stream brackets
+    # the K calls; the host runs ahead of the GPU, so the queue does not
+    # drain in between and the average is the per-launch GPU time.
+    stream = torch.cuda.current_stream()
+    batch, spread = {}, {}
     torch.cuda.synchronize()
-
-    ev = {c.name: [] for c in cases}
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        for c in cases:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
+    for c in cases:
+        for i in range(args.warmup):
             c(i)
-            b.record()
-            ev[c.name].append((a, b))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.steps):
+            c(i)
+        b.record(stream)
+        batch[c.name] = (a, b)
+        # 20 more calls with an event after each give the spread of single
+        # launches (median, max); they do not enter the average
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        marks[0].record(stream)
+        for i in range(20):
+            c(i)
+            marks[i + 1].record(stream)
+        spread[c.name] = marks
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_step = sum(a.elapsed_time(b) for a, b in batch.values()) * 1e-3 / args.steps
 
     per = {}
     total_ops = 0
     for c in cases:
-        times = sorted(a.elapsed_time(b) * 1e-3 for a, b in ev[c.name])
-        avg = sum(times) / len(times)
+        a, b = batch[c.name]
+        avg = a.elapsed_time(b) * 1e-3 / args.steps
+        m = spread[c.name]
+        times = sorted(m[i].elapsed_time(m[i + 1]) * 1e-3 for i in range(len(m) - 1))
         med = times[len(times) // 2]
-        p99 = times[min(len(times) - 1, int(0.99 * len(times)))]
+        p99 = times[-1]
         tops = c.ops / avg / 1e12
         gbs = c.bytes / avg / 1e9
-        per[c.name] = {"us_avg": round(avg * 1e6, 2), "us_median": round(med * 1e6, 2),
-                       "us_p99": round(p99 * 1e6, 2), "tops": round(tops, 2),
+        per[c.name] = {"us_avg": round(avg * 1e6, 2),
+                       "us_single_median": round(med * 1e6, 2),
+                       "us_single_max": round(p99 * 1e6, 2), "tops": round(tops, 2),
                        "gb_s": round(gbs, 1),
                        "pct_int8_mfma_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
                        "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                        "ops": c.ops, "alg_bytes": c.bytes,
                        "buffer_sets": ROTATE[c.name]}
         total_ops += c.ops
-    ms_per_step = wall / args.steps * 1e3
-    value = total_ops / (wall / args.steps) / 1e12
+    # one step = one timed call of every workload; warm-up calls are outside
+    ms_per_step = gpu_step * 1e3
+    value = total_ops / gpu_step / 1e12
 
     dom = max(per, key=lambda n: per[n]["us_avg"])
     mfma_bound = dom in ("s8s8", "s4s4", "conv3x3", "pointwise")
@@ -293,7 +367,12 @@ def main():
             {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
              "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
              "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
-                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..5"},
+                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..5",
+                   "timing": f"per workload: {args.warmup} warm-up + {args.steps} timed "
+                             f"back-to-back calls between two HIP events on the launch "
+                             f"stream; wall {wall:.3f} s for the whole timed region; "
+                             f"single-launch spread from 20 more calls with an event "
+                             f"after each"},
         "per_config": per,
         "roofline": roof,
     }

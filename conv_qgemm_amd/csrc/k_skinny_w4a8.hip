@@ -103,13 +103,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     const int ng = (p.ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int nunits = ng * nchunks;  // (group, chunk) units, group-major
 
-    // ---- per-column parameters of this workgroup's columns into LDS ----
-    for (int c = tid; c < ng * 16; c += kWaves * 64) {
-        const int n = min(((int)blockIdx.x + (c >> 4) * (int)gridDim.x) * 16 + (c & 15), p.N - 1);
-        prm[0][c] = p.bias ? p.bias[n] : 0;
-        prm[1][c] = p.mult[n];
-        prm[2][c] = p.shift[n];
-    }
+    // group i of this workgroup
+    auto group_of = [&](int i) { return (int)blockIdx.x + i * (int)gridDim.x; };
 
     // ---- activations: token rows past M read row M-1 (never stored) ----
     // value offset of (step s, lane group g) inside a wave's 1024 values: a
@@ -141,7 +136,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // activations), a piece crossing it reads clamped in-bounds addresses
     auto issue = [&](int u, int slot) {
         const int i = u / nchunks, c = u - i * nchunks;
-        const int grp = (int)blockIdx.x + i * (int)gridDim.x;
+        const int grp = group_of(i);
 #pragma unroll
         for (int l = 0; l < kLoads; ++l) {
             const int r = 2 * wave + l / kPieces, piece = l % kPieces;
@@ -221,10 +216,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
             red[i & 1][wave][lane] = acc;
     };
 
+    // ---- per-column parameters of this workgroup's columns into LDS ----
+    for (int c = tid; c < ng * 16; c += kWaves * 64) {
+        const int n = min(group_of(c >> 4) * 16 + (c & 15), p.N - 1);
+        prm[0][c] = p.bias ? p.bias[n] : 0;
+        prm[1][c] = p.mult[n];
+        prm[2][c] = p.shift[n];
+    }
     load_acts(0, af0);
+    issue(0, 0);
     if (ONE)
         fix_acts(0, af0);
-    issue(0, 0);
     for (int u = 0; u < nunits; u += 2) {
         step(u, 0, af0, af1);
         if (u + 1 < nunits) {
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     drain_and_barrier();
     const bool tok_ok = tok < p.M;
     for (int i = wave; i < ng; i += kWaves) {
-        const int n = ((int)blockIdx.x + i * (int)gridDim.x) * 16 + 4 * g;
+        const int n = group_of(i) * 16 + 4 * g;
         if (!tok_ok || n >= p.N)
             continue;
         const unsigned v = outb[i][lane];
