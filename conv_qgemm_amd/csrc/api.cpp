@@ -179,6 +179,8 @@ qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_
         return st;
     qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C_in, C_out, KH, KW,
                    stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo};
+    if (qg::conv_halo_fits(d))
+        return launched(qg::launch_conv_halo(d, (hipStream_t)stream));
     return launched(qg::launch_conv_nhwc(d, (hipStream_t)stream));
 }
 

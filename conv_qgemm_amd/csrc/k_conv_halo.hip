@@ -1,0 +1,347 @@
+// k_conv_halo.hip -- NHWC int8 conv with stride 1 and 64 input channels,
+// the input rows of a tile staged once in LDS, Q31 requantize fused.
+//
+// Method: the conv is a GEMM over an im2col matrix whose rows are output
+// pixels and whose K runs over (tap, input channel) (MCU conv front-end
+// article, news.rkmt.cn/news/16638, §3.2; geometry and zero padding §2.1,
+// §2.3; NHWC input and OHWI weights §3.1).  Walking K tap by tap makes the
+// 3x3 conv nine 1x1 convs over shifted inputs (Groq ResNet50 compilation
+// article, www.pwwt.cn/news/1982903, §2.1).  Nothing is materialized: every
+// tap reads the same input rows, so a workgroup stages those rows in LDS
+// once and reads all taps from there.
+//
+// Per workgroup (4 waves): 256 consecutive output pixels of one image times
+// 64 output channels.
+//   * the input rows those pixels touch (with the KH-1 halo rows) are read
+//     once with 16-byte loads and written to LDS with every pixel in 80
+//     bytes (64 channels + 16 unused), row by row with zero columns of
+//     padding on both sides and zero rows above and below the image: a tap
+//     of an output pixel is then one fixed LDS offset away from its (0, 0)
+//     tap, with no bounds test, and zero padding costs nothing;
+//   * 16 consecutive pixels at an 80-byte stride fall in 16 different LDS
+//     bank groups, so the operand reads are conflict free;
+//   * the workgroup's 64 weight rows (KH*KW*64 bytes each, OHWI) are copied
+//     with direct-to-LDS loads (global_load_lds_dwordx4, 1 KB of contiguous
+//     bytes per wave instruction), weight granule G of row oc stored at
+//     G ^ ((oc >> 2) & 3) of its 64-byte group for the same reason;
+//   * with 64 input channels one tap is exactly one K step of
+//     v_mfma_i32_16x16x64_i8: weights are the first operand (rows = output
+//     channels), pixels the second; each wave owns 64 pixels x 64 channels
+//     (4 x 4 MFMA tiles), and the operands of tap t+1 are read from LDS
+//     while tap t is multiplied;
+//   * the requantize uses the cheapest exact form that all 64 shifts of the
+//     workgroup allow; the int8 tile goes back to LDS and leaves with
+//     16-byte stores, contiguous when C_out == 64.
+// Two workgroups fit on a CU, so one stages its rows while the other
+// multiplies.
+#include <atomic>
+#include <type_traits>
+
+#include "dev_common.hpp"
+#include "launch.hpp"
+
+namespace qg {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int kTP = 256;     // output pixels per workgroup
+constexpr int kNT = 64;      // output channels per workgroup
+constexpr int kCin = 64;     // input channels = bytes per input pixel
+constexpr int kPixL = 80;    // LDS bytes per staged input pixel
+constexpr int kWaves = 4;
+constexpr int kMaxLds = 80 * 1024;  // two workgroups per CU
+constexpr int kMaxDevices = 64;
+
+struct HaloArgs {
+    const int8_t *X;
+    const int8_t *W;
+    const int32_t *bias;
+    const int32_t *mult;
+    const int32_t *shift;
+    int8_t *Y;
+    int H, Wd, C_out, ph, pw, Ho, Wo;
+    int tiles_per_img;
+    int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+};
+
+__device__ __forceinline__ void drain_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int KH, int KW>
+__global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
+{
+    constexpr int KK = KH * KW;
+    constexpr int kRowW = KK * kCin;  // bytes of one weight row (one output channel)
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t *IN = lds;
+    uint8_t *WT = lds + p.in_bytes;
+    int *prm = (int *)(WT + kNT * kRowW);  // bias, mult, shift [3][64]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int g = lane >> 4;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = bid / p.tiles_per_img, tile = bid - b * p.tiles_per_img;
+    const int HW = p.Ho * p.Wo;
+    const int p0 = tile * kTP, npix = min(kTP, HW - p0);
+    const int n0 = blockIdx.y * kNT;
+    const int oh_first = p0 / p.Wo, oh_last = (p0 + npix - 1) / p.Wo;
+    const int ih0 = oh_first - p.ph;  // input row of LDS row 0
+    const int ih_lo = max(ih0, 0), ih_hi = min(oh_last - p.ph + KH - 1, p.H - 1);
+    const int rowB = p.Wd * kCin;
+
+    // ---- per-channel parameters, loaded ahead of the bulk copies ----
+    int pb = 0, pm = 0, ps = 0;
+    if (tid < kNT) {
+        pb = p.bias ? p.bias[n0 + tid] : 0;
+        pm = p.mult[n0 + tid];
+        ps = p.shift[n0 + tid];
+    }
+
+    // ---- weight rows n0..n0+63 (OHWI, contiguous) -> LDS ----
+    {
+        const int8_t *src = p.W + (int64_t)n0 * kRowW;
+        constexpr int npieces = kNT * kRowW / 1024;
+        for (int P = wave; P < npieces; P += kWaves) {
+            const int pos = P * 1024 + 16 * lane;
+            const int oc = pos / kRowW;
+            const int G = (pos - oc * kRowW) >> 4;
+            const int sG = G ^ ((oc >> 2) & 3);
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(src + oc * kRowW + 16 * sG),
+                                             (lds_void_t *)(WT + P * 1024), 16, 0, 0);
+        }
+    }
+
+    // ---- input rows: LDS row r holds input row ih0 + r, LDS column c holds
+    //      input column c - pw; zero outside the image ----
+    const int colsL = p.Wd + 2 * p.pw;
+    const int rowL = colsL * kPixL;
+    const int nrow_in = oh_last - oh_first + KH;  // LDS rows this tile reads
+    // rows ih_lo..ih_hi are one contiguous NHWC span of 16-byte granules;
+    // a thread loads up to 8 of them per pass (loads past the end read the
+    // last granule and are not written), and the zero padding is written
+    // while the first pass is in flight
+    const int total = ih_lo <= ih_hi ? (ih_hi - ih_lo + 1) * p.Wd * 4 : 0;
+    const int8_t *src = p.X + ((int64_t)b * p.H + ih_lo) * rowB;
+    const int gpr = p.Wd * 4;  // granules per input row
+    for (int base = 0; base == 0 || base < total; base += 8 * kWaves * 64) {
+        v4i v[8];
+        if (total > 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = min(base + k * kWaves * 64 + tid, total - 1);
+                v[k] = *(const v4i *)(src + 16 * (int64_t)j);
+            }
+        }
+        if (base == 0) {
+            for (int e = tid; e < nrow_in * colsL; e += kWaves * 64) {
+                const int r = e / colsL, c = e - r * colsL;
+                const int ih = ih0 + r;
+                if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
+                    v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
+                    z[0] = z[1] = z[2] = z[3] = (v4i){0, 0, 0, 0};
+                }
+            }
+        }
+        if (total > 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = base + k * kWaves * 64 + tid;
+                if (j < total) {
+                    const int rr = j / gpr, rem = j - rr * gpr;
+                    const int r = ih_lo - ih0 + rr;
+                    *(v4i *)(IN + r * rowL + ((rem >> 2) + p.pw) * kPixL + 16 * (rem & 3)) = v[k];
+                }
+            }
+        }
+    }
+    drain_and_barrier();
+    if (tid < kNT) {
+        prm[tid] = pb;
+        prm[kNT + tid] = pm;
+        prm[2 * kNT + tid] = ps;
+    }
+    __syncthreads();
+
+    // ---- this lane's pixel in each of the wave's 4 M tiles, as the LDS
+    //      offset of its (0, 0) tap; pixels past the tile reuse the last one ----
+    int abase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = min(64 * wave + 16 * i + col, npix - 1);
+        const int pp = p0 + q;
+        const int oh = pp / p.Wo;
+        const int ow = pp - oh * p.Wo;
+        abase[i] = (oh - oh_first) * rowL + ow * kPixL + 16 * g;
+    }
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            acc[i][n] = (v4i){0, 0, 0, 0};
+
+    v4i a[2][4], w[2][4];
+    auto read_tap = [&](int t, v4i(&at)[4], v4i(&wt)[4]) {
+        const int kh = t / KW, kw = t - (t / KW) * KW;
+        const int toff = kh * rowL + kw * kPixL;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            at[i] = *(const v4i *)(IN + abase[i] + toff);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int oc = 16 * n + col;
+            const int G = 4 * t + g;
+            wt[n] = *(const v4i *)(WT + oc * kRowW + ((G ^ ((oc >> 2) & 3)) << 4));
+        }
+    };
+    read_tap(0, a[0], w[0]);
+#pragma unroll
+    for (int t = 0; t < KK; ++t) {
+        if (t + 1 < KK)
+            read_tap(t + 1, a[(t + 1) & 1], w[(t + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[t & 1][n], a[t & 1][i],
+                                                                 acc[i][n], 0, 0, 0);
+    }
+
+    // ---- requantize into LDS (the input rows are no longer needed) ----
+    __syncthreads();
+    // lane holds pixel 64*wave + 16*i + col and channels 16*n + 4*g + e; the
+    // requantize form is chosen once for the tile's 64 channels
+    const int sh_l = prm[2 * kNT + lane];
+    auto requant_tile = [&](auto tier_tag) {
+        constexpr int TIER = decltype(tier_tag)::value;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int c0 = 16 * n + 4 * g;
+            const v4i b4 = *(const v4i *)&prm[c0];
+            const v4i m4 = *(const v4i *)&prm[kNT + c0];
+            const v4i s4 = *(const v4i *)&prm[2 * kNT + c0];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int x = acc[i][n][e];
+                    if constexpr (TIER == 2)
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e]);
+                    else if constexpr (TIER == 1)
+                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                    else
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                }
+                const int q = 64 * wave + 16 * i + col;
+                *(unsigned *)(IN + q * 64 + c0) = pack4_i8(y[0], y[1], y[2], y[3]);
+            }
+        }
+    };
+    if (__builtin_amdgcn_ballot_w64(sh_l < 33) == 0)
+        requant_tile(std::integral_constant<int, 2>{});
+    else if (__builtin_amdgcn_ballot_w64(sh_l < 31) == 0)
+        requant_tile(std::integral_constant<int, 1>{});
+    else
+        requant_tile(std::integral_constant<int, 0>{});
+    __syncthreads();
+
+    // ---- 16-byte stores of the tile's npix x 64 output bytes ----
+    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C_out + n0;
+    for (int idx = tid; idx < npix * 4; idx += kWaves * 64) {
+        const int pix = idx >> 2, qq = idx & 3;
+        *(v4i *)(ybase + (int64_t)pix * p.C_out + 16 * qq) = *(const v4i *)(IN + pix * 64 + 16 * qq);
+    }
+}
+
+template <int KH, int KW>
+hipError_t run_halo(const HaloArgs &a, int batch, int lds_bytes, hipStream_t s)
+{
+    // the dynamic LDS limit above 64 KB is raised once per device
+    static std::atomic<bool> attr_set[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute((const void *)k_conv_halo<KH, KW>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (e != hipSuccess)
+            return e;
+        attr_set[dev].store(true, std::memory_order_release);
+    }
+    const dim3 grid(batch * a.tiles_per_img, a.C_out / kNT), block(kWaves * 64);
+    hipLaunchKernelGGL((k_conv_halo<KH, KW>), grid, block, lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+// LDS rows of the input region: the most output rows a tile of kTP
+// consecutive pixels touches, plus the KH-1 halo rows.
+int halo_rows(const ConvDesc &d)
+{
+    return (kTP - 1) / d.Wo + 2 + d.KH - 1;
+}
+
+// LDS bytes of the input-row region (at least the kTP x 64-byte output
+// staging), rounded up to 1 KB so that the weight rows start aligned.
+int64_t halo_in_bytes(const ConvDesc &d)
+{
+    int64_t in = (int64_t)halo_rows(d) * (d.Wd + 2 * d.pw) * kPixL;
+    if (in < (int64_t)kTP * 64)
+        in = (int64_t)kTP * 64;
+    return (in + 1023) & ~(int64_t)1023;
+}
+
+int64_t halo_lds_bytes(const ConvDesc &d)
+{
+    return halo_in_bytes(d) + (int64_t)kNT * d.KH * d.KW * kCin + 3 * kNT * 4;
+}
+
+}  // namespace
+
+bool conv_halo_fits(const ConvDesc &d)
+{
+    if (d.sh != 1 || d.sw != 1 || d.C_in != kCin || d.C_out % kNT != 0)
+        return false;
+    if (!((d.KH == 3 && d.KW == 3) || (d.KH == 1 && d.KW == 1)))
+        return false;
+    return halo_lds_bytes(d) <= kMaxLds;
+}
+
+hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s)
+{
+    HaloArgs a{};
+    a.X = d.X;
+    a.W = d.W;
+    a.bias = d.bias;
+    a.mult = d.mult;
+    a.shift = d.shift;
+    a.Y = d.Y;
+    a.H = d.H;
+    a.Wd = d.Wd;
+    a.C_out = d.C_out;
+    a.ph = d.ph;
+    a.pw = d.pw;
+    a.Ho = d.Ho;
+    a.Wo = d.Wo;
+    a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
+    a.in_bytes = (int)halo_in_bytes(d);
+    const int lds = (int)halo_lds_bytes(d);
+    if (d.KH == 3)
+        return run_halo<3, 3>(a, d.batch, lds, s);
+    return run_halo<1, 1>(a, d.batch, lds, s);
+}
+
+}  // namespace qg

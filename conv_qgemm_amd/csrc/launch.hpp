@@ -46,6 +46,11 @@ bool dma_gemm_fits(const GemmDesc &d, bool int4);
 hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
 
+// NHWC conv with stride 1 and 64 input channels, input rows staged in LDS
+// (k_conv_halo.hip); other convs use the implicit-im2col tile kernel
+bool conv_halo_fits(const ConvDesc &d);
+hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s);
+
 // Largest M the weight-streaming W4A8 kernel takes; larger M is tiled.
 constexpr int64_t kSkinnyMaxM = 64;
 

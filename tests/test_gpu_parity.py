@@ -198,6 +198,14 @@ CONV_GEOMS = [
     (1, 12, 13, 32, 128, 3, 3, (1, 1), (1, 1)),
     (1, 11, 9, 48, 80, 3, 3, (2, 2), (1, 1)),
     (1, 40, 32, 16, 16, 3, 3, (2, 2), (1, 1)),  # first layer of the MCU front-end, C_in padded to 16
+    # stride 1, 64 input channels: the kernel that stages input rows in LDS
+    (1, 12, 13, 64, 128, 3, 3, (1, 1), (1, 1)),   # two output-channel tiles
+    (2, 10, 9, 64, 64, 3, 3, (1, 1), (0, 0)),     # no padding
+    (1, 9, 30, 64, 192, 3, 3, (1, 1), (2, 0)),    # unequal padding, three channel tiles
+    (2, 40, 3, 64, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: a tile spans 86 rows
+    (1, 4, 100, 64, 64, 3, 3, (1, 1), (1, 1)),    # wide rows, near the LDS limit
+    (1, 5, 6, 64, 64, 1, 1, (1, 1), (1, 1)),      # 1x1 with padding: border pixels see zeros
+    (3, 17, 19, 64, 64, 3, 3, (1, 1), (1, 1)),    # several images, partial last tile
 ]
 
 
