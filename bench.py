@@ -14,8 +14,9 @@ L2-sized and reported hot).
 
 Prints ONE JSON line: whole-step int TOPS as `value`, per-workload times,
 TOPS, GB/s and fractions of the INT8 MFMA and HBM peaks, the roofline of the
-dominant kernel (per-launch HIP events on the launch stream), and the CPU
-oracle timed on a bounded sample of the same step.
+dominant kernel (HIP events on the launch stream around a graph replay of
+the timed calls), and the CPU oracle timed on a bounded sample of the same
+step.
 """
 from __future__ import annotations
 
@@ -281,43 +282,59 @@ def main():
     cases = [Case(n, torch, qgemm, datagen) for n in names]
     torch.cuda.synchronize()
 
-    # Timed region: each workload runs as its own phase of W warm-up calls and
-    # K timed back-to-back calls on one stream (lightest workload first), so a
-    # workload is not measured in the power state that a previous, heavier
-    # one leaves behind.  A pair of HIP events on the launch stream brackets
-    # the K calls; the host runs ahead of the GPU, so the queue does not
-    # drain in between and the average is the per-launch GPU time.
+    # Timed region: each workload runs as its own phase, lightest first, so
+    # that a workload is not measured in the power state a heavier one leaves
+    # behind.  A phase is W warm-up calls, then K back-to-back eager calls
+    # between two HIP events on the launch stream, then the same K calls
+    # captured once in a HIP graph and replayed (one untimed replay, one timed
+    # between events).  The graph replay is the per-launch GPU time without
+    # the Python binding's per-call host cost, which decides the launch-bound
+    # pointwise case and is hidden behind the GPU for the others.
     stream = torch.cuda.current_stream()
-    batch, spread = {}, {}
+    eager, graphed, spread = {}, {}, {}
+
+    def timed(fn):
+        s0 = torch.cuda.current_stream()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s0)
+        fn()
+        b.record(s0)
+        return a, b
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for c in cases:
         for i in range(args.warmup):
             c(i)
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(args.steps):
-            c(i)
-        b.record(stream)
-        batch[c.name] = (a, b)
-        # 20 more calls with an event after each give the spread of single
-        # launches (median, max); they do not enter the average
+        eager[c.name] = timed(lambda: [c(i) for i in range(args.steps)])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                c(i)
+        g.replay()
+        graphed[c.name] = timed(g.replay)
+        # 20 more eager calls with an event after each give the spread of
+        # single launches (median, max); they enter no average
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
         marks[0].record(stream)
         for i in range(20):
             c(i)
             marks[i + 1].record(stream)
         spread[c.name] = marks
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        del g
     wall = time.perf_counter() - t0
-    gpu_step = sum(a.elapsed_time(b) for a, b in batch.values()) * 1e-3 / args.steps
+    gpu_step = sum(a.elapsed_time(b) for a, b in graphed.values()) * 1e-3 / args.steps
 
     per = {}
     total_ops = 0
     for c in cases:
-        a, b = batch[c.name]
+        a, b = graphed[c.name]
         avg = a.elapsed_time(b) * 1e-3 / args.steps
+        a, b = eager[c.name]
+        avg_eager = a.elapsed_time(b) * 1e-3 / args.steps
         m = spread[c.name]
         times = sorted(m[i].elapsed_time(m[i + 1]) * 1e-3 for i in range(len(m) - 1))
         med = times[len(times) // 2]
@@ -325,6 +342,7 @@ def main():
         tops = c.ops / avg / 1e12
         gbs = c.bytes / avg / 1e9
         per[c.name] = {"us_avg": round(avg * 1e6, 2),
+                       "us_avg_eager": round(avg_eager * 1e6, 2),
                        "us_single_median": round(med * 1e6, 2),
                        "us_single_max": round(p99 * 1e6, 2), "tops": round(tops, 2),
                        "gb_s": round(gbs, 1),
@@ -368,11 +386,13 @@ def main():
              "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
              "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
                    "parallelism": "single GPU", "seeds": "numpy PCG64 1..5",
-                   "timing": f"per workload: {args.warmup} warm-up + {args.steps} timed "
-                             f"back-to-back calls between two HIP events on the launch "
-                             f"stream; wall {wall:.3f} s for the whole timed region; "
-                             f"single-launch spread from 20 more calls with an event "
-                             f"after each"},
+                   "timing": f"per workload: {args.warmup} warm-up calls, then "
+                             f"{args.steps} back-to-back calls captured in a HIP graph "
+                             f"and replayed between two HIP events (us_avg; value and "
+                             f"roofline use it), and the same {args.steps} calls issued "
+                             f"eagerly from Python (us_avg_eager); single-launch spread "
+                             f"from 20 more eager calls; wall {wall:.3f} s for all "
+                             f"phases"},
         "per_config": per,
         "roofline": roof,
     }

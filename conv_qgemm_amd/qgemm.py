@@ -86,11 +86,22 @@ def _check(status: int, what: str):
         raise QGemmError(status, what)
 
 
+def _on_device(t, name):
+    """The library launches on the current HIP device: every tensor must live
+    there (a host or foreign-device pointer would reach the kernels)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
 def _mat(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    _on_device(t, name)
     return t
 
 
@@ -99,6 +110,7 @@ def _vec(t, n, name):
         return None
     if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < n or t.stride(0) != 1:
         raise ValueError(f"{name} must be a contiguous int32 vector of length >= {n}")
+    _on_device(t, name)
     return t
 
 
@@ -178,6 +190,8 @@ def qconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1), 
         raise TypeError("X and W must be int8")
     if X.dim() != 4 or W.dim() != 4 or not X.is_contiguous() or not W.is_contiguous():
         raise ValueError("X [B,H,W,C_in] and W [C_out,KH,KW,C_in] must be contiguous 4-D")
+    _on_device(X, "X")
+    _on_device(W, "W")
     batch, H, Wd, C_in = X.shape
     C_out, KH, KW, C_in2 = W.shape
     if C_in2 != C_in:
@@ -188,6 +202,7 @@ def qconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1), 
                         device=X.device)
     if not Y.is_contiguous() or Y.dtype != torch.int8 or tuple(Y.shape) != (batch, Ho, Wo, C_out):
         raise ValueError("Y must be a contiguous int8 [batch, H_out, W_out, C_out] tensor")
+    _on_device(Y, "Y")
     st = lib.qconv2d_nhwc_s8_requant(_ptr(X), _ptr(W), _ptr(_vec(bias, C_out, "bias")),
                                      _ptr(_vec(mult, C_out, "mult")),
                                      _ptr(_vec(shift, C_out, "shift")), _ptr(Y),

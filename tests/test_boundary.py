@@ -157,3 +157,24 @@ def test_binding_rejects_bad_tensors(qg):
     with pytest.raises(ValueError):
         qg.qconv2d_nhwc_s8_requant(X, W, None, torch.zeros(16, dtype=torch.int32),
                                    torch.zeros(16, dtype=torch.int32))
+
+
+def test_binding_rejects_host_tensors(qg):
+    """Well-formed tensors in host memory never reach the library: their
+    pointers are not device addresses."""
+    import torch
+    A = torch.zeros((4, 32), dtype=torch.int8)
+    v = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qg.qgemm_s8s8_requant(A, A, v, v, v, C=torch.zeros((4, 4), dtype=torch.int8))
+    P = torch.zeros((4, 16), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qg.qgemm_s4s4_i32(P, P, C=torch.zeros((4, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qg.qgemm_w4a8_requant(A, P, v, v, v, C=torch.zeros((4, 4), dtype=torch.int8))
+    X = torch.zeros((1, 4, 4, 16), dtype=torch.int8)
+    W = torch.zeros((16, 3, 3, 16), dtype=torch.int8)
+    v16 = torch.zeros(16, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qg.qconv2d_nhwc_s8_requant(X, W, v16, v16, v16, Y=torch.zeros((1, 4, 4, 16),
+                                                                     dtype=torch.int8))

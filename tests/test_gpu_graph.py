@@ -1,0 +1,140 @@
+"""The four entry points inside a captured HIP graph (torch.cuda.CUDAGraph).
+
+The library only enqueues kernels on the caller's stream (no allocation, no
+memset, no synchronization), so a caller can capture a sequence of calls and
+replay it.  Every replay here runs with the program's own eager work and a
+synchronization in between, and is compared bit for bit with the eager
+result; the inputs are also rewritten in place between replays, which the
+replay must see.
+"""
+import numpy as np
+import pytest
+
+from conv_qgemm_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+@pytest.fixture(scope="module")
+def qg():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from conv_qgemm_amd import qgemm
+    return qgemm
+
+
+def _run_graph_case(torch, make_inputs, call):
+    """make_inputs(seed) -> dict of device tensors (inputs and the output 'out');
+    call(d) enqueues the library call writing d['out']."""
+    d = make_inputs(1)
+    call(d)  # eager first: one-time device setup happens outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(d)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        # new input contents in the captured buffers, eager reference beside
+        fresh = make_inputs(10 + r)
+        for k, v in fresh.items():
+            if k != "out":
+                d[k].copy_(v)
+        ref = {k: v.clone() for k, v in d.items()}
+        ref["out"] = torch.empty_like(d["out"])
+        call(ref)
+        d["out"].fill_(7)
+        junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"].cpu(), ref["out"].cpu()), f"replay {r} differs from eager"
+        del junk
+
+
+def test_graph_s8s8(qg):
+    import torch
+
+    def make(seed):
+        h = datagen.gemm_s8s8(70, 96, 160, seed, shift=(36, 42))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((70, 96), dtype=torch.int8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_s8s8_requant(
+        d["A"], d["B"], d["bias"], d["mult"], d["shift"], C=d["out"]))
+
+
+def test_graph_s8s8_large_tile(qg):
+    """The direct-to-LDS ring kernel (enough tiles to take that path)."""
+    import torch
+
+    def make(seed):
+        h = datagen.gemm_s8s8(4096, 2048, 256, seed, shift=(40, 46))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((4096, 2048), dtype=torch.int8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_s8s8_requant(
+        d["A"], d["B"], d["bias"], d["mult"], d["shift"], C=d["out"]))
+
+
+def test_graph_s4s4(qg):
+    import torch
+
+    def make(seed):
+        h = datagen.gemm_s4s4(64, 80, 256, seed)
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((64, 80), dtype=torch.int32, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_s4s4_i32(d["A"], d["B"], C=d["out"]))
+
+
+def test_graph_w4a8_skinny(qg):
+    import torch
+
+    def make(seed):
+        h = datagen.gemm_w4a8(16, 512, 1024, seed, shift=(36, 42))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((16, 512), dtype=torch.int8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_w4a8_requant(
+        d["A"], d["B"], d["bias"], d["mult"], d["shift"], C=d["out"]))
+
+
+@pytest.mark.parametrize("C_in", [64, 32])
+def test_graph_conv(qg, C_in):
+    """C_in 64 takes the LDS-staged kernel, C_in 32 the implicit-im2col one."""
+    import torch
+
+    def make(seed):
+        h = datagen.conv_nhwc(2, 9, 11, C_in, 64, 3, 3, seed, shift=(36, 42))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((2, 9, 11, 64), dtype=torch.int8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qconv2d_nhwc_s8_requant(
+        d["X"], d["W"], d["bias"], d["mult"], d["shift"], stride=(1, 1), pad=(1, 1),
+        Y=d["out"]))
+
+
+def test_graph_matches_oracle(qg, orc):
+    """One replayed result also checked against the oracle directly."""
+    import torch
+    h = datagen.gemm_s8s8(33, 48, 64, 3, shift=(36, 42))
+    d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+    C = torch.empty((33, 48), dtype=torch.int8, device="cuda")
+    qg.qgemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], C=C)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qg.qgemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], C=C)
+    C.fill_(0)
+    g.replay()
+    torch.cuda.synchronize()
+    want = orc.gemm_s8s8_requant(h["A"], h["B"], h["bias"], h["mult"], h["shift"])
+    assert np.array_equal(C.cpu().numpy(), want)
