@@ -165,12 +165,55 @@ def test_s4s4_extremes(qg):
     assert C[0, 1] == 64 * K and C[0, 0] == -56 * K
 
 
+def test_s4s4_max_k(qg):
+    """K at the API bound (131040): +-8 x +-8 products summed over K, scaled
+    by 256 inside the kernel, sit right at the int32 edge."""
+    M, N, K = 64, 64, 131040
+    A = np.full((M, K // 2), 0x88, np.uint8)  # all -8
+    B = np.full((N, K // 2), 0x88, np.uint8)
+    B[1::2] = 0x77                             # all 7
+    g = np.random.default_rng(11)
+    A[5:] = g.integers(0, 256, size=(M - 5, K // 2), dtype=np.uint8)
+    C = host(qg.qgemm_s4s4_i32(dev(A), dev(B)))
+    assert C[0, 0] == 64 * K and C[0, 1] == -56 * K
+    assert np.array_equal(C, oracle.gemm_s4s4_i32(A, B))
+
+
+def test_s4s4_max_k_ring_kernel(qg):
+    """The largest K (a multiple of 128) that the direct-to-LDS ring kernel
+    takes, on enough tiles to select it; constant operands give closed forms."""
+    M, N, K = 2048, 4096, 130944
+    A = torch.full((M, K // 2), 0x88, dtype=torch.uint8, device="cuda")
+    B = torch.full((N, K // 2), 0x88, dtype=torch.uint8, device="cuda")
+    B[1::2] = 0x77
+    C = host(qg.qgemm_s4s4_i32(A, B))
+    assert np.all(C[:, 0::2] == 64 * K) and np.all(C[:, 1::2] == -56 * K)
+
+
 # ---------------------------------------------------------------- w4a8
 
 W4_SHAPES = [
     (1, 16, 32), (5, 100, 544), (16, 64, 8192), (16, 1000, 8224), (16, 48, 16416),
     (33, 77, 256), (64, 32, 512), (65, 130, 160), (300, 260, 640),
 ]
+
+
+@pytest.mark.parametrize("M", [16, 100])
+def test_w4a8_max_k(qg, M):
+    """K at the API bound (131040) with -128 activations against -8 / 7
+    weights: the x16-scaled accumulator sits right at the int32 edge (M = 16
+    is the weight-streaming kernel, M = 100 the tile kernel)."""
+    N, K = 64, 131040
+    g = np.random.default_rng(12)
+    A = np.full((M, K), -128, np.int8)
+    A[3:] = g.integers(-128, 128, size=(M - 3, K), dtype=np.int8)
+    B = np.full((N, K // 2), 0x88, np.uint8)
+    B[1::2] = 0x77
+    bias = g.integers(-2 ** 15, 2 ** 15, size=N, dtype=np.int32)
+    mult = g.integers(2 ** 30, 2 ** 31, size=N, dtype=np.int64).astype(np.int32)
+    shift = g.integers(44, 53, size=N, dtype=np.int32)
+    C = qg.qgemm_w4a8_requant(dev(A), dev(B), dev(bias), dev(mult), dev(shift))
+    assert np.array_equal(host(C), oracle.gemm_w4a8_requant(A, B, bias, mult, shift))
 
 
 @pytest.mark.parametrize("M,N,K", W4_SHAPES)
