@@ -77,6 +77,12 @@ def _load():
     lib.orc_conv2d_acc.restype = ctypes.c_int
     lib.orc_conv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I64] * 11 + [P, I64]
     lib.orc_conv2d_nhwc_s8_requant.restype = ctypes.c_int
+    lib.orc_dwconv_macs.argtypes = [I64] * 10
+    lib.orc_dwconv_macs.restype = I64
+    lib.orc_dwconv2d_acc.argtypes = [P, P] + [I64] * 10 + [P, I64, P]
+    lib.orc_dwconv2d_acc.restype = ctypes.c_int
+    lib.orc_dwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I64] * 10 + [P, I64]
+    lib.orc_dwconv2d_nhwc_s8_requant.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
     lib.orc_max_threads.argtypes = []
@@ -270,4 +276,56 @@ def conv2d_nhwc_s8_requant(X, Wt, bias, mult, shift, stride=(1, 1), pad=(1, 1), 
     _check(st, "conv2d_nhwc_s8_requant")
     if pix is None:
         return Y.reshape(batch, Ho, Wo, C_out)
+    return Y
+
+
+# ---- depthwise conv: weights [KH][KW][C] (one input channel per output) ----
+
+def dwconv_macs(batch, H, W, C, KH, KW, sh, sw, ph, pw) -> int:
+    return int(_load().orc_dwconv_macs(*(int(v) for v in (batch, H, W, C, KH, KW,
+                                                            sh, sw, ph, pw))))
+
+
+def _dw_geom(X, Wt, stride, pad):
+    X = _c(X, np.int8)
+    Wt = _c(Wt, np.int8)
+    batch, H, W, C = X.shape
+    KH, KW, C2 = Wt.shape
+    assert C2 == C
+    sh, sw = stride
+    ph, pw = pad
+    Ho = conv_out_size(H, KH, sh, ph)
+    Wo = conv_out_size(W, KW, sw, pw)
+    return X, Wt, (batch, H, W, C, KH, KW, sh, sw, ph, pw), Ho, Wo
+
+
+def dwconv2d_acc(X, Wt, stride=(1, 1), pad=(1, 1), pix=None):
+    """int64 accumulators of a depthwise NHWC conv (Wt [KH, KW, C]); returns
+    [batch, Ho, Wo, C] or [npix, C]."""
+    X, Wt, g, Ho, Wo = _dw_geom(X, Wt, stride, pad)
+    batch, C = g[0], g[3]
+    r, nr = _rows(pix, batch * Ho * Wo)
+    out = np.zeros((nr, C), dtype=np.int64)
+    _check(_load().orc_dwconv2d_acc(X.ctypes.data, Wt.ctypes.data, *g, _ptr(r), nr,
+                                    out.ctypes.data), "dwconv2d_acc")
+    if pix is None:
+        return out.reshape(batch, Ho, Wo, C)
+    return out
+
+
+def dwconv2d_nhwc_s8_requant(X, Wt, bias, mult, shift, stride=(1, 1), pad=(1, 1), pix=None):
+    """Requantized int8 depthwise NHWC conv; returns [batch, Ho, Wo, C] or [npix, C]."""
+    X, Wt, g, Ho, Wo = _dw_geom(X, Wt, stride, pad)
+    batch, C = g[0], g[3]
+    bias_c = None if bias is None else _c(bias, np.int32)
+    mult = _c(mult, np.int32)
+    shift = _c(shift, np.int32)
+    r, nr = _rows(pix, batch * Ho * Wo)
+    Y = np.zeros((nr, C), dtype=np.int8)
+    st = _load().orc_dwconv2d_nhwc_s8_requant(X.ctypes.data, Wt.ctypes.data, _ptr(bias_c),
+                                              mult.ctypes.data, shift.ctypes.data,
+                                              Y.ctypes.data, *g, _ptr(r), nr)
+    _check(st, "dwconv2d_nhwc_s8_requant")
+    if pix is None:
+        return Y.reshape(batch, Ho, Wo, C)
     return Y

@@ -18,7 +18,9 @@
  *                  shift, saturate; symmetric zero point 0; padding equals
  *                  the zero point), §3.1 (NHWC activations, weights
  *                  [out][kh][kw][in]), §3.2 (conv as C = A x B over an
- *                  im2col matrix), §3.3 (bias enters the requantize step).
+ *                  im2col matrix), §3.3 (bias enters the requantize step;
+ *                  the depthwise conv: one input channel per output
+ *                  channel, weights [kh][kw][c]).
  *
  * Readings where the pages are silent or contradict themselves:
  *   - packed INT4: element 2i is the LOW nibble of byte i, element 2i+1 the
@@ -282,6 +284,94 @@ int orc_conv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
             int8_t y = 0;
             status |= orc_requant(acc, bias ? bias[oc] : 0, mult[oc], shift[oc], &y);
             Y[r * C_out + oc] = y;
+        }
+    }
+    return status;
+}
+
+/* ---- depthwise NHWC conv ([MCU-CONV] §3.3): every channel is convolved
+ * on its own, input channel c feeding only output channel c; the weights are
+ * [KH][KW][C], tap-major with the channels innermost, as that section's
+ * per-channel kernel walks them; positions outside the image are the zero
+ * point 0 ([MCU-CONV] §2.3). ---- */
+
+/* MACs = out_w * out_h * C * k_w * k_h per image: the [MCU-CONV] §2.1
+ * count with one input channel per output channel. */
+int64_t orc_dwconv_macs(int64_t batch, int64_t H, int64_t W, int64_t C, int64_t KH, int64_t KW,
+                        int64_t sh, int64_t sw, int64_t ph, int64_t pw)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    return batch * Ho * Wo * C * KH * KW;
+}
+
+static int64_t dwconv_acc_at(const int8_t *X, const int8_t *Wt,
+                             int64_t H, int64_t W, int64_t C,
+                             int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                             int64_t ph, int64_t pw,
+                             int64_t b, int64_t oh, int64_t ow, int64_t c)
+{
+    int64_t acc = 0;
+    for (int64_t kh = 0; kh < KH; ++kh) {
+        const int64_t ih = oh * sh + kh - ph;
+        for (int64_t kw = 0; kw < KW; ++kw) {
+            const int64_t iw = ow * sw + kw - pw;
+            if (ih < 0 || ih >= H || iw < 0 || iw >= W)
+                continue; /* padded tap: input value is the zero point 0 */
+            const int64_t x = X[((b * H + ih) * W + iw) * C + c];
+            const int64_t w = Wt[(kh * KW + kw) * C + c];
+            acc += x * w;
+        }
+    }
+    return acc;
+}
+
+/* Raw depthwise accumulators of the selected output pixels; out is
+ * [npix][C].  Pixel index p = (b * H_out + oh) * W_out + ow; pix == NULL
+ * means 0..npix-1. */
+int orc_dwconv2d_acc(const int8_t *X, const int8_t *Wt,
+                     int64_t batch, int64_t H, int64_t W, int64_t C,
+                     int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                     const int64_t *pix, int64_t npix, int64_t *out)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    (void)batch;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t c = 0; c < C; ++c)
+            out[r * C + c] = dwconv_acc_at(X, Wt, H, W, C, KH, KW, sh, sw, ph, pw, b, oh, ow, c);
+    }
+    return ORC_OK;
+}
+
+/* Depthwise conv followed by the per-channel requantize; Y is [npix][C]. */
+int orc_dwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
+                                 const int32_t *bias, const int32_t *mult,
+                                 const int32_t *shift, int8_t *Y,
+                                 int64_t batch, int64_t H, int64_t W, int64_t C,
+                                 int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                                 int64_t ph, int64_t pw, const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    int status = ORC_OK;
+    (void)batch;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(| : status)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t acc = dwconv_acc_at(X, Wt, H, W, C, KH, KW, sh, sw, ph, pw, b, oh, ow, c);
+            int8_t y = 0;
+            status |= orc_requant(acc, bias ? bias[c] : 0, mult[c], shift[c], &y);
+            Y[r * C + c] = y;
         }
     }
     return status;

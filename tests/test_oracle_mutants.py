@@ -12,7 +12,8 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_int4.py", "tests/test_oracle_requant.py",
-             "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py",
+             "tests/test_oracle_dwconv.py"]
 
 MUTANTS = {
     "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
@@ -32,6 +33,12 @@ MUTANTS = {
     "conv_weight_transposed": ("Wt[((oc * KH + kh) * KW + kw) * C_in + ci]",
                                "Wt[((oc * KW + kw) * KH + kh) * C_in + ci]"),
     "conv_out_size": ("return span / stride + 1;", "return span / stride;"),
+    "dw_pad_offset": ("const int64_t ih = oh * sh + kh - ph;", "const int64_t ih = oh * sh + kh;"),
+    "dw_weight_layout": ("Wt[(kh * KW + kw) * C + c]", "Wt[c * KH * KW + kh * KW + kw]"),
+    "dw_channel_mix": ("X[((b * H + ih) * W + iw) * C + c]",
+                       "X[((b * H + ih) * W + iw) * C + (c + 1) % C]"),
+    "dw_tap_dropped": ("for (int64_t kw = 0; kw < KW; ++kw) {\n            const int64_t iw",
+                       "for (int64_t kw = 0; kw + 1 < KW; ++kw) {\n            const int64_t iw"),
 }
 
 
