@@ -6,6 +6,7 @@ One step is one call of every entry point on its workload:
   s4s4       qgemm_s4s4_i32      M=N=K=4096, raw int32 out
   conv3x3    qconv2d_nhwc_s8_requant  batch 32, 56x56, 64->64, 3x3 s1 p1
   w4a8       qgemm_w4a8_requant  M=16 tokens, K=8192, N=28672 (skinny)
+  dw3x3      qdwconv2d_nhwc_s8_requant  batch 32, 56x56, 64 channels, 3x3 s1 p1
   s8s8       qgemm_s8s8_requant  M=N=K=8192
 Inputs are seeded synthetic arrays resident in HBM before timing starts.
 Each workload rotates through enough copies of its buffers that every call
@@ -33,15 +34,16 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
-ORDER = ["pointwise", "w4a8", "conv3x3", "s4s4", "s8s8"]
+ORDER = ["pointwise", "dw3x3", "w4a8", "conv3x3", "s4s4", "s8s8"]
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
-ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "w4a8": 5, "s8s8": 3}
+ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "dw3x3": 40, "w4a8": 5, "s8s8": 3}
 KERNEL_SOURCES = {
     "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "pointwise": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "conv3x3": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
+    "dw3x3": "conv_qgemm_amd/csrc/k_dwconv.hip",
 }
 
 
@@ -54,6 +56,13 @@ def ops_and_bytes(name):
     """(int ops = 2 * MACs, algorithmic bytes: inputs once, outputs once,
     plus 12 bytes per output channel of bias / multiplier / shift)."""
     w = shape_of(name)
+    if w["kind"] == "dwconv":
+        Ho, Wo = w["H"], w["W"]  # 3x3 s1 p1 keeps the size
+        pix = w["batch"] * Ho * Wo
+        macs = pix * w["C"] * w["KH"] * w["KW"]
+        by = w["batch"] * w["H"] * w["W"] * w["C"] + w["KH"] * w["KW"] * w["C"] + \
+            12 * w["C"] + pix * w["C"]
+        return 2 * macs, by
     if w["kind"] == "conv":
         Ho, Wo = w["H"], w["W"]  # 3x3 s1 p1 keeps the size
         pix = w["batch"] * Ho * Wo
@@ -117,6 +126,9 @@ class Case:
             if w["kind"] == "conv":
                 s["Y"] = torch.empty((w["batch"], w["H"], w["W"], w["C_out"]), dtype=torch.int8,
                                      device="cuda")
+            elif w["kind"] == "dwconv":
+                s["Y"] = torch.empty((w["batch"], w["H"], w["W"], w["C"]), dtype=torch.int8,
+                                     device="cuda")
             elif w["kind"] == "s4s4":
                 s["C"] = torch.empty((w["M"], w["N"]), dtype=torch.int32, device="cuda")
             else:
@@ -131,6 +143,9 @@ class Case:
             return q.qgemm_s4s4_i32(s["A"], s["B"], C=s["C"])
         if self.name == "w4a8":
             return q.qgemm_w4a8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
+        if self.name == "dw3x3":
+            return q.qdwconv2d_nhwc_s8_requant(s["X"], s["W"], s["bias"], s["mult"], s["shift"],
+                                               stride=(1, 1), pad=(1, 1), Y=s["Y"])
         if self.name == "conv3x3":
             return q.qconv2d_nhwc_s8_requant(s["X"], s["W"], s["bias"], s["mult"], s["shift"],
                                              stride=(1, 1), pad=(1, 1), Y=s["Y"])
@@ -166,6 +181,12 @@ def cpu_baseline(names, frac=16):
             oracle.gemm_w4a8_requant(d["A"], d["B"][cols], d["bias"][cols], d["mult"][cols],
                                      d["shift"][cols])
             part = len(cols) / w["N"]
+        elif w["kind"] == "dwconv":
+            npix = w["batch"] * w["H"] * w["W"]
+            pix = np.arange(0, npix, frac)
+            oracle.dwconv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                            pix=pix)
+            part = len(pix) / npix
         else:
             npix = w["batch"] * w["H"] * w["W"]
             pix = np.arange(0, npix, frac)
@@ -384,6 +405,7 @@ def main():
         "config": {"workload": "qgemm step: " + " + ".join(
             {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
              "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
+             "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
              "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
                    "parallelism": "single GPU", "seeds": "numpy PCG64 1..5",
                    "timing": f"per workload: {args.warmup} warm-up calls, then "

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "qgemm")
 LIB = os.path.join(PKG, "libqgemm.so")
-SOURCES = ["api.cpp", "k_tile_gemm.hip", "k_gemm_dma.hip", "k_skinny_w4a8.hip", "k_conv_halo.hip"]
+SOURCES = ["api.cpp", "k_tile_gemm.hip", "k_gemm_dma.hip", "k_skinny_w4a8.hip", "k_conv_halo.hip", "k_dwconv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

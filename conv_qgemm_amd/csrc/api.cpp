@@ -184,6 +184,43 @@ qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_
     return launched(qg::launch_conv_nhwc(d, (hipStream_t)stream));
 }
 
+qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_t *bias,
+                                    const int32_t *mult, const int32_t *shift, int8_t *Y,
+                                    int32_t batch, int32_t H, int32_t Wd, int32_t C,
+                                    int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
+                                    int32_t pad_h, int32_t pad_w, void *stream)
+{
+    if (!X || !W || !Y || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    if (batch < 1 || H < 1 || Wd < 1 || C < 1 || KH < 1 || KW < 1 || stride_h < 1 ||
+        stride_w < 1 || pad_h < 0 || pad_w < 0)
+        return QG_ERR_INVALID;
+    if (C % 16 != 0)
+        return QG_ERR_INVALID;
+    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
+    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
+    if (span_h < 0 || span_w < 0)
+        return QG_ERR_INVALID;
+    const int64_t Ho = span_h / stride_h + 1, Wo = span_w / stride_w + 1;
+    // kernel indices are int32 where they count pixels, rows or LDS bytes;
+    // element offsets are computed in 64 bits
+    const int64_t pixels = (int64_t)batch * Ho * Wo;
+    if (pixels > kMaxDim || (int64_t)batch * H * Wd > kMaxDim || C > 65536 ||
+        (int64_t)KH * KW * C > kMaxDim || (pixels * (C / 4) + 255) / 256 >= kMaxGrid)
+        return QG_ERR_INVALID;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+        return QG_ERR_INVALID;
+    qg_status st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C, C, KH, KW,
+                   stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo};
+    return launched(qg::launch_dwconv_nhwc(d, (hipStream_t)stream));
+}
+
 const char *qg_status_string(qg_status s)
 {
     switch (s) {

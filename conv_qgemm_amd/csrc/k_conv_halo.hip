@@ -34,6 +34,7 @@
 //     16-byte stores, contiguous when C_out == 64.
 // Two workgroups fit on a CU, so one stages its rows while the other
 // multiplies.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -288,10 +289,11 @@ hipError_t run_halo(const HaloArgs &a, int batch, int lds_bytes, hipStream_t s)
 }
 
 // LDS rows of the input region: the most output rows a tile of kTP
-// consecutive pixels touches, plus the KH-1 halo rows.
+// consecutive pixels touches (never more than the image has), plus the
+// KH-1 halo rows.
 int halo_rows(const ConvDesc &d)
 {
-    return (kTP - 1) / d.Wo + 2 + d.KH - 1;
+    return std::min((kTP - 1) / d.Wo + 2, d.Ho) + d.KH - 1;
 }
 
 // LDS bytes of the input-row region (at least the kTP x 64-byte output

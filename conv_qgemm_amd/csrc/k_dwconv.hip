@@ -1,0 +1,377 @@
+// k_dwconv.hip -- depthwise NHWC int8 conv with the Q31 requantize fused.
+//
+// Method (MCU conv front-end article, news.rkmt.cn/news/16638): in a
+// depthwise conv every channel is convolved on its own, input channel c
+// feeding only output channel c, with weights laid out [kh][kw][c] and the
+// border filled with the zero point (§3.3); the requantize is §2.3's.
+//
+// The 3x3 path (stride 1 or 2, channels a multiple of 16) runs on the int8
+// MFMA even though a depthwise output is only 9 products: the K axis of one
+// v_mfma_i32_16x16x64_i8 is laid out as 4 taps x 16 channels, and the other
+// operand holds the weights on a diagonal (weight w[t][c] at K position
+// (t, c) of column c, zero elsewhere).  Three MFMAs then give 16 pixels x 16
+// channels of a 3x3 conv (taps 9..11 have zero weights).  Per workgroup
+// (4 waves): 256 consecutive output pixels of one image x a 64-channel
+// slice.
+//   * the input rows those pixels touch are staged once in LDS, every pixel
+//     in 80 bytes (the slice's 64 channels + 16 unused) with zero columns and
+//     rows for the padding, so a tap is a fixed LDS offset and 16
+//     consecutive pixels fall in 16 different bank groups;
+//   * the diagonal weight operands live in registers (12 per lane);
+//   * the requantize takes the cheapest exact form all 64 shifts of the
+//     slice allow, and the tile leaves through LDS with 16-byte stores.
+// Other kernel sizes and strides use a direct kernel: one thread per output
+// pixel and 4 channels.
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
+#include "dev_common.hpp"
+#include "launch.hpp"
+
+namespace qg {
+
+namespace {
+
+constexpr int kTP = 256;     // output pixels per workgroup
+constexpr int kCS = 64;      // channels per workgroup slice
+constexpr int kPixL = 80;    // LDS bytes per staged input pixel
+constexpr int kWaves = 4;
+constexpr int kMaxLds = 80 * 1024;
+constexpr int kMaxDevices = 64;
+
+struct DwArgs {
+    const int8_t *X;
+    const int8_t *W;  // [KH][KW][C]
+    const int32_t *bias;
+    const int32_t *mult;
+    const int32_t *shift;
+    int8_t *Y;
+    int H, Wd, C, KH, KW, sh, sw, ph, pw, Ho, Wo;
+    int tiles_per_img;
+    int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+};
+
+__device__ __forceinline__ void drain_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- 3x3 depthwise on the MFMA ----
+template <int S>  // stride (both directions)
+__global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
+{
+    constexpr int KH = 3, KW = 3, KK = 9, kSlices = 3;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t *IN = lds;
+    int *prm = (int *)(lds + p.in_bytes);  // bias, mult, shift [3][64]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;
+    const int g = lane >> 4;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = bid / p.tiles_per_img, tile = bid - b * p.tiles_per_img;
+    const int HW = p.Ho * p.Wo;
+    const int p0 = tile * kTP, npix = min(kTP, HW - p0);
+    const int c0 = blockIdx.y * kCS;
+    const int cs = min(kCS, p.C - c0);  // channels of this slice (a multiple of 16)
+    const int ngrp = cs >> 4;
+    const int oh_first = p0 / p.Wo, oh_last = (p0 + npix - 1) / p.Wo;
+    const int ih0 = oh_first * S - p.ph;  // input row of LDS row 0
+    const int nrow_in = (oh_last - oh_first) * S + KH;
+    const int ih_lo = max(ih0, 0), ih_hi = min(ih0 + nrow_in - 1, p.H - 1);
+    const int colsL = p.Wd + 2 * p.pw;
+    const int rowL = colsL * kPixL;
+
+    // ---- per-channel parameters ----
+    int pb = 0, pm = 0, ps = 31;
+    if (tid < cs) {
+        pb = p.bias ? p.bias[c0 + tid] : 0;
+        pm = p.mult[c0 + tid];
+        ps = p.shift[c0 + tid];
+    }
+
+    // ---- diagonal weight operands: slice s (taps 4s..4s+3), group n; the
+    //      lane (column col = output channel 16n + col, K group g = tap
+    //      4s + g) holds w[4s + g][c0 + 16n + col] at byte col of 16 ----
+    v4i wd[kSlices][4];
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+        const int t = 4 * s + g;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int c = c0 + 16 * n + col;
+            int w = 0;
+            if (t < KK && 16 * n < cs)
+                w = (int)p.W[(int64_t)t * p.C + c] & 0xFF;
+            v4i v = {0, 0, 0, 0};
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                v[d] = (col >> 2) == d ? (w << (8 * (col & 3))) : 0;
+            wd[s][n] = v;
+        }
+    }
+
+    // ---- input rows (the slice's channels) -> LDS, zero outside the image ----
+    const int gpp = cs >> 4;  // 16-byte granules per pixel
+    const int total = ih_lo <= ih_hi ? (ih_hi - ih_lo + 1) * p.Wd * gpp : 0;
+    for (int base = 0; base == 0 || base < total; base += 8 * kWaves * 64) {
+        v4i v[8];
+        if (total > 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = min(base + k * kWaves * 64 + tid, total - 1);
+                const int pix = j / gpp, q = j - pix * gpp;  // pix over rows ih_lo.. x Wd
+                const int64_t src = ((int64_t)b * p.H + ih_lo) * p.Wd + pix;
+                v[k] = *(const v4i *)(p.X + src * p.C + c0 + 16 * q);
+            }
+        }
+        if (base == 0) {
+            for (int e = tid; e < nrow_in * colsL; e += kWaves * 64) {
+                const int r = e / colsL, c = e - r * colsL;
+                const int ih = ih0 + r;
+                if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
+                    v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
+                    z[0] = z[1] = z[2] = z[3] = (v4i){0, 0, 0, 0};
+                } else if (cs < kCS) {
+                    // channels past the slice meet zero weights; keep them finite
+                    for (int q = gpp; q < 4; ++q)
+                        *(v4i *)(IN + r * rowL + c * kPixL + 16 * q) = (v4i){0, 0, 0, 0};
+                }
+            }
+        }
+        if (total > 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = base + k * kWaves * 64 + tid;
+                if (j < total) {
+                    const int pix = j / gpp, q = j - pix * gpp;
+                    const int rr = pix / p.Wd, iw = pix - rr * p.Wd;
+                    const int r = ih_lo - ih0 + rr;
+                    *(v4i *)(IN + r * rowL + (iw + p.pw) * kPixL + 16 * q) = v[k];
+                }
+            }
+        }
+    }
+    drain_and_barrier();
+    if (tid < kCS) {
+        prm[tid] = pb;
+        prm[kCS + tid] = pm;
+        prm[2 * kCS + tid] = ps;
+    }
+    __syncthreads();
+
+    // ---- this lane's pixel in each of the wave's 4 M tiles (LDS offset of
+    //      its (0, 0) tap) and its tap in each slice ----
+    int abase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = min(64 * wave + 16 * i + col, npix - 1);
+        const int pp = p0 + q;
+        const int oh = pp / p.Wo;
+        const int ow = pp - oh * p.Wo;
+        abase[i] = (oh - oh_first) * S * rowL + ow * S * kPixL;
+    }
+    int toff[kSlices];
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+        const int t = 4 * s + g < KK ? 4 * s + g : 0;  // taps past the last have zero weights
+        toff[s] = (t / KW) * rowL + (t % KW) * kPixL;
+    }
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            acc[i][n] = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+        v4i a[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                a[i][n] = *(const v4i *)(IN + abase[i] + toff[s] + 16 * n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[i][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wd[s][n], a[i][n], acc[i][n],
+                                                                 0, 0, 0);
+    }
+
+    // ---- requantize into LDS; lane holds pixel 64*wave + 16*i + col and
+    //      channels 16*n + 4*g + e of the slice ----
+    __syncthreads();
+    const int sh_l = prm[2 * kCS + lane];
+    auto requant_tile = [&](auto tier_tag) {
+        constexpr int TIER = decltype(tier_tag)::value;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int cc = 16 * n + 4 * g;
+            const v4i b4 = *(const v4i *)&prm[cc];
+            const v4i m4 = *(const v4i *)&prm[kCS + cc];
+            const v4i s4 = *(const v4i *)&prm[2 * kCS + cc];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int x = acc[i][n][e];
+                    if constexpr (TIER == 2)
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e]);
+                    else if constexpr (TIER == 1)
+                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                    else
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                }
+                const int q = 64 * wave + 16 * i + col;
+                *(unsigned *)(IN + q * 64 + cc) = pack4_i8(y[0], y[1], y[2], y[3]);
+            }
+        }
+    };
+    // parameters of channels past the slice read as shift 31 (a valid value)
+    if (__builtin_amdgcn_ballot_w64(sh_l < 33) == 0)
+        requant_tile(std::integral_constant<int, 2>{});
+    else if (__builtin_amdgcn_ballot_w64(sh_l < 31) == 0)
+        requant_tile(std::integral_constant<int, 1>{});
+    else
+        requant_tile(std::integral_constant<int, 0>{});
+    __syncthreads();
+
+    // ---- 16-byte stores of the tile's npix x cs output bytes ----
+    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C + c0;
+    for (int idx = tid; idx < npix * ngrp; idx += kWaves * 64) {
+        const int pix = idx / ngrp, qq = idx - pix * ngrp;
+        *(v4i *)(ybase + (int64_t)pix * p.C + 16 * qq) = *(const v4i *)(IN + pix * 64 + 16 * qq);
+    }
+}
+
+// ---- any kernel size and stride: one thread per output pixel x 4 channels ----
+__global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
+{
+    const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (item >= nitems)
+        return;
+    const int cq = p.C >> 2;
+    const int64_t pix = item / cq;
+    const int c = (int)(item - pix * cq) * 4;
+    const int HW = p.Ho * p.Wo;
+    const int b = (int)(pix / HW);
+    const int rem = (int)(pix - (int64_t)b * HW);
+    const int oh = rem / p.Wo, ow = rem - (rem / p.Wo) * p.Wo;
+    int acc[4] = {0, 0, 0, 0};
+    for (int kh = 0; kh < p.KH; ++kh) {
+        const int ih = oh * p.sh - p.ph + kh;
+        if (ih < 0 || ih >= p.H)
+            continue;
+        for (int kw = 0; kw < p.KW; ++kw) {
+            const int iw = ow * p.sw - p.pw + kw;
+            if (iw < 0 || iw >= p.Wd)
+                continue;
+            const unsigned xv = *(const unsigned *)(p.X + (((int64_t)b * p.H + ih) * p.Wd + iw) * p.C + c);
+            const unsigned wv = *(const unsigned *)(p.W + (int64_t)(kh * p.KW + kw) * p.C + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[e] += (int)(int8_t)(xv >> (8 * e)) * (int)(int8_t)(wv >> (8 * e));
+        }
+    }
+    int y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int s = p.shift[c + e];
+        y[e] = requant_one(acc[e], p.bias ? p.bias[c + e] : 0, p.mult[c + e], s,
+                           1ll << ((s - 1) & 63));
+    }
+    *(unsigned *)(p.Y + pix * p.C + c) = pack4_i8(y[0], y[1], y[2], y[3]);
+}
+
+// LDS bytes of the staged input rows for a 3x3 conv with stride S: the
+// output rows a tile of kTP consecutive pixels touches (never more than the
+// image has), times S, plus the halo; at least the kTP x 64-byte output
+// staging; rounded to 1 KB.
+int64_t dw_in_bytes(const ConvDesc &d)
+{
+    const int64_t span = std::min<int64_t>((kTP - 1) / d.Wo + 1, d.Ho - 1);
+    const int64_t rows = span * d.sh + d.KH;
+    int64_t in = rows * (d.Wd + 2 * d.pw) * kPixL;
+    if (in < (int64_t)kTP * 64)
+        in = (int64_t)kTP * 64;
+    return (in + 1023) & ~(int64_t)1023;
+}
+
+int64_t dw_lds_bytes(const ConvDesc &d)
+{
+    return dw_in_bytes(d) + 3 * kCS * 4;
+}
+
+bool dw_mfma_fits(const ConvDesc &d)
+{
+    if (d.KH != 3 || d.KW != 3 || d.sh != d.sw || (d.sh != 1 && d.sh != 2))
+        return false;
+    return d.C_in % 16 == 0 && dw_lds_bytes(d) <= kMaxLds;
+}
+
+template <int S>
+hipError_t run_dw3x3(const DwArgs &a, int batch, int lds_bytes, hipStream_t s)
+{
+    static std::atomic<bool> attr_set[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    if (!attr_set[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute((const void *)k_dwconv3x3<S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+        if (e != hipSuccess)
+            return e;
+        attr_set[dev].store(true, std::memory_order_release);
+    }
+    const dim3 grid(batch * a.tiles_per_img, (a.C + kCS - 1) / kCS), block(kWaves * 64);
+    hipLaunchKernelGGL((k_dwconv3x3<S>), grid, block, lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s)
+{
+    DwArgs a{};
+    a.X = d.X;
+    a.W = d.W;
+    a.bias = d.bias;
+    a.mult = d.mult;
+    a.shift = d.shift;
+    a.Y = d.Y;
+    a.H = d.H;
+    a.Wd = d.Wd;
+    a.C = d.C_in;
+    a.KH = d.KH;
+    a.KW = d.KW;
+    a.sh = d.sh;
+    a.sw = d.sw;
+    a.ph = d.ph;
+    a.pw = d.pw;
+    a.Ho = d.Ho;
+    a.Wo = d.Wo;
+    if (dw_mfma_fits(d)) {
+        a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
+        a.in_bytes = (int)dw_in_bytes(d);
+        const int lds = (int)dw_lds_bytes(d);
+        if (d.sh == 1)
+            return run_dw3x3<1>(a, d.batch, lds, s);
+        return run_dw3x3<2>(a, d.batch, lds, s);
+    }
+    const int64_t nitems = (int64_t)d.batch * d.Ho * d.Wo * (d.C_in / 4);
+    const int64_t blocks = (nitems + 255) / 256;
+    hipLaunchKernelGGL(k_dwconv_direct, dim3((unsigned)blocks), dim3(256), 0, s, a, nitems);
+    return hipGetLastError();
+}
+
+}  // namespace qg

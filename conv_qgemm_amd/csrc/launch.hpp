@@ -51,6 +51,9 @@ hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
 bool conv_halo_fits(const ConvDesc &d);
 hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s);
 
+// depthwise NHWC conv (k_dwconv.hip); C_in == C_out == the channel count
+hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s);
+
 // Largest M the weight-streaming W4A8 kernel takes; larger M is tiled.
 constexpr int64_t kSkinnyMaxM = 64;
 

@@ -19,6 +19,8 @@ bias in [-2^15, 2^15], Q31 multiplier in [2^30, 2^31), shift in 31..40):
   conv3x3     NHWC 3x3 s1 p1, batch 32, 56x56, 64 -> 64 channels
   w4a8        skinny M=16, K=8192, N=28672, packed int4 weights
   s8s8        M=N=K=8192 int8, shift 35..44
+  dw3x3       depthwise NHWC 3x3 s1 p1, batch 32, 56x56, 64 channels,
+              weights [3][3][64] (the MCU front-end page's depthwise layout)
 """
 from __future__ import annotations
 
@@ -39,12 +41,14 @@ WORKLOADS = {
                     stride=(1, 1), pad=(1, 1), shift=(31, 40), seed=3),
     "w4a8": dict(kind="w4a8", M=16, N=28672, K=8192, shift=(31, 40), seed=4),
     "s8s8": dict(kind="s8s8", M=8192, N=8192, K=8192, shift=(35, 44), seed=5),
+    "dw3x3": dict(kind="dwconv", batch=32, H=56, W=56, C=64, KH=3, KW=3,
+                  stride=(1, 1), pad=(1, 1), shift=(31, 40), seed=6),
 }
 
 # Variants whose shift windows keep most outputs inside [-128, 127], so that
 # parity is also exercised away from saturation.
 UNSATURATED_SHIFT = {"pointwise": (38, 44), "conv3x3": (39, 45), "w4a8": (37, 43),
-                     "s8s8": (41, 47)}
+                     "s8s8": (41, 47), "dw3x3": (39, 45)}
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -100,6 +104,15 @@ def conv_nhwc(batch, H, W, C_in, C_out, KH, KW, seed, shift=SHIFT_DEFAULT):
     return dict(X=X, W=Wt, bias=bias, mult=mult, shift=sh)
 
 
+def dwconv_nhwc(batch, H, W, C, KH, KW, seed, shift=SHIFT_DEFAULT):
+    """Depthwise conv operands: X [batch][H][W][C], weights [KH][KW][C]."""
+    g = rng(seed)
+    X = int8_uniform(g, (batch, H, W, C))
+    Wt = int8_uniform(g, (KH, KW, C))
+    bias, mult, sh = channel_params(g, C, shift)
+    return dict(X=X, W=Wt, bias=bias, mult=mult, shift=sh)
+
+
 def workload(name: str, unsaturated: bool = False, seed: int | None = None):
     """Arrays of a named workload (seeded); ``unsaturated`` picks the
     parity variant's shift window and seeds 101..105."""
@@ -116,6 +129,8 @@ def workload(name: str, unsaturated: bool = False, seed: int | None = None):
     if k == "conv":
         return conv_nhwc(w["batch"], w["H"], w["W"], w["C_in"], w["C_out"], w["KH"], w["KW"],
                          s, shift)
+    if k == "dwconv":
+        return dwconv_nhwc(w["batch"], w["H"], w["W"], w["C"], w["KH"], w["KW"], s, shift)
     raise KeyError(name)
 
 

@@ -49,6 +49,8 @@ def _load():
     lib.qgemm_w4a8_requant.restype = S
     lib.qconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 11 + [P]
     lib.qconv2d_nhwc_s8_requant.restype = S
+    lib.qdwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 10 + [P]
+    lib.qdwconv2d_nhwc_s8_requant.restype = S
     lib.qg_status_string.argtypes = [S]
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
@@ -58,7 +60,8 @@ def _load():
 
 lib = _load()
 EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
-           "qconv2d_nhwc_s8_requant", "qg_status_string", "qg_version")
+           "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qg_status_string",
+           "qg_version")
 
 
 def status_string(status: int) -> str:
@@ -209,4 +212,36 @@ def qconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1), 
                                      batch, H, Wd, C_in, C_out, KH, KW, stride[0], stride[1],
                                      pad[0], pad[1], _stream(stream))
     _check(st, "qconv2d_nhwc_s8_requant")
+    return Y
+
+
+def qdwconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1), Y=None,
+                              stream=None):
+    """Depthwise NHWC int8 conv (output channel c sees only input channel c)
+    with zero-point-0 padding and the fused requantize.
+
+    X int8 [batch, H, W, C] and W int8 [KH, KW, C], both contiguous; returns
+    Y int8 [batch, H_out, W_out, C].
+    """
+    if X.dtype != torch.int8 or W.dtype != torch.int8:
+        raise TypeError("X and W must be int8")
+    if X.dim() != 4 or W.dim() != 3 or not X.is_contiguous() or not W.is_contiguous():
+        raise ValueError("X [B,H,W,C] and W [KH,KW,C] must be contiguous")
+    _on_device(X, "X")
+    _on_device(W, "W")
+    batch, H, Wd, C = X.shape
+    KH, KW, C2 = W.shape
+    if C2 != C:
+        raise ValueError("X and W disagree on C")
+    Ho, Wo = conv_out_hw(H, Wd, KH, KW, stride, pad)
+    if Y is None:
+        Y = torch.empty((batch, max(Ho, 0), max(Wo, 0), C), dtype=torch.int8, device=X.device)
+    if not Y.is_contiguous() or Y.dtype != torch.int8 or tuple(Y.shape) != (batch, Ho, Wo, C):
+        raise ValueError("Y must be a contiguous int8 [batch, H_out, W_out, C] tensor")
+    _on_device(Y, "Y")
+    st = lib.qdwconv2d_nhwc_s8_requant(_ptr(X), _ptr(W), _ptr(_vec(bias, C, "bias")),
+                                       _ptr(_vec(mult, C, "mult")), _ptr(_vec(shift, C, "shift")),
+                                       _ptr(Y), batch, H, Wd, C, KH, KW, stride[0], stride[1],
+                                       pad[0], pad[1], _stream(stream))
+    _check(st, "qdwconv2d_nhwc_s8_requant")
     return Y

@@ -140,6 +140,27 @@ qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W,
                                   int32_t stride_h, int32_t stride_w,
                                   int32_t pad_h, int32_t pad_w, void *stream);
 
+/*
+ * qdwconv2d_nhwc_s8_requant -- depthwise int8 NHWC conv, zero-point-0
+ * padding, requant: output channel c is the conv of input channel c alone.
+ *   X     int8 [batch][H][Wd][C]  (NHWC, dense)
+ *   W     int8 [KH][KW][C]        (tap-major, channels innermost, dense)
+ *   bias/mult/shift int32 [C] (bias may be NULL)
+ *   Y     int8 [batch][H_out][W_out][C] (NHWC, dense)
+ *   H_out, W_out as for qconv2d_nhwc_s8_requant; both >= 1.
+ *   batch, H, Wd, C, KH, KW, stride >= 1; pad >= 0; C % 16 == 0.
+ * MCU conv front-end article §3.3 (one input channel per output channel,
+ * weights indexed [kh][kw][c], border filled with the zero point), §2.3
+ * (requantize).  3x3 with equal strides 1 or 2 runs on the int8 matrix
+ * cores; other shapes run a direct kernel.
+ */
+qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W,
+                                    const int32_t *bias, const int32_t *mult,
+                                    const int32_t *shift, int8_t *Y,
+                                    int32_t batch, int32_t H, int32_t Wd, int32_t C,
+                                    int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
+                                    int32_t pad_h, int32_t pad_w, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *qg_status_string(qg_status s);
 

@@ -75,6 +75,12 @@ def cv(qg, X=P, W=P, bias=P, mult=P, shift=P, Y=P, batch=1, H=8, Wd=8, C_in=16, 
                                           KH, KW, sh, sw, ph, pw, None)
 
 
+def dw(qg, X=P, W=P, bias=P, mult=P, shift=P, Y=P, batch=1, H=8, Wd=8, C=16, KH=3, KW=3,
+       sh=1, sw=1, ph=1, pw=1):
+    return qg.lib.qdwconv2d_nhwc_s8_requant(X, W, bias, mult, shift, Y, batch, H, Wd, C, KH, KW,
+                                            sh, sw, ph, pw, None)
+
+
 def test_nullptr(qg):
     E = qg.QG_ERR_NULLPTR
     for kw in ("A", "B", "C", "mult", "shift"):
@@ -84,6 +90,7 @@ def test_nullptr(qg):
         assert s4(qg, **{kw: NULL}) == E, kw
     for kw in ("X", "W", "Y", "mult", "shift"):
         assert cv(qg, **{kw: NULL}) == E, kw
+        assert dw(qg, **{kw: NULL}) == E, kw
 
 
 def test_invalid_gemm_sizes(qg):
@@ -122,6 +129,7 @@ def test_invalid_alignment(qg):
         assert w4(qg, **{kw: P + 4}) == E, kw
     for kw in ("X", "W", "Y", "mult"):
         assert cv(qg, **{kw: P + 4}) == E, kw
+        assert dw(qg, **{kw: P + 4}) == E, kw
 
 
 def test_invalid_conv(qg):
@@ -137,6 +145,18 @@ def test_invalid_conv(qg):
     assert cv(qg, batch=2 ** 20, H=2 ** 10, Wd=2 ** 10) == E  # too many pixels
 
 
+def test_invalid_dwconv(qg):
+    E = qg.QG_ERR_INVALID
+    for kw in ("batch", "H", "Wd", "C", "KH", "KW", "sh", "sw"):
+        assert dw(qg, **{kw: 0}) == E, kw
+    assert dw(qg, ph=-1) == E
+    assert dw(qg, pw=-1) == E
+    assert dw(qg, C=24) == E                # C % 16
+    assert dw(qg, H=2, KH=5, ph=1) == E     # H_out < 1
+    assert dw(qg, Wd=1, KW=4, pw=1) == E    # W_out < 1
+    assert dw(qg, batch=2 ** 20, H=2 ** 10, Wd=2 ** 10) == E  # too many pixels
+
+
 def test_valid_call_without_gpu_reports_no_device(qg):
     import torch
     if torch.cuda.is_available():
@@ -145,6 +165,7 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert s4(qg) == qg.QG_ERR_NO_DEVICE
     assert w4(qg) == qg.QG_ERR_NO_DEVICE
     assert cv(qg) == qg.QG_ERR_NO_DEVICE
+    assert dw(qg) == qg.QG_ERR_NO_DEVICE
 
 
 def test_binding_rejects_bad_tensors(qg):

@@ -122,6 +122,22 @@ def test_graph_conv(qg, C_in):
         Y=d["out"]))
 
 
+@pytest.mark.parametrize("KH", [3, 5])
+def test_graph_dwconv(qg, KH):
+    """3x3 takes the matrix-core kernel, 5x5 the direct one."""
+    import torch
+
+    def make(seed):
+        h = datagen.dwconv_nhwc(2, 9, 11, 64, KH, KH, seed, shift=(36, 42))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((2, 9, 11, 64), dtype=torch.int8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qdwconv2d_nhwc_s8_requant(
+        d["X"], d["W"], d["bias"], d["mult"], d["shift"], stride=(1, 1),
+        pad=(KH // 2, KH // 2), Y=d["out"]))
+
+
 def test_graph_matches_oracle(qg, orc):
     """One replayed result also checked against the oracle directly."""
     import torch

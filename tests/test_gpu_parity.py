@@ -275,6 +275,49 @@ def test_conv_pointwise_equals_gemm(qg):
     assert np.array_equal(host(Y).reshape(320, 64), host(C))
 
 
+# ---------------------------------------------------------------- depthwise conv
+
+DW_GEOMS = [
+    # batch, H, W, C, KH, KW, stride, pad
+    (1, 7, 6, 16, 3, 3, (1, 1), (1, 1)),
+    (2, 9, 8, 32, 3, 3, (2, 2), (1, 1)),
+    (1, 10, 7, 96, 3, 3, (1, 1), (0, 0)),     # a full and a 32-channel slice
+    (1, 20, 16, 16, 3, 3, (1, 1), (1, 1)),    # the MCU front-end's 20x16x16 map
+    (2, 40, 3, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: a tile spans 86 rows
+    (1, 13, 30, 128, 3, 3, (2, 2), (1, 1)),   # stride 2, two slices
+    (3, 17, 19, 64, 3, 3, (1, 1), (2, 0)),    # unequal padding, several images
+    (1, 8, 8, 16, 5, 5, (1, 1), (2, 2)),      # direct kernel: 5x5
+    (2, 6, 11, 32, 1, 3, (1, 2), (0, 1)),     # direct kernel: 1x3, unequal strides
+    (1, 9, 9, 48, 3, 3, (2, 1), (1, 1)),      # direct kernel: unequal strides
+    (1, 3, 200, 16, 3, 3, (2, 2), (1, 1)),    # wide rows at stride 2
+]
+
+
+@pytest.mark.parametrize("geom", DW_GEOMS)
+def test_dwconv_small(qg, geom):
+    b, H, Wd, C, KH, KW, stride, pad = geom
+    _say("dwconv", geom)
+    d = datagen.dwconv_nhwc(b, H, Wd, C, KH, KW, seed=H * Wd + C, shift=(36, 42))
+    Y = qg.qdwconv2d_nhwc_s8_requant(dev(d["X"]), dev(d["W"]), dev(d["bias"]), dev(d["mult"]),
+                                     dev(d["shift"]), stride=stride, pad=pad)
+    want = oracle.dwconv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                           stride=stride, pad=pad)
+    assert np.array_equal(host(Y), want)
+
+
+def test_dwconv_extremes(qg):
+    """-128 inputs against -128 / 127 weights, shifts at both ends."""
+    b, H, Wd, C = 1, 9, 10, 32
+    X = np.full((b, H, Wd, C), -128, np.int8)
+    Wt = np.full((3, 3, C), -128, np.int8)
+    Wt[..., 1::2] = 127
+    bias = np.zeros(C, np.int32)
+    mult = np.full(C, 2 ** 31 - 1, np.int32)
+    shift = np.array([1, 63, 31, 44] * (C // 4), np.int32)
+    Y = qg.qdwconv2d_nhwc_s8_requant(dev(X), dev(Wt), dev(bias), dev(mult), dev(shift))
+    assert np.array_equal(host(Y), oracle.dwconv2d_nhwc_s8_requant(X, Wt, bias, mult, shift))
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("unsat", [False, True])
@@ -303,6 +346,18 @@ def test_workload_conv3x3_full(qg, unsat):
                                         pad=(1, 1)))
     want = oracle.conv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
                                          stride=(1, 1), pad=(1, 1))
+    assert np.array_equal(Y, want)
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_dw3x3_full(qg, unsat):
+    _say("workload dw3x3 full", unsat)
+    d = datagen.workload("dw3x3", unsaturated=unsat)
+    Y = host(qg.qdwconv2d_nhwc_s8_requant(dev(d["X"]), dev(d["W"]), dev(d["bias"]),
+                                          dev(d["mult"]), dev(d["shift"]), stride=(1, 1),
+                                          pad=(1, 1)))
+    want = oracle.dwconv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                           stride=(1, 1), pad=(1, 1))
     assert np.array_equal(Y, want)
 
 
