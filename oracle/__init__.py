@@ -83,6 +83,13 @@ def _load():
     lib.orc_dwconv2d_acc.restype = ctypes.c_int
     lib.orc_dwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I64] * 10 + [P, I64]
     lib.orc_dwconv2d_nhwc_s8_requant.restype = ctypes.c_int
+    lib.orc_quant_per_token.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_float,
+                                         ctypes.c_int, P, I64, P]
+    lib.orc_quant_per_token.restype = ctypes.c_int
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = ctypes.c_float
+    lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_to_f32.restype = ctypes.c_float
     lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_set_threads.restype = None
     lib.orc_max_threads.argtypes = []
@@ -329,3 +336,43 @@ def dwconv2d_nhwc_s8_requant(X, Wt, bias, mult, shift, stride=(1, 1), pad=(1, 1)
     if pix is None:
         return Y.reshape(batch, Ho, Wo, C)
     return Y
+
+
+# ---- per-token activation quantizer ----
+
+_DTYPES = {"float32": 0, "float16": 1, "bfloat16": 2}
+
+
+def quant_per_token(X, bits=8, clip_ratio=1.0, dtype=None):
+    """Per-token symmetric quantization of X [M][K] to int8 (bits 8) or packed
+    int4 (bits 4, uint8 [M][K/2]); returns (Q, scale float32 [M]).
+
+    X is a float32 or float16 array, or a uint16 array of bfloat16 bit
+    patterns with dtype="bfloat16".  Codes are decided in binary32."""
+    X = np.ascontiguousarray(X)
+    if dtype is None:
+        dtype = {np.dtype(np.float32): "float32", np.dtype(np.float16): "float16"}[X.dtype]
+    code = _DTYPES[dtype]
+    if code == 2 and X.dtype != np.uint16:
+        raise TypeError("bfloat16 input is passed as uint16 bit patterns")
+    M, K = X.shape
+    if bits == 4:
+        assert K % 2 == 0
+        Q = np.zeros((M, K // 2), dtype=np.uint8)
+        ldq = K
+    else:
+        Q = np.zeros((M, K), dtype=np.int8)
+        ldq = K
+    scale = np.zeros(M, dtype=np.float32)
+    st = _load().orc_quant_per_token(X.ctypes.data, code, K, M, K, float(clip_ratio), bits,
+                                     Q.ctypes.data, ldq, scale.ctypes.data)
+    _check(st, "quant_per_token")
+    return Q, scale
+
+
+def f16_to_f32(h):
+    return float(_load().orc_f16_to_f32(int(h)))
+
+
+def bf16_to_f32(b):
+    return float(_load().orc_bf16_to_f32(int(b)))

@@ -22,6 +22,11 @@
  *                  the depthwise conv: one input channel per output
  *                  channel, weights [kh][kw][c]).
  *
+ *   [FLATQUANT]  Ascend FlatQuant operator article, www.zwxr.cn/news/277566
+ *                  «per-token 模式» (per-token INT4 scale from max|x|).
+ *   [VOYAGER]    Voyager quantization article, www.dpshk.com/news/2695434
+ *                  §1.1 (Q = round(x / scale) + zero_point).
+ *
  * Readings where the pages are silent or contradict themselves:
  *   - packed INT4: element 2i is the LOW nibble of byte i, element 2i+1 the
  *     high nibble; codes are 4-bit two's complement (0x8 = -8).
@@ -375,6 +380,99 @@ int orc_dwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
         }
     }
     return status;
+}
+
+/* ---- per-token activation quantizer ([FLATQUANT] «per-token 模式»:
+ * per token, scale = max|x| / (qmax / clip_ratio), codes = x / scale;
+ * [VOYAGER] §1.1: Q = round(x / scale) + zero_point with round-half-away
+ * rounding, zero point 0 here).  qmax is 7 for int4 (as the page states)
+ * and 127 for int8.  The codes are decided in IEEE binary32, the precision
+ * the GPU kernel computes in: the divisions are correctly rounded float
+ * divisions, then the quotient is rounded half away from zero and clamped
+ * to [-qmax, qmax].  A token whose values are all zero gets scale 0 and
+ * codes 0.  Inputs must be finite. ---- */
+
+/* binary16 / bfloat16 bit patterns to float (both convert exactly). */
+float orc_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    int32_t e = (h >> 10) & 0x1F;
+    uint32_t m = h & 0x3FF;
+    float v;
+    if (e == 0) {
+        v = (float)m * (1.0f / 16777216.0f); /* m * 2^-24, exact */
+    } else if (e == 31) {
+        union { uint32_t u; float f; } inf = {0x7F800000u | (m << 13)};
+        v = inf.f;
+    } else {
+        union { uint32_t u; float f; } x = {((uint32_t)(e - 15 + 127) << 23) | (m << 13)};
+        v = x.f;
+    }
+    return sign ? -v : v;
+}
+
+float orc_bf16_to_f32(uint16_t b)
+{
+    union { uint32_t u; float f; } x = {(uint32_t)b << 16};
+    return x.f;
+}
+
+/* round half away from zero of a binary32 value, as an integer */
+static int64_t round_half_away(float q)
+{
+    float a = q < 0 ? -q : q;
+    float f = (float)(int64_t)a;          /* floor of a (a < 2^62 here) */
+    int64_t r = (int64_t)f + ((a - f) >= 0.5f ? 1 : 0);
+    return q < 0 ? -r : r;
+}
+
+/* dtype: 0 = binary32, 1 = binary16, 2 = bfloat16; X is [M][ldx] elements.
+ * bits 8: Q is int8 [M][ldq]; bits 4: Q is packed int4 [M][ldq/2 bytes]
+ * (element 2i in the low nibble of byte i).  scale is [M]. */
+int orc_quant_per_token(const void *X, int dtype, int64_t ldx, int64_t M, int64_t K,
+                        float clip_ratio, int bits, void *Q, int64_t ldq, float *scale)
+{
+    const float qmax = bits == 4 ? 7.0f : 127.0f;
+    if ((bits != 4 && bits != 8) || !(clip_ratio > 0.0f))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float v = dtype == 0 ? ((const float *)X)[m * ldx + k]
+                    : dtype == 1 ? orc_f16_to_f32(((const uint16_t *)X)[m * ldx + k])
+                                 : orc_bf16_to_f32(((const uint16_t *)X)[m * ldx + k]);
+            float a = v < 0 ? -v : v;
+            if (a > amax)
+                amax = a;
+        }
+        const float sc = amax / (qmax / clip_ratio);
+        scale[m] = sc;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t q = 0;
+            if (sc > 0.0f) {
+                float v = dtype == 0 ? ((const float *)X)[m * ldx + k]
+                        : dtype == 1 ? orc_f16_to_f32(((const uint16_t *)X)[m * ldx + k])
+                                     : orc_bf16_to_f32(((const uint16_t *)X)[m * ldx + k]);
+                q = round_half_away(v / sc);
+                if (q > (int64_t)qmax)
+                    q = (int64_t)qmax;
+                if (q < -(int64_t)qmax)
+                    q = -(int64_t)qmax;
+            }
+            if (bits == 8) {
+                ((int8_t *)Q)[m * ldq + k] = (int8_t)q;
+            } else {
+                uint8_t *byte = (uint8_t *)Q + m * (ldq / 2) + k / 2;
+                uint8_t nib = (uint8_t)(q & 0xF);
+                if (k % 2 == 0)
+                    *byte = (uint8_t)((*byte & 0xF0) | nib);
+                else
+                    *byte = (uint8_t)((*byte & 0x0F) | (nib << 4));
+            }
+        }
+    }
+    return ORC_OK;
 }
 
 /* ---- threading controls, so a caller can state the cores it used ---- */

@@ -13,7 +13,7 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_int4.py", "tests/test_oracle_requant.py",
              "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py",
-             "tests/test_oracle_dwconv.py"]
+             "tests/test_oracle_dwconv.py", "tests/test_oracle_quant.py"]
 
 MUTANTS = {
     "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
@@ -37,6 +37,16 @@ MUTANTS = {
     "dw_weight_layout": ("Wt[(kh * KW + kw) * C + c]", "Wt[c * KH * KW + kh * KW + kw]"),
     "dw_channel_mix": ("X[((b * H + ih) * W + iw) * C + c]",
                        "X[((b * H + ih) * W + iw) * C + (c + 1) % C]"),
+    "quant_half_even": ("int64_t r = (int64_t)f + ((a - f) >= 0.5f ? 1 : 0);",
+                        "int64_t r = (int64_t)f + ((a - f) > 0.5f ? 1 : 0);"),
+    "quant_qmax_int4": ("const float qmax = bits == 4 ? 7.0f : 127.0f;",
+                        "const float qmax = bits == 4 ? 8.0f : 127.0f;"),
+    "quant_clip_inverted": ("const float sc = amax / (qmax / clip_ratio);",
+                            "const float sc = amax / (qmax * clip_ratio);"),
+    "quant_signed_max": ("float a = v < 0 ? -v : v;\n            if (a > amax)",
+                         "float a = v;\n            if (a > amax)"),
+    "quant_nibble_swap": ("if (k % 2 == 0)\n                    *byte",
+                          "if (k % 2 == 1)\n                    *byte"),
     "dw_tap_dropped": ("for (int64_t kw = 0; kw < KW; ++kw) {\n            const int64_t iw",
                        "for (int64_t kw = 0; kw + 1 < KW; ++kw) {\n            const int64_t iw"),
 }
