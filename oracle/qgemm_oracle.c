@@ -421,7 +421,9 @@ float orc_bf16_to_f32(uint16_t b)
 static int64_t round_half_away(float q)
 {
     float a = q < 0 ? -q : q;
-    float f = (float)(int64_t)a;          /* floor of a (a < 2^62 here) */
+    if (a >= 2147483648.0f)               /* clamps to +-qmax anyway; keeps the cast defined */
+        a = 2147483648.0f;
+    float f = (float)(int64_t)a;          /* floor of a */
     int64_t r = (int64_t)f + ((a - f) >= 0.5f ? 1 : 0);
     return q < 0 ? -r : r;
 }

@@ -58,6 +58,10 @@ def test_clip_ratio_clamps(orc):
     Q4, _ = orc.quant_per_token(X, bits=4, clip_ratio=0.5)
     codes = [orc.int4_at(Q4[0], i) for i in range(4)]
     assert codes == [-7, 1, 7, 7]
+    # a tiny clip ratio puts x / scale far past 2^31: every nonzero code clamps
+    Xt = np.array([[1e-3, -1.0, 0.0, 1.0]], np.float32)
+    Qt, _ = orc.quant_per_token(Xt, bits=8, clip_ratio=1e-20)
+    assert Qt[0].tolist() == [127, -127, 0, 127]
 
 
 def _random_tokens(g, M, K):
