@@ -7,6 +7,8 @@ One step is one call of every entry point on its workload:
   conv3x3    qconv2d_nhwc_s8_requant  batch 32, 56x56, 64->64, 3x3 s1 p1
   w4a8       qgemm_w4a8_requant  M=16 tokens, K=8192, N=28672 (skinny)
   dw3x3      qdwconv2d_nhwc_s8_requant  batch 32, 56x56, 64 channels, 3x3 s1 p1
+  quant_a8   qquant_per_token    8192 tokens x 8192 channels, bfloat16 -> int8
+             codes + float32 scales (the s8s8 A operand; no integer ops)
   s8s8       qgemm_s8s8_requant  M=N=K=8192
 Inputs are seeded synthetic arrays resident in HBM before timing starts.
 Each workload rotates through enough copies of its buffers that every call
@@ -34,9 +36,10 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
-ORDER = ["pointwise", "dw3x3", "w4a8", "conv3x3", "s4s4", "s8s8"]
+ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "s4s4", "s8s8"]
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
-ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "dw3x3": 40, "w4a8": 5, "s8s8": 3}
+ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "dw3x3": 40, "quant_a8": 3, "w4a8": 5,
+          "s8s8": 3}
 KERNEL_SOURCES = {
     "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
@@ -44,6 +47,7 @@ KERNEL_SOURCES = {
     "conv3x3": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
     "dw3x3": "conv_qgemm_amd/csrc/k_dwconv.hip",
+    "quant_a8": "conv_qgemm_amd/csrc/k_quant.hip",
 }
 
 
@@ -56,6 +60,9 @@ def ops_and_bytes(name):
     """(int ops = 2 * MACs, algorithmic bytes: inputs once, outputs once,
     plus 12 bytes per output channel of bias / multiplier / shift)."""
     w = shape_of(name)
+    if w["kind"] == "quant":
+        eb = {"float32": 4, "float16": 2, "bfloat16": 2}[w["dtype"]]
+        return 0, w["M"] * w["K"] * eb + w["M"] * w["K"] * w["bits"] // 8 + 4 * w["M"]
     if w["kind"] == "dwconv":
         Ho, Wo = w["H"], w["W"]  # 3x3 s1 p1 keeps the size
         pix = w["batch"] * Ho * Wo
@@ -118,12 +125,20 @@ class Case:
         self.host = d
         nrot = ROTATE[name]
         dev = lambda a: torch.from_numpy(a).cuda()
-        base = {k: dev(v) for k, v in d.items()}
+        w = shape_of(name)
+        if w["kind"] == "quant":
+            base = {"X": torch.from_numpy(d["X"]).to(getattr(torch, w["dtype"])).cuda()}
+        else:
+            base = {k: dev(v) for k, v in d.items()}
         self.sets = []
         for r in range(nrot):
             s = {k: (v if r == 0 else v.clone()) for k, v in base.items()}
-            w = shape_of(name)
-            if w["kind"] == "conv":
+            if w["kind"] == "quant":
+                s["Q"] = torch.empty((w["M"], w["K"] * w["bits"] // 8),
+                                     dtype=torch.int8 if w["bits"] == 8 else torch.uint8,
+                                     device="cuda")
+                s["scale"] = torch.empty(w["M"], dtype=torch.float32, device="cuda")
+            elif w["kind"] == "conv":
                 s["Y"] = torch.empty((w["batch"], w["H"], w["W"], w["C_out"]), dtype=torch.int8,
                                      device="cuda")
             elif w["kind"] == "dwconv":
@@ -143,6 +158,9 @@ class Case:
             return q.qgemm_s4s4_i32(s["A"], s["B"], C=s["C"])
         if self.name == "w4a8":
             return q.qgemm_w4a8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
+        if self.name == "quant_a8":
+            return q.qquant_per_token(s["X"], bits=shape_of("quant_a8")["bits"], Q=s["Q"],
+                                      scale=s["scale"])
         if self.name == "dw3x3":
             return q.qdwconv2d_nhwc_s8_requant(s["X"], s["W"], s["bias"], s["mult"], s["shift"],
                                                stride=(1, 1), pad=(1, 1), Y=s["Y"])
@@ -181,6 +199,17 @@ def cpu_baseline(names, frac=16):
             oracle.gemm_w4a8_requant(d["A"], d["B"][cols], d["bias"][cols], d["mult"][cols],
                                      d["shift"][cols])
             part = len(cols) / w["N"]
+        elif w["kind"] == "quant":
+            import torch
+            rows = np.arange(0, w["M"], frac)
+            Xs = torch.from_numpy(d["X"][rows]).to(getattr(torch, w["dtype"]))
+            if w["dtype"] == "bfloat16":
+                Xs = Xs.view(torch.int16).numpy().view(np.uint16)
+            else:
+                Xs = Xs.numpy()
+            t0 = time.perf_counter()  # the conversion to the input type is not the oracle's
+            oracle.quant_per_token(Xs, bits=w["bits"], dtype=w["dtype"])
+            part = len(rows) / w["M"]
         elif w["kind"] == "dwconv":
             npix = w["batch"] * w["H"] * w["W"]
             pix = np.arange(0, npix, frac)
@@ -199,7 +228,7 @@ def cpu_baseline(names, frac=16):
         parts.append(f"{name}:{part:.4f}")
     return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
             "kind": "oracle", "seconds": round(total_t, 2),
-            "sample": f"every {frac}th output row/pixel/weight row of each workload of one "
+            "sample": f"every {frac}th output row/pixel/weight row/token of each workload of one "
                       f"step ({', '.join(parts)} of the outputs)"}
 
 
@@ -406,8 +435,9 @@ def main():
             {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
              "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
              "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
+             "quant_a8": "per-token quant bf16 8192x8192 -> int8",
              "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
-                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..5",
+                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..7",
                    "timing": f"per workload: {args.warmup} warm-up calls, then "
                              f"{args.steps} back-to-back calls captured in a HIP graph "
                              f"and replayed between two HIP events (us_avg; value and "

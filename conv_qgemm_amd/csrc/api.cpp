@@ -221,6 +221,36 @@ qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int3
     return launched(qg::launch_dwconv_nhwc(d, (hipStream_t)stream));
 }
 
+qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, int64_t ldq,
+                           float *scale, int64_t M, int64_t K, float clip, int32_t bits,
+                           void *stream)
+{
+    if (!X || !Q || !scale)
+        return QG_ERR_NULLPTR;
+    if (dtype != QG_DT_F32 && dtype != QG_DT_F16 && dtype != QG_DT_BF16)
+        return QG_ERR_INVALID;
+    if (bits != 8 && bits != 4)
+        return QG_ERR_INVALID;
+    if (!(clip > 0.0f && clip <= 1.0f))  // also rejects NaN
+        return QG_ERR_INVALID;
+    if (M < 1 || K < 16 || K % 16 != 0 || M > kMaxDim || K > kMaxDim)
+        return QG_ERR_INVALID;
+    // whole 16-byte vectors per input row; 16-byte input rows; output rows
+    // 16 (int8) or 8 (int4) bytes
+    if (ldx < K || ldq < K || ldx % (dtype == QG_DT_F32 ? 4 : 8) != 0 || ldq % 16 != 0)
+        return QG_ERR_INVALID;
+    if ((M + 3) / 4 >= kMaxGrid)
+        return QG_ERR_INVALID;
+    if (!aligned16(X) || !aligned16(Q) || ((uintptr_t)scale & 3u) != 0)
+        return QG_ERR_INVALID;
+    int cus = 0;
+    qg_status st = check_device(&cus);
+    if (st != QG_OK)
+        return st;
+    qg::QuantDesc d{X, dtype, ldx, Q, ldq, scale, M, K, clip, bits};
+    return launched(qg::launch_quant_per_token(d, (hipStream_t)stream));
+}
+
 const char *qg_status_string(qg_status s)
 {
     switch (s) {

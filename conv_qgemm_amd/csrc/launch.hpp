@@ -54,6 +54,23 @@ hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s);
 // depthwise NHWC conv (k_dwconv.hip); C_in == C_out == the channel count
 hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s);
 
+// Per-token activation quantizer (k_quant.hip).  dtype 0 binary32, 1
+// binary16, 2 bfloat16; ldx in elements; ldq in output values (nibbles for
+// bits 4).
+struct QuantDesc {
+    const void *X;
+    int dtype;
+    int64_t ldx;
+    void *Q;
+    int64_t ldq;
+    float *scale;
+    int64_t M, K;
+    float clip;
+    int bits;
+};
+
+hipError_t launch_quant_per_token(const QuantDesc &d, hipStream_t s);
+
 // Largest M the weight-streaming W4A8 kernel takes; larger M is tiled.
 constexpr int64_t kSkinnyMaxM = 64;
 

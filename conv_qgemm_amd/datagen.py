@@ -21,6 +21,14 @@ bias in [-2^15, 2^15], Q31 multiplier in [2^30, 2^31), shift in 31..40):
   s8s8        M=N=K=8192 int8, shift 35..44
   dw3x3       depthwise NHWC 3x3 s1 p1, batch 32, 56x56, 64 channels,
               weights [3][3][64] (the MCU front-end page's depthwise layout)
+  quant_a8    per-token quantization of bfloat16 activations [8192][8192]
+              to int8 codes and float32 scales: the A operand of s8s8
+
+Float activations (``activations``) are standard normal, each token (row)
+scaled by a magnitude drawn log-uniformly from [1/16, 16], and a fixed set of
+outlier channels (columns, 1 in 128) scaled by 32 -- the shape of a
+transformer layer's input, whose per-token spread and few large channels are
+what per-token scales and clipping are for.
 """
 from __future__ import annotations
 
@@ -43,6 +51,7 @@ WORKLOADS = {
     "s8s8": dict(kind="s8s8", M=8192, N=8192, K=8192, shift=(35, 44), seed=5),
     "dw3x3": dict(kind="dwconv", batch=32, H=56, W=56, C=64, KH=3, KW=3,
                   stride=(1, 1), pad=(1, 1), shift=(31, 40), seed=6),
+    "quant_a8": dict(kind="quant", M=8192, K=8192, dtype="bfloat16", bits=8, seed=7),
 }
 
 # Variants whose shift windows keep most outputs inside [-128, 127], so that
@@ -113,6 +122,20 @@ def dwconv_nhwc(batch, H, W, C, KH, KW, seed, shift=SHIFT_DEFAULT):
     return dict(X=X, W=Wt, bias=bias, mult=mult, shift=sh)
 
 
+def activations(M, K, seed, outlier_every=128, outlier_gain=32.0):
+    """Float32 activations [M][K]: standard normal, times a per-token
+    magnitude 2^u with u uniform in [-4, 4), with every outlier_every-th
+    channel (from a random offset) times outlier_gain.  Draw order: values,
+    token exponents, outlier offset."""
+    g = rng(seed)
+    X = g.standard_normal((M, K), dtype=np.float32)
+    u = g.uniform(-4.0, 4.0, size=(M, 1)).astype(np.float32)
+    X *= np.exp2(u)
+    off = int(g.integers(0, outlier_every))
+    X[:, off::outlier_every] *= np.float32(outlier_gain)
+    return X
+
+
 def workload(name: str, unsaturated: bool = False, seed: int | None = None):
     """Arrays of a named workload (seeded); ``unsaturated`` picks the
     parity variant's shift window and seeds 101..105."""
@@ -131,6 +154,8 @@ def workload(name: str, unsaturated: bool = False, seed: int | None = None):
                          s, shift)
     if k == "dwconv":
         return dwconv_nhwc(w["batch"], w["H"], w["W"], w["C"], w["KH"], w["KW"], s, shift)
+    if k == "quant":
+        return dict(X=activations(w["M"], w["K"], s))
     raise KeyError(name)
 
 

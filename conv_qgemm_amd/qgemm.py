@@ -28,6 +28,12 @@ QG_ERR_LAUNCH = 4
 QG_S4S4_MAX_K = 131040
 QG_W4A8_MAX_K = 131040
 
+QG_DT_F32 = 0
+QG_DT_F16 = 1
+QG_DT_BF16 = 2
+_QUANT_DTYPES = {torch.float32: QG_DT_F32, torch.float16: QG_DT_F16,
+                 torch.bfloat16: QG_DT_BF16}
+
 
 class QGemmError(RuntimeError):
     def __init__(self, status: int, what: str):
@@ -51,6 +57,8 @@ def _load():
     lib.qconv2d_nhwc_s8_requant.restype = S
     lib.qdwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 10 + [P]
     lib.qdwconv2d_nhwc_s8_requant.restype = S
+    lib.qquant_per_token.argtypes = [P, I32, I64, P, I64, P, I64, I64, ctypes.c_float, I32, P]
+    lib.qquant_per_token.restype = S
     lib.qg_status_string.argtypes = [S]
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
@@ -60,8 +68,8 @@ def _load():
 
 lib = _load()
 EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
-           "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qg_status_string",
-           "qg_version")
+           "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qquant_per_token",
+           "qg_status_string", "qg_version")
 
 
 def status_string(status: int) -> str:
@@ -245,3 +253,40 @@ def qdwconv2d_nhwc_s8_requant(X, W, bias, mult, shift, stride=(1, 1), pad=(1, 1)
                                        pad[0], pad[1], _stream(stream))
     _check(st, "qdwconv2d_nhwc_s8_requant")
     return Y
+
+
+def qquant_per_token(X, bits=8, clip_ratio=1.0, Q=None, scale=None, stream=None):
+    """Symmetric per-token quantization of X [M, K] (float32, float16 or
+    bfloat16, unit column stride): scale[m] = max|X[m]| / (qmax / clip_ratio),
+    codes X / scale rounded half away from zero, clamped to +-qmax (127 for
+    bits 8, 7 for bits 4).  Returns (Q, scale): Q int8 [M, K], or for bits 4
+    uint8 [M, K/2] with element 2i in the low nibble of byte i; scale float32
+    [M]."""
+    if X.dtype not in _QUANT_DTYPES:
+        raise TypeError(f"X must be float32, float16 or bfloat16, got {X.dtype}")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D tensor with unit column stride")
+    _on_device(X, "X")
+    M, K = X.shape
+    if bits == 8:
+        qdtype, qcols = torch.int8, K
+    elif bits == 4:
+        qdtype, qcols = torch.uint8, K // 2
+    else:
+        raise ValueError("bits must be 8 or 4")
+    if Q is None:
+        Q = torch.empty((M, qcols), dtype=qdtype, device=X.device)
+    _mat(Q, qdtype, "Q")
+    if Q.shape[0] != M or Q.shape[1] < qcols:
+        raise ValueError(f"Q must have {M} rows of at least {qcols} columns")
+    if scale is None:
+        scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if scale.dtype != torch.float32 or scale.dim() != 1 or scale.numel() < M or \
+            scale.stride(0) != 1:
+        raise ValueError(f"scale must be a contiguous float32 vector of length >= {M}")
+    _on_device(scale, "scale")
+    ldq = Q.stride(0) * (2 if bits == 4 else 1)
+    st = lib.qquant_per_token(_ptr(X), _QUANT_DTYPES[X.dtype], X.stride(0), _ptr(Q), ldq,
+                              _ptr(scale), M, K, float(clip_ratio), bits, _stream(stream))
+    _check(st, "qquant_per_token")
+    return Q, scale

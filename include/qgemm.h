@@ -75,6 +75,11 @@ typedef enum {
 #define QG_S4S4_MAX_K 131040
 #define QG_W4A8_MAX_K 131040
 
+/* Input element types of qquant_per_token. */
+#define QG_DT_F32 0
+#define QG_DT_F16 1
+#define QG_DT_BF16 2
+
 /*
  * qgemm_s8s8_requant -- C[m][n] = requant(sum_k A[m][k] * B[n][k]).
  *   A     int8  [M][lda], row-major, lda >= K
@@ -160,6 +165,30 @@ qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W,
                                     int32_t batch, int32_t H, int32_t Wd, int32_t C,
                                     int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
                                     int32_t pad_h, int32_t pad_w, void *stream);
+
+/*
+ * qquant_per_token -- symmetric per-token quantization of float activations.
+ *   X      [M][ldx] elements of dtype: QG_DT_F32 (binary32), QG_DT_F16
+ *          (binary16) or QG_DT_BF16 (bfloat16); finite values
+ *   Q      bits 8: int8 [M][ldq]; bits 4: packed int4 [M][ldq/2 bytes],
+ *          element 2i in the low nibble of byte i
+ *   scale  float32 [M], written: scale[m] = max_k |X[m][k]| / (qmax / clip)
+ *   qmax = 127 (bits 8) or 7 (bits 4); Q[m][k] = X[m][k] / scale[m] in
+ *   binary32, rounded half away from zero and clamped to [-qmax, qmax];
+ *   a token of zeros gets scale 0 and codes 0.  All arithmetic is IEEE
+ *   binary32 (half inputs are widened exactly first).
+ *   M >= 1; 16 <= K, K % 16 == 0; ldx >= K with ldx % 8 == 0 (ldx % 4 == 0
+ *   for binary32); ldq >= K, ldq % 16 == 0; 0 < clip <= 1; X, Q 16-byte
+ *   aligned, scale 4-byte aligned.
+ * Ascend FlatQuant operator article (www.zwxr.cn/news/277566), per-token
+ * mode (the scale, clip_ratio, int4 range); Voyager quantization article
+ * (www.dpshk.com/news/2695434) §1.1 (round half away from zero, zero point
+ * 0); INT4 GEMM article §2.1 (nibble order).  The codes feed the A operand
+ * of the GEMMs above.
+ */
+qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, int64_t ldq,
+                           float *scale, int64_t M, int64_t K, float clip, int32_t bits,
+                           void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *qg_status_string(qg_status s);

@@ -28,7 +28,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(qg):
     names = _declared_functions()
     assert set(names) >= {"qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
-                          "qconv2d_nhwc_s8_requant", "qg_status_string", "qg_version"}
+                          "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant",
+                          "qquant_per_token", "qg_status_string", "qg_version"}
     raw = ctypes.CDLL(qg._LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -51,6 +52,8 @@ def test_header_constants_match_binding(qg):
     assert 256 * 64 * qg.QG_S4S4_MAX_K < 2 ** 31
     assert 16 * 128 * 8 * qg.QG_W4A8_MAX_K < 2 ** 31
     assert qg.QG_S4S4_MAX_K % 32 == 0
+    for name in ("QG_DT_F32", "QG_DT_F16", "QG_DT_BF16"):
+        assert int(re.search(name + r" (\d+)", text).group(1)) == getattr(qg, name)
 
 
 P = 0x10000  # fake, 16-byte aligned device addresses
@@ -81,6 +84,10 @@ def dw(qg, X=P, W=P, bias=P, mult=P, shift=P, Y=P, batch=1, H=8, Wd=8, C=16, KH=
                                             sh, sw, ph, pw, None)
 
 
+def qt(qg, X=P, dtype=0, ldx=64, Q=P, ldq=64, scale=P, M=8, K=64, clip=1.0, bits=8):
+    return qg.lib.qquant_per_token(X, dtype, ldx, Q, ldq, scale, M, K, clip, bits, None)
+
+
 def test_nullptr(qg):
     E = qg.QG_ERR_NULLPTR
     for kw in ("A", "B", "C", "mult", "shift"):
@@ -91,6 +98,8 @@ def test_nullptr(qg):
     for kw in ("X", "W", "Y", "mult", "shift"):
         assert cv(qg, **{kw: NULL}) == E, kw
         assert dw(qg, **{kw: NULL}) == E, kw
+    for kw in ("X", "Q", "scale"):
+        assert qt(qg, **{kw: NULL}) == E, kw
 
 
 def test_invalid_gemm_sizes(qg):
@@ -157,6 +166,29 @@ def test_invalid_dwconv(qg):
     assert dw(qg, batch=2 ** 20, H=2 ** 10, Wd=2 ** 10) == E  # too many pixels
 
 
+def test_invalid_quant(qg):
+    E = qg.QG_ERR_INVALID
+    assert qt(qg, dtype=3) == E
+    assert qt(qg, dtype=-1) == E
+    for bits in (0, 2, 16):
+        assert qt(qg, bits=bits) == E
+    for clip in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert qt(qg, clip=clip) == E, clip
+    assert qt(qg, M=0) == E
+    assert qt(qg, K=0) == E
+    assert qt(qg, K=8, ldx=64) == E             # K < 16
+    assert qt(qg, K=40, ldx=64, ldq=64) == E    # K % 16
+    assert qt(qg, ldx=48, K=64) == E            # ldx < K
+    assert qt(qg, ldq=48, K=64) == E            # ldq < K
+    assert qt(qg, ldx=68, K=64, dtype=1) == E   # half rows must be 16-byte multiples
+    assert qt(qg, ldx=66, K=64, dtype=0) == E   # float rows must be 16-byte multiples
+    assert qt(qg, ldq=72, K=64) == E            # ldq % 16
+    assert qt(qg, M=2 ** 31) == E
+    for kw in ("X", "Q"):
+        assert qt(qg, **{kw: P + 8}) == E, kw
+    assert qt(qg, scale=P + 2) == E
+
+
 def test_valid_call_without_gpu_reports_no_device(qg):
     import torch
     if torch.cuda.is_available():
@@ -166,6 +198,8 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert w4(qg) == qg.QG_ERR_NO_DEVICE
     assert cv(qg) == qg.QG_ERR_NO_DEVICE
     assert dw(qg) == qg.QG_ERR_NO_DEVICE
+    assert qt(qg) == qg.QG_ERR_NO_DEVICE
+    assert qt(qg, dtype=2, bits=4, ldx=72, ldq=80, scale=P + 4, clip=0.25) == qg.QG_ERR_NO_DEVICE
 
 
 def test_binding_rejects_bad_tensors(qg):
@@ -199,3 +233,7 @@ def test_binding_rejects_host_tensors(qg):
     with pytest.raises(ValueError, match="GPU tensor"):
         qg.qconv2d_nhwc_s8_requant(X, W, v16, v16, v16, Y=torch.zeros((1, 4, 4, 16),
                                                                      dtype=torch.int8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qg.qquant_per_token(torch.zeros((4, 64), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        qg.qquant_per_token(torch.zeros((4, 64), dtype=torch.float64))

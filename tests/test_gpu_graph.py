@@ -1,4 +1,4 @@
-"""The four entry points inside a captured HIP graph (torch.cuda.CUDAGraph).
+"""The entry points inside a captured HIP graph (torch.cuda.CUDAGraph).
 
 The library only enqueues kernels on the caller's stream (no allocation, no
 memset, no synchronization), so a caller can capture a sequence of calls and
@@ -26,9 +26,9 @@ def qg():
     return qgemm
 
 
-def _run_graph_case(torch, make_inputs, call):
-    """make_inputs(seed) -> dict of device tensors (inputs and the output 'out');
-    call(d) enqueues the library call writing d['out']."""
+def _run_graph_case(torch, make_inputs, call, outs=("out",)):
+    """make_inputs(seed) -> dict of device tensors (inputs and the outputs
+    named in outs); call(d) enqueues the library call writing the outputs."""
     d = make_inputs(1)
     call(d)  # eager first: one-time device setup happens outside the capture
     torch.cuda.synchronize()
@@ -40,17 +40,20 @@ def _run_graph_case(torch, make_inputs, call):
         # new input contents in the captured buffers, eager reference beside
         fresh = make_inputs(10 + r)
         for k, v in fresh.items():
-            if k != "out":
+            if k not in outs:
                 d[k].copy_(v)
         ref = {k: v.clone() for k, v in d.items()}
-        ref["out"] = torch.empty_like(d["out"])
+        for k in outs:
+            ref[k] = torch.empty_like(d[k])
         call(ref)
-        d["out"].fill_(7)
+        for k in outs:
+            d[k].fill_(7)
         junk = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(d["out"].cpu(), ref["out"].cpu()), f"replay {r} differs from eager"
+        for k in outs:
+            assert torch.equal(d[k].cpu(), ref[k].cpu()), f"replay {r}: {k} differs from eager"
         del junk
 
 
@@ -136,6 +139,22 @@ def test_graph_dwconv(qg, KH):
     _run_graph_case(torch, make, lambda d: qg.qdwconv2d_nhwc_s8_requant(
         d["X"], d["W"], d["bias"], d["mult"], d["shift"], stride=(1, 1),
         pad=(KH // 2, KH // 2), Y=d["out"]))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_graph_quant(qg, bits):
+    import torch
+
+    def make(seed):
+        X = torch.from_numpy(datagen.activations(40, 1040, seed)).to(torch.bfloat16).cuda()
+        cols = 1040 if bits == 8 else 520
+        return {"X": X,
+                "out": torch.empty((40, cols), dtype=torch.int8 if bits == 8 else torch.uint8,
+                                   device="cuda"),
+                "scale": torch.empty(40, dtype=torch.float32, device="cuda")}
+
+    _run_graph_case(torch, make, lambda d: qg.qquant_per_token(
+        d["X"], bits=bits, Q=d["out"], scale=d["scale"]), outs=("out", "scale"))
 
 
 def test_graph_matches_oracle(qg, orc):
