@@ -83,6 +83,29 @@ def _load():
     lib.orc_dwconv2d_acc.restype = ctypes.c_int
     lib.orc_dwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I64] * 10 + [P, I64]
     lib.orc_dwconv2d_nhwc_s8_requant.restype = ctypes.c_int
+    lib.orc_requant_zp.argtypes = [I64, I32, I32, I32, I32, P]
+    lib.orc_requant_zp.restype = ctypes.c_int
+    lib.orc_gemm_s8s8_acc_zp.argtypes = [P, I64, P, I64, I32, I32, I64, I64, P, I64, P]
+    lib.orc_gemm_s8s8_acc_zp.restype = ctypes.c_int
+    lib.orc_gemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, P, I64,
+                                             I64, I64, P, I64]
+    lib.orc_gemm_s8s8_requant_zp.restype = ctypes.c_int
+    lib.orc_conv2d_acc_zp.argtypes = [P, P] + [I64] * 11 + [I32, I32, P, I64, P]
+    lib.orc_conv2d_acc_zp.restype = ctypes.c_int
+    lib.orc_conv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+        [I64] * 11 + [P, I64]
+    lib.orc_conv2d_nhwc_s8_requant_zp.restype = ctypes.c_int
+    lib.orc_dwconv2d_acc_zp.argtypes = [P, P] + [I64] * 10 + [I32, I32, P, I64, P]
+    lib.orc_dwconv2d_acc_zp.restype = ctypes.c_int
+    lib.orc_dwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+        [I64] * 10 + [P, I64]
+    lib.orc_dwconv2d_nhwc_s8_requant_zp.restype = ctypes.c_int
+    lib.orc_int4_at_msb.argtypes = [P, I64]
+    lib.orc_int4_at_msb.restype = ctypes.c_int
+    lib.orc_gemm_s4s4_i32_msb.argtypes = [P, I64, P, I64, P, I64, I64, I64, P, I64]
+    lib.orc_gemm_s4s4_i32_msb.restype = ctypes.c_int
+    lib.orc_gemm_w4a8_requant_msb.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, P, I64]
+    lib.orc_gemm_w4a8_requant_msb.restype = ctypes.c_int
     lib.orc_quant_per_token.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_float,
                                          ctypes.c_int, P, I64, P]
     lib.orc_quant_per_token.restype = ctypes.c_int
@@ -148,6 +171,23 @@ def int4_at(packed_row: np.ndarray, i: int) -> int:
     return int(_load().orc_int4_at(row.ctypes.data, int(i)))
 
 
+def int4_at_msb(packed_row: np.ndarray, i: int) -> int:
+    """Signed value of element i of an MSB-first packed int4 row."""
+    row = _c(packed_row, np.uint8)
+    if not 0 <= i < 2 * row.size:
+        raise IndexError(i)
+    return int(_load().orc_int4_at_msb(row.ctypes.data, int(i)))
+
+
+def requant_zp(acc: int, bias: int, mult: int, shift: int, out_zero: int) -> int:
+    """clamp((((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero)."""
+    out = np.zeros(1, dtype=np.int8)
+    st = _load().orc_requant_zp(int(acc), int(bias), int(mult), int(shift), int(out_zero),
+                                out.ctypes.data)
+    _check(st, "requant_zp")
+    return int(out[0])
+
+
 def requant(acc: int, bias: int, mult: int, shift: int) -> int:
     """One Q31 requantize: clamp(((acc + bias) * mult + 2^(shift-1)) >> shift)."""
     out = np.zeros(1, dtype=np.int8)
@@ -200,7 +240,9 @@ def gemm_s8s8_requant(A, B, bias, mult, shift, rows=None):
     return C
 
 
-def gemm_w4a8_requant(A, Bp, bias, mult, shift, rows=None):
+def gemm_w4a8_requant(A, Bp, bias, mult, shift, rows=None, msb_first=False):
+    """int8 A [M][K] x packed int4 B [N][K/2] (low nibble first, or high
+    nibble first with msb_first) -> requantized int8."""
     A = _c(A, np.int8)
     Bp = _c(Bp, np.uint8)
     M, K = A.shape
@@ -211,14 +253,17 @@ def gemm_w4a8_requant(A, Bp, bias, mult, shift, rows=None):
     shift = _c(shift, np.int32)
     r, nr = _rows(rows, M)
     C = np.zeros((nr, N), dtype=np.int8)
-    st = _load().orc_gemm_w4a8_requant(A.ctypes.data, K, Bp.ctypes.data, K, _ptr(bias_c),
+    f = _load().orc_gemm_w4a8_requant_msb if msb_first else _load().orc_gemm_w4a8_requant
+    st = f(A.ctypes.data, K, Bp.ctypes.data, K, _ptr(bias_c),
                                        mult.ctypes.data, shift.ctypes.data, C.ctypes.data, N,
                                        N, K, _ptr(r), nr)
     _check(st, "gemm_w4a8_requant")
     return C
 
 
-def gemm_s4s4_i32(Ap, Bp, rows=None):
+def gemm_s4s4_i32(Ap, Bp, rows=None, msb_first=False):
+    """packed int4 A [M][K/2] x packed int4 B [N][K/2] -> raw int32; both
+    operands low nibble first, or both high nibble first with msb_first."""
     Ap = _c(Ap, np.uint8)
     Bp = _c(Bp, np.uint8)
     M, Kh = Ap.shape
@@ -227,7 +272,8 @@ def gemm_s4s4_i32(Ap, Bp, rows=None):
     K = 2 * Kh
     r, nr = _rows(rows, M)
     C = np.zeros((nr, N), dtype=np.int32)
-    st = _load().orc_gemm_s4s4_i32(Ap.ctypes.data, K, Bp.ctypes.data, K, C.ctypes.data, N,
+    f = _load().orc_gemm_s4s4_i32_msb if msb_first else _load().orc_gemm_s4s4_i32
+    st = f(Ap.ctypes.data, K, Bp.ctypes.data, K, C.ctypes.data, N,
                                    N, K, _ptr(r), nr)
     _check(st, "gemm_s4s4_i32")
     return C
@@ -376,3 +422,104 @@ def f16_to_f32(h):
 
 def bf16_to_f32(b):
     return float(_load().orc_bf16_to_f32(int(b)))
+
+
+# ---- asymmetric forms: per-tensor zero points of A (or X), B (or W) and
+# the output; padding holds the input zero point ----
+
+def gemm_s8s8_acc_zp(A, B, a_zero, b_zero, rows=None):
+    """int64 accumulators sum_k (A[m][k] - a_zero) * (B[n][k] - b_zero)."""
+    A = _c(A, np.int8)
+    B = _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    r, nr = _rows(rows, M)
+    out = np.zeros((nr, N), dtype=np.int64)
+    _check(_load().orc_gemm_s8s8_acc_zp(A.ctypes.data, K, B.ctypes.data, K, int(a_zero),
+                                        int(b_zero), N, K, _ptr(r), nr, out.ctypes.data),
+           "gemm_s8s8_acc_zp")
+    return out
+
+
+def gemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, rows=None):
+    A = _c(A, np.int8)
+    B = _c(B, np.int8)
+    M, K = A.shape
+    N = B.shape[0]
+    assert B.shape[1] == K
+    bias_c = None if bias is None else _c(bias, np.int32)
+    mult = _c(mult, np.int32)
+    shift = _c(shift, np.int32)
+    r, nr = _rows(rows, M)
+    C = np.zeros((nr, N), dtype=np.int8)
+    st = _load().orc_gemm_s8s8_requant_zp(A.ctypes.data, K, B.ctypes.data, K, _ptr(bias_c),
+                                          mult.ctypes.data, shift.ctypes.data, int(a_zero),
+                                          int(b_zero), int(out_zero), C.ctypes.data, N, N, K,
+                                          _ptr(r), nr)
+    _check(st, "gemm_s8s8_requant_zp")
+    return C
+
+
+def conv2d_acc_zp(X, Wt, a_zero, b_zero, stride=(1, 1), pad=(1, 1), pix=None):
+    X, Wt, g, Ho, Wo = _conv_geom(X, Wt, stride, pad)
+    batch, C_out = g[0], g[4]
+    r, nr = _rows(pix, batch * Ho * Wo)
+    out = np.zeros((nr, C_out), dtype=np.int64)
+    _check(_load().orc_conv2d_acc_zp(X.ctypes.data, Wt.ctypes.data, *g, int(a_zero),
+                                     int(b_zero), _ptr(r), nr, out.ctypes.data),
+           "conv2d_acc_zp")
+    if pix is None:
+        return out.reshape(batch, Ho, Wo, C_out)
+    return out
+
+
+def conv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_zero,
+                              stride=(1, 1), pad=(1, 1), pix=None):
+    X, Wt, g, Ho, Wo = _conv_geom(X, Wt, stride, pad)
+    batch, C_out = g[0], g[4]
+    bias_c = None if bias is None else _c(bias, np.int32)
+    mult = _c(mult, np.int32)
+    shift = _c(shift, np.int32)
+    r, nr = _rows(pix, batch * Ho * Wo)
+    Y = np.zeros((nr, C_out), dtype=np.int8)
+    st = _load().orc_conv2d_nhwc_s8_requant_zp(X.ctypes.data, Wt.ctypes.data, _ptr(bias_c),
+                                               mult.ctypes.data, shift.ctypes.data,
+                                               int(a_zero), int(b_zero), int(out_zero),
+                                               Y.ctypes.data, *g, _ptr(r), nr)
+    _check(st, "conv2d_nhwc_s8_requant_zp")
+    if pix is None:
+        return Y.reshape(batch, Ho, Wo, C_out)
+    return Y
+
+
+def dwconv2d_acc_zp(X, Wt, a_zero, b_zero, stride=(1, 1), pad=(1, 1), pix=None):
+    X, Wt, g, Ho, Wo = _dw_geom(X, Wt, stride, pad)
+    batch, C = g[0], g[3]
+    r, nr = _rows(pix, batch * Ho * Wo)
+    out = np.zeros((nr, C), dtype=np.int64)
+    _check(_load().orc_dwconv2d_acc_zp(X.ctypes.data, Wt.ctypes.data, *g, int(a_zero),
+                                       int(b_zero), _ptr(r), nr, out.ctypes.data),
+           "dwconv2d_acc_zp")
+    if pix is None:
+        return out.reshape(batch, Ho, Wo, C)
+    return out
+
+
+def dwconv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_zero,
+                                stride=(1, 1), pad=(1, 1), pix=None):
+    X, Wt, g, Ho, Wo = _dw_geom(X, Wt, stride, pad)
+    batch, C = g[0], g[3]
+    bias_c = None if bias is None else _c(bias, np.int32)
+    mult = _c(mult, np.int32)
+    shift = _c(shift, np.int32)
+    r, nr = _rows(pix, batch * Ho * Wo)
+    Y = np.zeros((nr, C), dtype=np.int8)
+    st = _load().orc_dwconv2d_nhwc_s8_requant_zp(X.ctypes.data, Wt.ctypes.data, _ptr(bias_c),
+                                                 mult.ctypes.data, shift.ctypes.data,
+                                                 int(a_zero), int(b_zero), int(out_zero),
+                                                 Y.ctypes.data, *g, _ptr(r), nr)
+    _check(st, "dwconv2d_nhwc_s8_requant_zp")
+    if pix is None:
+        return Y.reshape(batch, Ho, Wo, C)
+    return Y

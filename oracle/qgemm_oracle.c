@@ -39,7 +39,11 @@
  *   - GEMM layouts: A is [M][lda] row-major, B is [N][ldb] (K contiguous,
  *     i.e. column-major K x N); packed operands count lda/ldb in nibbles.
  *   - conv: NHWC input, OHWI weights, dilation 1, one group, symmetric
- *     padding filled with 0, floor output-size formula.
+ *     padding filled with the input zero point (0 unless given), floor
+ *     output-size formula.
+ *   - asymmetric forms: one zero point per tensor for each operand and for
+ *     the output, in [-128, 127]; the output zero point is added to the
+ *     shifted value before the int8 saturation.
  *
  * Every entry point can compute a subset of output rows (GEMM) or output
  * pixels (conv) so that full-size problems can be checked on samples; the
@@ -377,6 +381,300 @@ int orc_dwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
             int8_t y = 0;
             status |= orc_requant(acc, bias ? bias[c] : 0, mult[c], shift[c], &y);
             Y[r * C + c] = y;
+        }
+    }
+    return status;
+}
+
+/* ---- asymmetric quantization.  [VOYAGER] §1.1: a code Q stands for the
+ * real value (Q - zero_point) * scale.  [INT4-GEMM] §4.1: both GEMM operands
+ * carry a zero point, and the product picks up a compensation term.
+ * [MCU-CONV] §2.3: the padding of an asymmetric input is its zero point;
+ * §3.3: the requantize adds the output zero point.  Zero points are per
+ * tensor, in the int8 code range.  The product of two dequantized operands
+ * is scale_a * scale_b * (A - za) * (B - zb), so the integer accumulator is
+ * sum_k (A[m][k] - za) * (B[n][k] - zb), written out below term by term. ---- */
+
+/* Q31 requantize with an output zero point: the shifted value plus
+ * out_zero, saturated to int8. */
+int orc_requant_zp(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int32_t out_zero,
+                   int8_t *out)
+{
+    const int64_t x = acc + bias;
+    if (x < INT32_MIN || x > INT32_MAX)
+        return ORC_E_RANGE;
+    if (shift < 1 || shift > 63 || mult < 0 || out_zero < -128 || out_zero > 127)
+        return ORC_E_DOMAIN;
+    int64_t t = (int64_t)mult * x;          /* |t| < 2^62 */
+    t += (int64_t)1 << (shift - 1);         /* half an LSB */
+    t >>= shift;                            /* arithmetic shift (gcc) */
+    t += out_zero;                          /* output zero point */
+    *out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));
+    return ORC_OK;
+}
+
+static int zero_point_ok(int32_t z)
+{
+    return z >= -128 && z <= 127;
+}
+
+static int64_t dot_s8_s8_zp(const int8_t *a, const int8_t *b, int64_t K, int64_t za, int64_t zb)
+{
+    int64_t acc = 0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);
+    return acc;
+}
+
+/* acc[r][n] = sum_k (A[m_r][k] - a_zero) * (B[n][k] - b_zero) as int64. */
+int orc_gemm_s8s8_acc_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                         int32_t a_zero, int32_t b_zero, int64_t N, int64_t K,
+                         const int64_t *rows, int64_t nrows, int64_t *out)
+{
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n)
+            out[r * N + n] = dot_s8_s8_zp(A + m * lda, B + n * ldb, K, a_zero, b_zero);
+    }
+    return ORC_OK;
+}
+
+/* asymmetric int8 x int8 -> requantized int8 with an output zero point */
+int orc_gemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                             const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                             int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                             int8_t *C, int64_t ldc, int64_t N, int64_t K,
+                             const int64_t *rows, int64_t nrows)
+{
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = dot_s8_s8_zp(A + m * lda, B + n * ldb, K, a_zero, b_zero);
+            int8_t y = 0;
+            status |= orc_requant_zp(acc, bias ? bias[n] : 0, mult[n], shift[n], out_zero, &y);
+            C[r * ldc + n] = y;
+        }
+    }
+    return status;
+}
+
+/* One output element of the asymmetric conv: positions outside the image
+ * hold the input zero point, so they contribute (za - za) * (w - zb) = 0. */
+static int64_t conv_acc_zp_at(const int8_t *X, const int8_t *Wt,
+                              int64_t H, int64_t W, int64_t C_in,
+                              int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                              int64_t ph, int64_t pw, int64_t za, int64_t zb,
+                              int64_t b, int64_t oh, int64_t ow, int64_t oc)
+{
+    const int8_t *wrow = Wt + oc * KH * KW * C_in;  /* OHWI row of channel oc */
+    int64_t acc = 0;
+    for (int64_t kh = 0; kh < KH; ++kh) {
+        for (int64_t kw = 0; kw < KW; ++kw) {
+            const int64_t y = kh + oh * sh - ph;
+            const int64_t xx = kw + ow * sw - pw;
+            const int inside = y >= 0 && y < H && xx >= 0 && xx < W;
+            for (int64_t ci = 0; ci < C_in; ++ci) {
+                int64_t x = inside ? X[((b * H + y) * W + xx) * C_in + ci] : za;
+                int64_t w = wrow[(kh * KW + kw) * C_in + ci];
+                acc += (x - za) * (w - zb);
+            }
+        }
+    }
+    return acc;
+}
+
+int orc_conv2d_acc_zp(const int8_t *X, const int8_t *Wt,
+                      int64_t batch, int64_t H, int64_t W, int64_t C_in, int64_t C_out,
+                      int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                      int32_t a_zero, int32_t b_zero,
+                      const int64_t *pix, int64_t npix, int64_t *out)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    (void)batch;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t oc = 0; oc < C_out; ++oc)
+            out[r * C_out + oc] = conv_acc_zp_at(X, Wt, H, W, C_in, KH, KW, sh, sw, ph, pw,
+                                                 a_zero, b_zero, b, oh, ow, oc);
+    }
+    return ORC_OK;
+}
+
+int orc_conv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
+                                  const int32_t *bias, const int32_t *mult,
+                                  const int32_t *shift, int32_t a_zero, int32_t b_zero,
+                                  int32_t out_zero, int8_t *Y,
+                                  int64_t batch, int64_t H, int64_t W, int64_t C_in,
+                                  int64_t C_out, int64_t KH, int64_t KW, int64_t sh,
+                                  int64_t sw, int64_t ph, int64_t pw,
+                                  const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    int status = ORC_OK;
+    (void)batch;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(| : status)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t oc = 0; oc < C_out; ++oc) {
+            int64_t acc = conv_acc_zp_at(X, Wt, H, W, C_in, KH, KW, sh, sw, ph, pw,
+                                         a_zero, b_zero, b, oh, ow, oc);
+            int8_t y = 0;
+            status |= orc_requant_zp(acc, bias ? bias[oc] : 0, mult[oc], shift[oc], out_zero,
+                                     &y);
+            Y[r * C_out + oc] = y;
+        }
+    }
+    return status;
+}
+
+/* The depthwise form: channel c alone, weights [kh][kw][c]. */
+static int64_t dwconv_acc_zp_at(const int8_t *X, const int8_t *Wt,
+                                int64_t H, int64_t W, int64_t C,
+                                int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                                int64_t ph, int64_t pw, int64_t za, int64_t zb,
+                                int64_t b, int64_t oh, int64_t ow, int64_t c)
+{
+    int64_t acc = 0;
+    for (int64_t t = 0; t < KH * KW; ++t) {      /* taps in [kh][kw] order */
+        const int64_t kh = t / KW, kw = t % KW;
+        const int64_t y = kh + oh * sh - ph;
+        const int64_t xx = kw + ow * sw - pw;
+        const int inside = y >= 0 && y < H && xx >= 0 && xx < W;
+        const int64_t x = inside ? X[(((b * H) + y) * W + xx) * C + c] : za;
+        const int64_t w = Wt[t * C + c];
+        acc += (x - za) * (w - zb);
+    }
+    return acc;
+}
+
+int orc_dwconv2d_acc_zp(const int8_t *X, const int8_t *Wt,
+                        int64_t batch, int64_t H, int64_t W, int64_t C,
+                        int64_t KH, int64_t KW, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                        int32_t a_zero, int32_t b_zero,
+                        const int64_t *pix, int64_t npix, int64_t *out)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    (void)batch;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t c = 0; c < C; ++c)
+            out[r * C + c] = dwconv_acc_zp_at(X, Wt, H, W, C, KH, KW, sh, sw, ph, pw,
+                                              a_zero, b_zero, b, oh, ow, c);
+    }
+    return ORC_OK;
+}
+
+int orc_dwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
+                                    const int32_t *bias, const int32_t *mult,
+                                    const int32_t *shift, int32_t a_zero, int32_t b_zero,
+                                    int32_t out_zero, int8_t *Y,
+                                    int64_t batch, int64_t H, int64_t W, int64_t C,
+                                    int64_t KH, int64_t KW, int64_t sh, int64_t sw,
+                                    int64_t ph, int64_t pw, const int64_t *pix, int64_t npix)
+{
+    int64_t Ho = orc_conv_out_size(H, KH, sh, ph);
+    int64_t Wo = orc_conv_out_size(W, KW, sw, pw);
+    int status = ORC_OK;
+    (void)batch;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero))
+        return ORC_E_DOMAIN;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(| : status)
+    for (int64_t r = 0; r < npix; ++r) {
+        int64_t p = pix ? pix[r] : r;
+        int64_t b = p / (Ho * Wo);
+        int64_t oh = (p / Wo) % Ho;
+        int64_t ow = p % Wo;
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t acc = dwconv_acc_zp_at(X, Wt, H, W, C, KH, KW, sh, sw, ph, pw,
+                                           a_zero, b_zero, b, oh, ow, c);
+            int8_t y = 0;
+            status |= orc_requant_zp(acc, bias ? bias[c] : 0, mult[c], shift[c], out_zero, &y);
+            Y[r * C + c] = y;
+        }
+    }
+    return status;
+}
+
+/* ---- MSB-first INT4 packing ([INT4-GEMM] §3.2 names it as the order some
+ * NPUs expect; the conversion script of its §4.1 packs the first element of
+ * each pair into the high nibble): element 2i is the HIGH nibble of byte i,
+ * element 2i+1 the low one; codes stay 4-bit two's complement. ---- */
+int orc_int4_at_msb(const uint8_t *row, int64_t i)
+{
+    const int byte = row[i / 2];
+    const int code = (i % 2 == 0) ? (byte >> 4) : (byte & 0x0F);
+    return code >= 8 ? code - 16 : code;
+}
+
+/* packed int4 x packed int4 -> raw int32, both operands MSB-first */
+int orc_gemm_s4s4_i32_msb(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                          int32_t *C, int64_t ldc, int64_t N, int64_t K,
+                          const int64_t *rows, int64_t nrows)
+{
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        const uint8_t *a = A + m * (lda / 2);
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *b = B + n * (ldb / 2);
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)orc_int4_at_msb(a, k) * (int64_t)orc_int4_at_msb(b, k);
+            if (acc < INT32_MIN || acc > INT32_MAX)
+                status |= ORC_E_RANGE;
+            C[r * ldc + n] = (int32_t)acc;
+        }
+    }
+    return status;
+}
+
+/* int8 activations x MSB-first packed int4 weights -> requantized int8 */
+int orc_gemm_w4a8_requant_msb(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                              const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                              int8_t *C, int64_t ldc, int64_t N, int64_t K,
+                              const int64_t *rows, int64_t nrows)
+{
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        const int8_t *a = A + m * lda;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *b = B + n * (ldb / 2);
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)a[k] * (int64_t)orc_int4_at_msb(b, k);
+            int8_t y = 0;
+            status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[n], &y);
+            C[r * ldc + n] = y;
         }
     }
     return status;

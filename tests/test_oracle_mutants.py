@@ -13,7 +13,8 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_int4.py", "tests/test_oracle_requant.py",
              "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py",
-             "tests/test_oracle_dwconv.py", "tests/test_oracle_quant.py"]
+             "tests/test_oracle_dwconv.py", "tests/test_oracle_quant.py",
+             "tests/test_oracle_zp.py"]
 
 MUTANTS = {
     "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
@@ -47,6 +48,22 @@ MUTANTS = {
                          "float a = v;\n            if (a > amax)"),
     "quant_nibble_swap": ("if (k % 2 == 0)\n                    *byte",
                           "if (k % 2 == 1)\n                    *byte"),
+    "zp_out_zero_dropped": ("t += out_zero;", "t += 0;"),
+    "zp_out_zero_after_clamp": ("t += out_zero;                          /* output zero point */\n"
+                                "    *out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));",
+                                "*out = (int8_t)((t > 127 ? 127 : (t < -128 ? -128 : t)) + out_zero);"),
+    "zp_a_zero_dropped": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",
+                          "acc += ((int64_t)a[k]) * ((int64_t)b[k] - zb);"),
+    "zp_b_zero_sign": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",
+                       "acc += ((int64_t)a[k] - za) * ((int64_t)b[k] + zb);"),
+    "zp_conv_pad_zero": ("int64_t x = inside ? X[((b * H + y) * W + xx) * C_in + ci] : za;",
+                         "int64_t x = inside ? X[((b * H + y) * W + xx) * C_in + ci] : 0;"),
+    "zp_dw_pad_zero": ("const int64_t x = inside ? X[(((b * H) + y) * W + xx) * C + c] : za;",
+                       "const int64_t x = inside ? X[(((b * H) + y) * W + xx) * C + c] : 0;"),
+    "zp_dw_w_zero_dropped": ("const int64_t w = Wt[t * C + c];\n        acc += (x - za) * (w - zb);",
+                             "const int64_t w = Wt[t * C + c];\n        acc += (x - za) * w;"),
+    "msb_nibble_order": ("const int code = (i % 2 == 0) ? (byte >> 4) : (byte & 0x0F);",
+                         "const int code = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);"),
     "dw_tap_dropped": ("for (int64_t kw = 0; kw < KW; ++kw) {\n            const int64_t iw",
                        "for (int64_t kw = 0; kw + 1 < KW; ++kw) {\n            const int64_t iw"),
 }
@@ -87,6 +104,7 @@ def test_ubsan_build_runs_clean(tmp_path):
                  out=str(lib))
     env = dict(os.environ, QG_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_requant.py", "tests/test_oracle_conv.py"],
+                        "tests/test_oracle_requant.py", "tests/test_oracle_conv.py",
+                        "tests/test_oracle_zp.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
