@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "qgemm")
 LIB = os.path.join(PKG, "libqgemm.so")
 SOURCES = ["api.cpp", "k_tile_gemm.hip", "k_gemm_dma.hip", "k_skinny_w4a8.hip", "k_conv_halo.hip", "k_dwconv.hip",
-           "k_quant.hip"]
+           "k_quant.hip", "k_zp.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -86,6 +86,76 @@ qg_status check_params(const int32_t *bias, const int32_t *mult, const int32_t *
     return QG_OK;
 }
 
+// Conv checks shared by the symmetric and asymmetric entry points; returns
+// the output size.
+qg_status check_conv(const int8_t *X, const int8_t *W, const int8_t *Y, int32_t batch, int32_t H,
+                     int32_t Wd, int32_t C_in, int32_t C_out, int32_t KH, int32_t KW,
+                     int32_t stride_h, int32_t stride_w, int32_t pad_h, int32_t pad_w,
+                     int64_t *Ho_out, int64_t *Wo_out)
+{
+    if (batch < 1 || H < 1 || Wd < 1 || C_in < 1 || C_out < 1 || KH < 1 || KW < 1 ||
+        stride_h < 1 || stride_w < 1 || pad_h < 0 || pad_w < 0)
+        return QG_ERR_INVALID;
+    if (C_in % 16 != 0 || C_out % 16 != 0)
+        return QG_ERR_INVALID;
+    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
+    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
+    if (span_h < 0 || span_w < 0)
+        return QG_ERR_INVALID;
+    const int64_t Ho = span_h / stride_h + 1, Wo = span_w / stride_w + 1;
+    // kernel indices are int32: pixels, K and element offsets must fit
+    const int64_t pixels = (int64_t)batch * Ho * Wo;
+    const int64_t K = (int64_t)KH * KW * C_in;
+    if (pixels > kMaxDim || K > kMaxDim || (int64_t)batch * H > kMaxDim ||
+        ((pixels + 63) / 64) * ((C_out + 63) / 64) >= kMaxGrid)
+        return QG_ERR_INVALID;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+        return QG_ERR_INVALID;
+    *Ho_out = Ho;
+    *Wo_out = Wo;
+    return QG_OK;
+}
+
+qg_status check_dwconv(const int8_t *X, const int8_t *W, const int8_t *Y, int32_t batch,
+                       int32_t H, int32_t Wd, int32_t C, int32_t KH, int32_t KW,
+                       int32_t stride_h, int32_t stride_w, int32_t pad_h, int32_t pad_w,
+                       int64_t *Ho_out, int64_t *Wo_out)
+{
+    if (batch < 1 || H < 1 || Wd < 1 || C < 1 || KH < 1 || KW < 1 || stride_h < 1 ||
+        stride_w < 1 || pad_h < 0 || pad_w < 0)
+        return QG_ERR_INVALID;
+    if (C % 16 != 0)
+        return QG_ERR_INVALID;
+    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
+    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
+    if (span_h < 0 || span_w < 0)
+        return QG_ERR_INVALID;
+    const int64_t Ho = span_h / stride_h + 1, Wo = span_w / stride_w + 1;
+    // kernel indices are int32 where they count pixels, rows or LDS bytes;
+    // element offsets are computed in 64 bits
+    const int64_t pixels = (int64_t)batch * Ho * Wo;
+    if (pixels > kMaxDim || (int64_t)batch * H * Wd > kMaxDim || C > 65536 ||
+        (int64_t)KH * KW * C > kMaxDim || (pixels * (C / 4) + 255) / 256 >= kMaxGrid)
+        return QG_ERR_INVALID;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+        return QG_ERR_INVALID;
+    *Ho_out = Ho;
+    *Wo_out = Wo;
+    return QG_OK;
+}
+
+bool zero_point_ok(int32_t z) { return z >= -128 && z <= 127; }
+
+// a workspace of at least `need` bytes, 16-byte aligned
+qg_status check_workspace(const void *ws, size_t bytes, int64_t need)
+{
+    if (!ws)
+        return QG_ERR_NULLPTR;
+    if ((int64_t)bytes < need || !aligned16(ws))
+        return QG_ERR_INVALID;
+    return QG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,25 +223,11 @@ qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_
 {
     if (!X || !W || !Y || !mult || !shift)
         return QG_ERR_NULLPTR;
-    if (batch < 1 || H < 1 || Wd < 1 || C_in < 1 || C_out < 1 || KH < 1 || KW < 1 ||
-        stride_h < 1 || stride_w < 1 || pad_h < 0 || pad_w < 0)
-        return QG_ERR_INVALID;
-    if (C_in % 16 != 0 || C_out % 16 != 0)
-        return QG_ERR_INVALID;
-    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
-    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
-    if (span_h < 0 || span_w < 0)
-        return QG_ERR_INVALID;
-    const int64_t Ho = span_h / stride_h + 1, Wo = span_w / stride_w + 1;
-    // kernel indices are int32: pixels, K and element offsets must fit
-    const int64_t pixels = (int64_t)batch * Ho * Wo;
-    const int64_t K = (int64_t)KH * KW * C_in;
-    if (pixels > kMaxDim || K > kMaxDim || (int64_t)batch * H > kMaxDim ||
-        ((pixels + 63) / 64) * ((C_out + 63) / 64) >= kMaxGrid)
-        return QG_ERR_INVALID;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
-        return QG_ERR_INVALID;
-    qg_status st = check_params(bias, mult, shift);
+    int64_t Ho = 0, Wo = 0;
+    qg_status st = check_conv(X, W, Y, batch, H, Wd, C_in, C_out, KH, KW, stride_h, stride_w,
+                              pad_h, pad_w, &Ho, &Wo);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
     int cus = 0;
@@ -192,25 +248,11 @@ qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int3
 {
     if (!X || !W || !Y || !mult || !shift)
         return QG_ERR_NULLPTR;
-    if (batch < 1 || H < 1 || Wd < 1 || C < 1 || KH < 1 || KW < 1 || stride_h < 1 ||
-        stride_w < 1 || pad_h < 0 || pad_w < 0)
-        return QG_ERR_INVALID;
-    if (C % 16 != 0)
-        return QG_ERR_INVALID;
-    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
-    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
-    if (span_h < 0 || span_w < 0)
-        return QG_ERR_INVALID;
-    const int64_t Ho = span_h / stride_h + 1, Wo = span_w / stride_w + 1;
-    // kernel indices are int32 where they count pixels, rows or LDS bytes;
-    // element offsets are computed in 64 bits
-    const int64_t pixels = (int64_t)batch * Ho * Wo;
-    if (pixels > kMaxDim || (int64_t)batch * H * Wd > kMaxDim || C > 65536 ||
-        (int64_t)KH * KW * C > kMaxDim || (pixels * (C / 4) + 255) / 256 >= kMaxGrid)
-        return QG_ERR_INVALID;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
-        return QG_ERR_INVALID;
-    qg_status st = check_params(bias, mult, shift);
+    int64_t Ho = 0, Wo = 0;
+    qg_status st = check_dwconv(X, W, Y, batch, H, Wd, C, KH, KW, stride_h, stride_w, pad_h,
+                                pad_w, &Ho, &Wo);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
     int cus = 0;
@@ -249,6 +291,127 @@ qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, i
         return st;
     qg::QuantDesc d{X, dtype, ldx, Q, ldq, scale, M, K, clip, bits};
     return launched(qg::launch_quant_per_token(d, (hipStream_t)stream));
+}
+
+// ---- asymmetric forms ----
+
+size_t qgemm_s8s8_requant_zp_workspace_size(int64_t M, int64_t N)
+{
+    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim)
+        return 0;
+    return (size_t)qg::zp_gemm_workspace_bytes(M, N);
+}
+
+qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                                const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                                int32_t a_zero, int32_t b_zero, int32_t out_zero, int8_t *C,
+                                int64_t ldc, int64_t M, int64_t N, int64_t K, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    if (!A || !B || !C || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    qg_status st = check_gemm(A, lda, false, B, ldb, false, C, ldc, 1, M, N, K, kMaxDim);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+        return QG_ERR_INVALID;
+    if ((st = check_workspace(workspace, workspace_bytes, qg::zp_gemm_workspace_bytes(M, N))) !=
+        QG_OK)
+        return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, cus, nullptr, out_zero};
+    return launched(qg::run_s8s8_requant_zp(d, a_zero, b_zero, workspace, (hipStream_t)stream));
+}
+
+size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32_t Wd,
+                                                 int32_t C_out, int32_t KH, int32_t KW,
+                                                 int32_t stride_h, int32_t stride_w,
+                                                 int32_t pad_h, int32_t pad_w)
+{
+    if (batch < 1 || H < 1 || Wd < 1 || C_out < 1 || KH < 1 || KW < 1 || stride_h < 1 ||
+        stride_w < 1 || pad_h < 0 || pad_w < 0)
+        return 0;
+    const int64_t span_h = (int64_t)H + 2 * (int64_t)pad_h - KH;
+    const int64_t span_w = (int64_t)Wd + 2 * (int64_t)pad_w - KW;
+    if (span_h < 0 || span_w < 0)
+        return 0;
+    const int64_t pixels = (int64_t)batch * (span_h / stride_h + 1) * (span_w / stride_w + 1);
+    if (pixels > kMaxDim)
+        return 0;
+    return (size_t)qg::zp_conv_workspace_bytes(C_out, pixels);
+}
+
+qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
+                                     const int32_t *mult, const int32_t *shift, int32_t a_zero,
+                                     int32_t b_zero, int32_t out_zero, int8_t *Y, int32_t batch,
+                                     int32_t H, int32_t Wd, int32_t C_in, int32_t C_out,
+                                     int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
+                                     int32_t pad_h, int32_t pad_w, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    if (!X || !W || !Y || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    int64_t Ho = 0, Wo = 0;
+    qg_status st = check_conv(X, W, Y, batch, H, Wd, C_in, C_out, KH, KW, stride_h, stride_w,
+                              pad_h, pad_w, &Ho, &Wo);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+        return QG_ERR_INVALID;
+    const int64_t pixels = (int64_t)batch * Ho * Wo;
+    if ((st = check_workspace(workspace, workspace_bytes,
+                              qg::zp_conv_workspace_bytes(C_out, pixels))) != QG_OK)
+        return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C_in, C_out, KH, KW,
+                   stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo,
+                   true, a_zero, b_zero, out_zero, nullptr};
+    return launched(qg::run_conv_zp(d, workspace, (hipStream_t)stream));
+}
+
+size_t qdwconv2d_nhwc_s8_requant_zp_workspace_size(int32_t C)
+{
+    if (C < 1)
+        return 0;
+    return (size_t)qg::zp_dw_workspace_bytes(C);
+}
+
+qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
+                                       const int32_t *mult, const int32_t *shift,
+                                       int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                       int8_t *Y, int32_t batch, int32_t H, int32_t Wd,
+                                       int32_t C, int32_t KH, int32_t KW, int32_t stride_h,
+                                       int32_t stride_w, int32_t pad_h, int32_t pad_w,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!X || !W || !Y || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    int64_t Ho = 0, Wo = 0;
+    qg_status st = check_dwconv(X, W, Y, batch, H, Wd, C, KH, KW, stride_h, stride_w, pad_h,
+                                pad_w, &Ho, &Wo);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+        return QG_ERR_INVALID;
+    if ((st = check_workspace(workspace, workspace_bytes, qg::zp_dw_workspace_bytes(C))) != QG_OK)
+        return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C, C, KH, KW,
+                   stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo,
+                   true, a_zero, b_zero, out_zero, nullptr};
+    return launched(qg::run_dwconv_zp(d, workspace, (hipStream_t)stream));
 }
 
 const char *qg_status_string(qg_status s)

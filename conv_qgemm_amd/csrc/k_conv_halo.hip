@@ -14,10 +14,11 @@
 // 64 output channels.
 //   * the input rows those pixels touch (with the KH-1 halo rows) are read
 //     once with 16-byte loads and written to LDS with every pixel in 80
-//     bytes (64 channels + 16 unused), row by row with zero columns of
-//     padding on both sides and zero rows above and below the image: a tap
-//     of an output pixel is then one fixed LDS offset away from its (0, 0)
-//     tap, with no bounds test, and zero padding costs nothing;
+//     bytes (64 channels + 16 unused), row by row with padding columns on
+//     both sides and padding rows above and below the image, filled with
+//     the input zero point (0 for symmetric inputs): a tap of an output pixel
+//     is then one fixed LDS offset away from its (0, 0) tap, with no bounds
+//     test, and the padding costs nothing;
 //   * 16 consecutive pixels at an 80-byte stride fall in 16 different LDS
 //     bank groups, so the operand reads are conflict free;
 //   * the workgroup's 64 weight rows (KH*KW*64 bytes each, OHWI) are copied
@@ -66,6 +67,9 @@ struct HaloArgs {
     int H, Wd, C_out, ph, pw, Ho, Wo;
     int tiles_per_img;
     int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+    int pad4;              // padding byte (the input zero point) x4
+    const int32_t *rterm;  // ZP: per-pixel term, or null
+    int out_zero;          // ZP: output zero point
 };
 
 __device__ __forceinline__ void drain_and_barrier()
@@ -73,7 +77,9 @@ __device__ __forceinline__ void drain_and_barrier()
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int KH, int KW>
+// ZP: the asymmetric form -- `bias` holds the per-channel term, rterm the
+// per-pixel one, and the output zero point joins before the saturation
+template <int KH, int KW, bool ZP>
 __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 {
     constexpr int KK = KH * KW;
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     }
 
     // ---- input rows: LDS row r holds input row ih0 + r, LDS column c holds
-    //      input column c - pw; zero outside the image ----
+    //      input column c - pw; the padding value outside the image ----
     const int colsL = p.Wd + 2 * p.pw;
     const int rowL = colsL * kPixL;
     const int nrow_in = oh_last - oh_first + KH;  // LDS rows this tile reads
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
                 const int ih = ih0 + r;
                 if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
                     v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
-                    z[0] = z[1] = z[2] = z[3] = (v4i){0, 0, 0, 0};
+                    z[0] = z[1] = z[2] = z[3] = (v4i){p.pad4, p.pad4, p.pad4, p.pad4};
                 }
             }
         }
@@ -174,10 +180,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 
     // ---- this lane's pixel in each of the wave's 4 M tiles, as the LDS
     //      offset of its (0, 0) tap; pixels past the tile reuse the last one ----
-    int abase[4];
+    int abase[4], rt[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = min(64 * wave + 16 * i + col, npix - 1);
+        if constexpr (ZP) {
+            if (p.rterm)
+                rt[i] = p.rterm[(int64_t)b * HW + p0 + q];
+        }
         const int pp = p0 + q;
         const int oh = pp / p.Wo;
         const int ow = pp - oh * p.Wo;
@@ -236,13 +246,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
                 int y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int x = acc[i][n][e];
+                    const int x = ZP ? wrap_sub(acc[i][n][e], rt[i]) : acc[i][n][e];
+                    const int zo = ZP ? p.out_zero : 0;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e]);
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo);
                     else if constexpr (TIER == 1)
-                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
+                                               zo);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo);
                 }
                 const int q = 64 * wave + 16 * i + col;
                 *(unsigned *)(IN + q * 64 + c0) = pack4_i8(y[0], y[1], y[2], y[3]);
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     }
 }
 
-template <int KH, int KW>
+template <int KH, int KW, bool ZP>
 hipError_t run_halo(const HaloArgs &a, int batch, int lds_bytes, hipStream_t s)
 {
     // the dynamic LDS limit above 64 KB is raised once per device
@@ -277,14 +289,14 @@ hipError_t run_halo(const HaloArgs &a, int batch, int lds_bytes, hipStream_t s)
     if (dev < 0 || dev >= kMaxDevices)
         return hipErrorInvalidDevice;
     if (!attr_set[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute((const void *)k_conv_halo<KH, KW>,
+        e = hipFuncSetAttribute((const void *)k_conv_halo<KH, KW, ZP>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         if (e != hipSuccess)
             return e;
         attr_set[dev].store(true, std::memory_order_release);
     }
     const dim3 grid(batch * a.tiles_per_img, a.C_out / kNT), block(kWaves * 64);
-    hipLaunchKernelGGL((k_conv_halo<KH, KW>), grid, block, lds_bytes, s, a);
+    hipLaunchKernelGGL((k_conv_halo<KH, KW, ZP>), grid, block, lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -340,10 +352,18 @@ hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s)
     a.Wo = d.Wo;
     a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
     a.in_bytes = (int)halo_in_bytes(d);
+    a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
+    a.rterm = d.rterm;
+    a.out_zero = d.out_zero;
     const int lds = (int)halo_lds_bytes(d);
+    if (d.asym) {
+        if (d.KH == 3)
+            return run_halo<3, 3, true>(a, d.batch, lds, s);
+        return run_halo<1, 1, true>(a, d.batch, lds, s);
+    }
     if (d.KH == 3)
-        return run_halo<3, 3>(a, d.batch, lds, s);
-    return run_halo<1, 1>(a, d.batch, lds, s);
+        return run_halo<3, 3, false>(a, d.batch, lds, s);
+    return run_halo<1, 1, false>(a, d.batch, lds, s);
 }
 
 }  // namespace qg

@@ -14,9 +14,10 @@
 // (4 waves): 256 consecutive output pixels of one image x a 64-channel
 // slice.
 //   * the input rows those pixels touch are staged once in LDS, every pixel
-//     in 80 bytes (the slice's 64 channels + 16 unused) with zero columns and
-//     rows for the padding, so a tap is a fixed LDS offset and 16
-//     consecutive pixels fall in 16 different bank groups;
+//     in 80 bytes (the slice's 64 channels + 16 unused) with columns and
+//     rows of the padding value (the input zero point, 0 when symmetric), so
+//     a tap is a fixed LDS offset and 16 consecutive pixels fall in 16
+//     different bank groups;
 //   * the diagonal weight operands live in registers (12 per lane);
 //   * the requantize takes the cheapest exact form all 64 shifts of the
 //     slice allow, and the tile leaves through LDS with 16-byte stores.
@@ -50,6 +51,9 @@ struct DwArgs {
     int H, Wd, C, KH, KW, sh, sw, ph, pw, Ho, Wo;
     int tiles_per_img;
     int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+    // asymmetric form: the padding byte x4 and the zero points; the 3x3 path
+    // takes zb = 0 with `bias` holding bias - za * sum_t w[t][c]
+    int pad4, a_zero, b_zero, out_zero;
 };
 
 __device__ __forceinline__ void drain_and_barrier()
@@ -58,7 +62,9 @@ __device__ __forceinline__ void drain_and_barrier()
 }
 
 // ---- 3x3 depthwise on the MFMA ----
-template <int S>  // stride (both directions)
+// S: stride (both directions); ZP: the asymmetric form (padding a_zero, the
+// output zero point before the saturation)
+template <int S, bool ZP>
 __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
 {
     constexpr int KH = 3, KW = 3, KK = 9, kSlices = 3;
@@ -115,7 +121,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
         }
     }
 
-    // ---- input rows (the slice's channels) -> LDS, zero outside the image ----
+    // ---- input rows (the slice's channels) -> LDS, the padding value
+    //      outside the image ----
     const int gpp = cs >> 4;  // 16-byte granules per pixel
     const int total = ih_lo <= ih_hi ? (ih_hi - ih_lo + 1) * p.Wd * gpp : 0;
     for (int base = 0; base == 0 || base < total; base += 8 * kWaves * 64) {
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
                 const int ih = ih0 + r;
                 if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
                     v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
-                    z[0] = z[1] = z[2] = z[3] = (v4i){0, 0, 0, 0};
+                    z[0] = z[1] = z[2] = z[3] = (v4i){p.pad4, p.pad4, p.pad4, p.pad4};
                 } else if (cs < kCS) {
                     // channels past the slice meet zero weights; keep them finite
                     for (int q = gpp; q < 4; ++q)
@@ -222,12 +229,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int x = acc[i][n][e];
+                    const int zo = ZP ? p.out_zero : 0;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e]);
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo);
                     else if constexpr (TIER == 1)
-                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
+                                               zo);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo);
                 }
                 const int q = 64 * wave + 16 * i + col;
                 *(unsigned *)(IN + q * 64 + cc) = pack4_i8(y[0], y[1], y[2], y[3]);
@@ -251,7 +260,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
     }
 }
 
-// ---- any kernel size and stride: one thread per output pixel x 4 channels ----
+// ---- any kernel size and stride: one thread per output pixel x 4 channels;
+//      the asymmetric form multiplies (x - za) * (w - zb) directly, so a
+//      padded tap (x = za) adds nothing and `bias` is the plain bias ----
 __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
 {
     const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -277,7 +288,8 @@ __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
             const unsigned wv = *(const unsigned *)(p.W + (int64_t)(kh * p.KW + kw) * p.C + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[e] += (int)(int8_t)(xv >> (8 * e)) * (int)(int8_t)(wv >> (8 * e));
+                acc[e] = wrap_add(acc[e], ((int)(int8_t)(xv >> (8 * e)) - p.a_zero) *
+                                              ((int)(int8_t)(wv >> (8 * e)) - p.b_zero));
         }
     }
     int y[4];
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
     for (int e = 0; e < 4; ++e) {
         const int s = p.shift[c + e];
         y[e] = requant_one(acc[e], p.bias ? p.bias[c + e] : 0, p.mult[c + e], s,
-                           1ll << ((s - 1) & 63));
+                           1ll << ((s - 1) & 63), p.out_zero);
     }
     *(unsigned *)(p.Y + pix * p.C + c) = pack4_i8(y[0], y[1], y[2], y[3]);
 }
@@ -316,7 +328,7 @@ bool dw_mfma_fits(const ConvDesc &d)
     return d.C_in % 16 == 0 && dw_lds_bytes(d) <= kMaxLds;
 }
 
-template <int S>
+template <int S, bool ZP>
 hipError_t run_dw3x3(const DwArgs &a, int batch, int lds_bytes, hipStream_t s)
 {
     static std::atomic<bool> attr_set[kMaxDevices];
@@ -327,19 +339,26 @@ hipError_t run_dw3x3(const DwArgs &a, int batch, int lds_bytes, hipStream_t s)
     if (dev < 0 || dev >= kMaxDevices)
         return hipErrorInvalidDevice;
     if (!attr_set[dev].load(std::memory_order_acquire)) {
-        e = hipFuncSetAttribute((const void *)k_dwconv3x3<S>,
+        e = hipFuncSetAttribute((const void *)k_dwconv3x3<S, ZP>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
         if (e != hipSuccess)
             return e;
         attr_set[dev].store(true, std::memory_order_release);
     }
     const dim3 grid(batch * a.tiles_per_img, (a.C + kCS - 1) / kCS), block(kWaves * 64);
-    hipLaunchKernelGGL((k_dwconv3x3<S>), grid, block, lds_bytes, s, a);
+    hipLaunchKernelGGL((k_dwconv3x3<S, ZP>), grid, block, lds_bytes, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
+bool dw_takes_mfma(const ConvDesc &d)
+{
+    return dw_mfma_fits(d) && (!d.asym || d.b_zero == 0);
+}
+
+// The asymmetric 3x3 path reads `bias` as bias - za * sum_t w[t][c]
+// (launch_zp_dw_terms); the direct path takes the plain bias.
 hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s)
 {
     DwArgs a{};
@@ -360,13 +379,21 @@ hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s)
     a.pw = d.pw;
     a.Ho = d.Ho;
     a.Wo = d.Wo;
-    if (dw_mfma_fits(d)) {
+    if (d.asym) {
+        a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
+        a.a_zero = d.a_zero;
+        a.b_zero = d.b_zero;
+        a.out_zero = d.out_zero;
+    }
+    if (dw_takes_mfma(d)) {
         a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
         a.in_bytes = (int)dw_in_bytes(d);
         const int lds = (int)dw_lds_bytes(d);
-        if (d.sh == 1)
-            return run_dw3x3<1>(a, d.batch, lds, s);
-        return run_dw3x3<2>(a, d.batch, lds, s);
+        if (d.asym)
+            return d.sh == 1 ? run_dw3x3<1, true>(a, d.batch, lds, s)
+                             : run_dw3x3<2, true>(a, d.batch, lds, s);
+        return d.sh == 1 ? run_dw3x3<1, false>(a, d.batch, lds, s)
+                         : run_dw3x3<2, false>(a, d.batch, lds, s);
     }
     const int64_t nitems = (int64_t)d.batch * d.Ho * d.Wo * (d.C_in / 4);
     const int64_t blocks = (nitems + 255) / 256;

@@ -59,7 +59,12 @@ constexpr int kGroupM = 4;
 constexpr int kOutStride = kBN + 16;          // LDS row stride of the int8 output tile
 
 enum { OP_S8 = 8, OP_S4 = 4 };
-enum { EPI_REQUANT = 0, EPI_I32 = 1 };
+// EPI_REQUANT_ZP: the asymmetric form.  `bias` then holds the per-column
+// term bias - za * sum_k B + K * za * zb, `rterm` the per-row zb * sum_k A
+// (or null when zb = 0), and the output zero point is added before the int8
+// saturation; all of it modulo 2^32, which gives the true value whenever
+// sum (A - za)(B - zb) + bias fits in int32.
+enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2 };
 
 struct DmaArgs {
     const uint8_t *A;
@@ -73,6 +78,8 @@ struct DmaArgs {
     int64_t ldc;
     int M, N, K;
     int tiles_m, tiles_n;
+    const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
+    int out_zero;          // EPI_REQUANT_ZP: output zero point
 };
 
 // A 16-byte LDS read is served 16 lanes per cycle over 64 4-byte banks; the
@@ -99,12 +106,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     constexpr int STEPS_PER_READ = KIND == OP_S8 ? 1 : 2;
     constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : 0;
     constexpr int MG = 16 * STEPS_PER_READ;  // MFMAs per read group
+    constexpr bool RQ = EPI != EPI_I32;
+    constexpr bool ZP = EPI == EPI_REQUANT_ZP;
 
     // one LDS object: the operand ring, then the per-column bias / multiplier
-    // / shift of this tile's 256 output columns (a second __shared__ object
-    // makes the compiler wait for every direct-to-LDS load before any read)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage + 3 * kBN * 4];
+    // / shift of this tile's 256 output columns and the per-row term of its
+    // 256 rows (a second __shared__ object makes the compiler wait for every
+    // direct-to-LDS load before any read)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage + 4 * kBN * 4];
     int(*prm)[kBN] = (int(*)[kBN])(lds + kStages * kStage);
+    static_assert(kBM == kBN, "the row terms share the column-parameter layout");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -124,12 +135,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     // requantize parameters of column n0 + tid, fetched now and parked in LDS
     // (the barrier of the prologue publishes them) so the epilogue reads
     // them without global-memory latency
-    int pb = 0, pm = 0, ps = 0;
-    if constexpr (EPI == EPI_REQUANT) {
+    int pb = 0, pm = 0, ps = 0, pr = 0;
+    if constexpr (RQ) {
         const int n = min(n0 + tid, p.N - 1);
         pb = p.bias ? p.bias[n] : 0;
         pm = p.mult[n];
         ps = p.shift[n];
+    }
+    if constexpr (ZP) {
+        if (p.rterm)
+            pr = p.rterm[min(m0 + tid, p.M - 1)];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -227,11 +242,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 #pragma unroll
     for (int l = 0; l < kEarlyLoads; ++l)
         issue(kStages - 1, l);
-    if constexpr (EPI == EPI_REQUANT) {
+    if constexpr (RQ) {
         prm[0][tid] = pb;
         prm[1][tid] = pm;
         prm[2][tid] = ps;
     }
+    if constexpr (ZP)
+        prm[3][tid] = pr;
     wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage + kEarlyLoads>();
     read_group(0, 0, fa[0], fb[0]);
 
@@ -288,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     //      nl = wn*128 + j*32 + q*8 + (lane/32)*4 + e of the tile in
     //      accumulator registers 4q + e of sub-tile (j, i) ----
     const int khalf = lane >> 5;
-    if constexpr (EPI == EPI_REQUANT) {
+    if constexpr (RQ) {
         // requantize into an LDS copy of the 256 x 256 int8 tile, with the
         // cheapest exact form that every shift of the tile allows (chosen
         // once, so the accumulator indices stay compile-time constants)
@@ -312,18 +329,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int ml = wm * 128 + i * 32 + (lane & 31);
+                        const int rt = ZP ? prm[3][ml] : 0;
+                        const int zo = ZP ? p.out_zero : 0;
                         int y[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int a = acc[j * 4 + i][4 * q + e] >> ACC_SHIFT;
+                            int a = acc[j * 4 + i][4 * q + e] >> ACC_SHIFT;
+                            if constexpr (ZP)
+                                a = wrap_sub(a, rt);
                             if constexpr (TIER == 2)
-                                y[e] = requant_one_s33(a, b4[e], m4[e], s4[e]);
+                                y[e] = requant_one_s33(a, b4[e], m4[e], s4[e], zo);
                             else if constexpr (TIER == 1)
                                 y[e] = requant_one_s31(a, b4[e], m4[e], s4[e],
-                                                       1ll << ((s4[e] - 1) & 63));
+                                                       1ll << ((s4[e] - 1) & 63), zo);
                             else
                                 y[e] = requant_one(a, b4[e], m4[e], s4[e],
-                                                   1ll << ((s4[e] - 1) & 63));
+                                                   1ll << ((s4[e] - 1) & 63), zo);
                         }
                         *(unsigned *)(otile + ml * kOutStride + nl) =
                             pack4_i8(y[0], y[1], y[2], y[3]);
@@ -408,6 +429,8 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     a.K = (int)d.K;
     a.tiles_m = (int)((d.M + kBM - 1) / kBM);
     a.tiles_n = (int)((d.N + kBN - 1) / kBN);
+    a.rterm = d.rterm;
+    a.out_zero = d.out_zero;
     hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -435,6 +458,11 @@ hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s)
 hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s)
 {
     return run<OP_S4, EPI_I32>(d, s);
+}
+
+hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s)
+{
+    return run<OP_S8, EPI_REQUANT_ZP>(d, s);
 }
 
 }  // namespace qg

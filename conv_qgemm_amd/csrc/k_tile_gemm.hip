@@ -32,7 +32,11 @@
 namespace qg {
 
 enum { OP_S8 = 8, OP_S4 = 4 };
-enum { EPI_REQUANT = 0, EPI_I32 = 1 };
+// EPI_REQUANT_ZP is the asymmetric form: `bias` holds the per-column term
+// (bias - za * sum_k B + K * za * zb), `rterm` the per-row zb * sum_k A (null
+// when zb = 0), and the output zero point joins before the saturation; the
+// sums wrap modulo 2^32 and give the true value whenever it fits in int32.
+enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2 };
 enum { AL_DENSE = 0, AL_CONV = 1 };
 
 struct TileArgs {
@@ -49,6 +53,9 @@ struct TileArgs {
     int tiles_m, tiles_n;
     // implicit-im2col geometry (AL_CONV only)
     int H, W, C_in, KW, Ho, Wo, sh, sw, ph, pw;
+    int pad4;              // AL_CONV: padding byte (the input zero point) x4
+    const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
+    int out_zero;          // EPI_REQUANT_ZP: output zero point
 };
 
 constexpr int kThreads = 256;
@@ -128,6 +135,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
 
     v4i ra[CA], rb[CB];
     const v4i zero4 = {0, 0, 0, 0};
+    const v4i pad4 = {p.pad4, p.pad4, p.pad4, p.pad4};
 
     auto load_tile = [&](int kt) {
         const int kbA = kt * RBA + ca * 16;
@@ -142,10 +150,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
             const int kw = tap - kh * p.KW;
             for (int i = 0; i < CA; ++i) {
                 const int ih = cv_ih[i] + kh, iw = cv_iw[i] + kw;
-                const bool ok = kbA < KbA && (unsigned)ih < (unsigned)p.H &&
-                                (unsigned)iw < (unsigned)p.W;
+                const bool inside = (unsigned)ih < (unsigned)p.H && (unsigned)iw < (unsigned)p.W;
                 const int64_t off = ((a_off[i] + ih) * p.W + iw) * p.C_in + ci;
-                ra[i] = ok ? *(const v4i *)(p.A + off) : zero4;  // padding reads 0
+                // spatial padding holds the input zero point; K past the
+                // filter meets zero weights, so its value does not matter
+                ra[i] = kbA < KbA && inside ? *(const v4i *)(p.A + off) : pad4;
             }
         }
         const int kbB = kt * RBB + cb * 16;
@@ -238,7 +247,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
             const bool full = n + 3 < p.N;
             // 4 results per store when the row stride keeps them aligned
             const bool vec = full && (p.ldc & 3) == 0;
-            if constexpr (EPI == EPI_REQUANT) {
+            if constexpr (EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP) {
+                constexpr bool ZP = EPI == EPI_REQUANT_ZP;
                 int bia[4], mul[4], shf[4];
                 long long rnd[4];
                 if (full) {
@@ -265,9 +275,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
                 for (int i = 0; i < TM; ++i) {
                     const int m = m0 + wm * WTM + i * 32 + (lane & 31);
                     const v16i &a = acc[j * TM + i];
+                    const int rt = ZP && p.rterm ? p.rterm[min(m, p.M - 1)] : 0;
+                    const int zo = ZP ? p.out_zero : 0;
                     int y[4];
                     for (int e = 0; e < 4; ++e)
-                        y[e] = requant_one(a[4 * q + e] >> ACC_SHIFT, bia[e], mul[e], shf[e], rnd[e]);
+                        y[e] = requant_one(wrap_sub(a[4 * q + e] >> ACC_SHIFT, rt), bia[e], mul[e],
+                                           shf[e], rnd[e], zo);
                     if (m < p.M) {
                         int8_t *dst = C + (int64_t)m * p.ldc + n;
                         if (vec) {
@@ -333,6 +346,8 @@ static TileArgs gemm_args(const GemmDesc &d)
     a.M = (int)d.M;
     a.N = (int)d.N;
     a.K = (int)d.K;
+    a.rterm = d.rterm;
+    a.out_zero = d.out_zero;
     return a;
 }
 
@@ -382,6 +397,13 @@ hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s)
     return run_gemm<OP_S8, OP_S4, EPI_REQUANT, 128>(d, s);
 }
 
+hipError_t launch_s8s8_requant_zp(const GemmDesc &d, hipStream_t s)
+{
+    if (dma_gemm_fits(d, false))
+        return launch_s8s8_requant_zp_dma(d, s);
+    return run_gemm<OP_S8, OP_S8, EPI_REQUANT_ZP, 128>(d, s);
+}
+
 hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s)
 {
     TileArgs a{};
@@ -407,6 +429,14 @@ hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s)
     a.sw = d.sw;
     a.ph = d.ph;
     a.pw = d.pw;
+    a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
+    a.rterm = d.rterm;
+    a.out_zero = d.out_zero;
+    if (d.asym) {
+        if (d.C_out <= 64)
+            return run_tile<OP_S8, OP_S8, EPI_REQUANT_ZP, AL_CONV, 256, 64, 64, 4, 1>(a, s);
+        return run_tile<OP_S8, OP_S8, EPI_REQUANT_ZP, AL_CONV, 128, 128, 64, 2, 2>(a, s);
+    }
     if (d.C_out <= 64)
         return run_tile<OP_S8, OP_S8, EPI_REQUANT, AL_CONV, 256, 64, 64, 4, 1>(a, s);
     return run_tile<OP_S8, OP_S8, EPI_REQUANT, AL_CONV, 128, 128, 64, 2, 2>(a, s);

@@ -21,6 +21,10 @@ struct GemmDesc {
     int64_t ldc;
     int64_t M, N, K;  // K in values
     int cus;          // compute units of the current device
+    // asymmetric form (launch_s8s8_requant_zp): `bias` is the per-column
+    // term, rterm the per-row term (or null), out_zero the output zero point
+    const int32_t *rterm;
+    int out_zero;
 };
 
 // One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,
@@ -33,6 +37,12 @@ struct ConvDesc {
     const int32_t *shift;
     int8_t *Y;
     int batch, H, Wd, C_in, C_out, KH, KW, sh, sw, ph, pw, Ho, Wo;
+    // asymmetric form: padding holds a_zero, `bias` is the per-channel term,
+    // rterm the per-pixel term (or null), out_zero the output zero point;
+    // b_zero is used only by the direct depthwise kernel
+    bool asym;
+    int a_zero, b_zero, out_zero;
+    const int32_t *rterm;
 };
 
 hipError_t launch_s8s8_requant(const GemmDesc &d, hipStream_t s);
@@ -45,13 +55,45 @@ hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s);
 bool dma_gemm_fits(const GemmDesc &d, bool int4);
 hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
+hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s);
+
+// asymmetric int8 GEMM: the terms come from launch_zp_gemm_terms
+hipError_t launch_s8s8_requant_zp(const GemmDesc &d, hipStream_t s);
+
+// Compensation terms of the asymmetric forms (k_zp.hip), modulo 2^32:
+//   cterm[n] = bias[n] - za * sum_k B[n][k] + K * za * zb   (n < N)
+//   rterm[m] = zb * sum_k A[m][k]                           (m < M; only
+//              when rterm is not null)
+// B and A are int8 [rows][ld] with K % 16 == 0 and 16-byte rows.
+hipError_t launch_zp_gemm_terms(const int8_t *A, int64_t lda_b, const int8_t *B, int64_t ldb_b,
+                                const int32_t *bias, int64_t M, int64_t N, int64_t K, int za,
+                                int zb, int32_t *cterm, int32_t *rterm, hipStream_t s);
+// Per-pixel term of the asymmetric conv: rterm[p] = zb * (sum over the taps
+// and input channels of output pixel p, padding counted as za).
+hipError_t launch_zp_conv_rowterm(const ConvDesc &d, int32_t *rterm, hipStream_t s);
+// Per-channel term of the asymmetric depthwise conv with zb = 0:
+// cterm[c] = bias[c] - za * sum over taps of W[t][c].
+hipError_t launch_zp_dw_terms(const ConvDesc &d, int32_t *cterm, hipStream_t s);
+
+// The asymmetric entry points' sequences (k_zp.hip): the terms into the
+// workspace, then the GEMM / conv kernel.  Workspace bytes: cterm, then
+// rterm, each rounded up to 256 bytes.
+int64_t zp_gemm_workspace_bytes(int64_t M, int64_t N);
+int64_t zp_conv_workspace_bytes(int64_t C_out, int64_t pixels);
+int64_t zp_dw_workspace_bytes(int64_t C);
+hipError_t run_s8s8_requant_zp(GemmDesc d, int za, int zb, void *ws, hipStream_t s);
+hipError_t run_conv_zp(ConvDesc d, void *ws, hipStream_t s);
+hipError_t run_dwconv_zp(ConvDesc d, void *ws, hipStream_t s);
 
 // NHWC conv with stride 1 and 64 input channels, input rows staged in LDS
 // (k_conv_halo.hip); other convs use the implicit-im2col tile kernel
 bool conv_halo_fits(const ConvDesc &d);
 hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s);
 
-// depthwise NHWC conv (k_dwconv.hip); C_in == C_out == the channel count
+// depthwise NHWC conv (k_dwconv.hip); C_in == C_out == the channel count.
+// dw_takes_mfma: the 3x3 matrix-core path runs (its asymmetric form needs
+// the per-channel term in `bias`); otherwise the direct kernel runs.
+bool dw_takes_mfma(const ConvDesc &d);
 hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s);
 
 // Per-token activation quantizer (k_quant.hip).  dtype 0 binary32, 1

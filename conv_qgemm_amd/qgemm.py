@@ -59,6 +59,22 @@ def _load():
     lib.qdwconv2d_nhwc_s8_requant.restype = S
     lib.qquant_per_token.argtypes = [P, I32, I64, P, I64, P, I64, I64, ctypes.c_float, I32, P]
     lib.qquant_per_token.restype = S
+    Z = ctypes.c_size_t
+    lib.qgemm_s8s8_requant_zp_workspace_size.argtypes = [I64, I64]
+    lib.qgemm_s8s8_requant_zp_workspace_size.restype = Z
+    lib.qgemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, P, I64, I64,
+                                          I64, I64, P, Z, P]
+    lib.qgemm_s8s8_requant_zp.restype = S
+    lib.qconv2d_nhwc_s8_requant_zp_workspace_size.argtypes = [I32] * 10
+    lib.qconv2d_nhwc_s8_requant_zp_workspace_size.restype = Z
+    lib.qconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + [I32] * 11 + \
+        [P, Z, P]
+    lib.qconv2d_nhwc_s8_requant_zp.restype = S
+    lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size.argtypes = [I32]
+    lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size.restype = Z
+    lib.qdwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+        [I32] * 10 + [P, Z, P]
+    lib.qdwconv2d_nhwc_s8_requant_zp.restype = S
     lib.qg_status_string.argtypes = [S]
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
@@ -69,6 +85,9 @@ def _load():
 lib = _load()
 EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
            "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qquant_per_token",
+           "qgemm_s8s8_requant_zp_workspace_size", "qgemm_s8s8_requant_zp",
+           "qconv2d_nhwc_s8_requant_zp_workspace_size", "qconv2d_nhwc_s8_requant_zp",
+           "qdwconv2d_nhwc_s8_requant_zp_workspace_size", "qdwconv2d_nhwc_s8_requant_zp",
            "qg_status_string", "qg_version")
 
 
@@ -290,3 +309,108 @@ def qquant_per_token(X, bits=8, clip_ratio=1.0, Q=None, scale=None, stream=None)
                               _ptr(scale), M, K, float(clip_ratio), bits, _stream(stream))
     _check(st, "qquant_per_token")
     return Q, scale
+
+
+# ---- asymmetric (zero-point) forms ----
+
+def _workspace(ws, need, device):
+    """The caller's workspace (a uint8 GPU tensor of at least `need` bytes),
+    or a new one."""
+    if need == 0:
+        raise ValueError("the library rejects this shape")
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.numel() < need:
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of >= {need} bytes")
+    _on_device(ws, "workspace")
+    return ws
+
+
+def qgemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, C=None,
+                          workspace=None, stream=None):
+    """Asymmetric int8 GEMM: C = requant(sum_k (A - a_zero)(B - b_zero)) +
+    out_zero, saturated to int8.  A int8 [M, K], B int8 [N, K]."""
+    _mat(A, torch.int8, "A")
+    _mat(B, torch.int8, "B")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.int8, device=A.device)
+    _mat(C, torch.int8, "C")
+    ws = _workspace(workspace, int(lib.qgemm_s8s8_requant_zp_workspace_size(M, N)), A.device)
+    st = lib.qgemm_s8s8_requant_zp(_ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                   _ptr(_vec(bias, N, "bias")), _ptr(_vec(mult, N, "mult")),
+                                   _ptr(_vec(shift, N, "shift")), int(a_zero), int(b_zero),
+                                   int(out_zero), _ptr(C), C.stride(0), M, N, K, _ptr(ws),
+                                   ws.numel(), _stream(stream))
+    _check(st, "qgemm_s8s8_requant_zp")
+    return C
+
+
+def qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero, stride=(1, 1),
+                               pad=(1, 1), Y=None, workspace=None, stream=None):
+    """Asymmetric NHWC int8 conv: padding holds a_zero, products are
+    (X - a_zero)(W - b_zero), the output gets out_zero before the int8
+    saturation.  X [batch, H, W, C_in], W [C_out, KH, KW, C_in]."""
+    if X.dtype != torch.int8 or W.dtype != torch.int8:
+        raise TypeError("X and W must be int8")
+    if X.dim() != 4 or W.dim() != 4 or not X.is_contiguous() or not W.is_contiguous():
+        raise ValueError("X [B,H,W,C_in] and W [C_out,KH,KW,C_in] must be contiguous 4-D")
+    _on_device(X, "X")
+    _on_device(W, "W")
+    batch, H, Wd, C_in = X.shape
+    C_out, KH, KW, C_in2 = W.shape
+    if C_in2 != C_in:
+        raise ValueError("X and W disagree on C_in")
+    Ho, Wo = conv_out_hw(H, Wd, KH, KW, stride, pad)
+    if Y is None:
+        Y = torch.empty((batch, max(Ho, 0), max(Wo, 0), C_out), dtype=torch.int8,
+                        device=X.device)
+    if not Y.is_contiguous() or Y.dtype != torch.int8 or tuple(Y.shape) != (batch, Ho, Wo, C_out):
+        raise ValueError("Y must be a contiguous int8 [batch, H_out, W_out, C_out] tensor")
+    _on_device(Y, "Y")
+    need = int(lib.qconv2d_nhwc_s8_requant_zp_workspace_size(batch, H, Wd, C_out, KH, KW,
+                                                             stride[0], stride[1], pad[0],
+                                                             pad[1]))
+    ws = _workspace(workspace, need, X.device)
+    st = lib.qconv2d_nhwc_s8_requant_zp(_ptr(X), _ptr(W), _ptr(_vec(bias, C_out, "bias")),
+                                        _ptr(_vec(mult, C_out, "mult")),
+                                        _ptr(_vec(shift, C_out, "shift")), int(a_zero),
+                                        int(b_zero), int(out_zero), _ptr(Y), batch, H, Wd, C_in,
+                                        C_out, KH, KW, stride[0], stride[1], pad[0], pad[1],
+                                        _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "qconv2d_nhwc_s8_requant_zp")
+    return Y
+
+
+def qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero,
+                                 stride=(1, 1), pad=(1, 1), Y=None, workspace=None, stream=None):
+    """Asymmetric depthwise NHWC int8 conv (W [KH, KW, C]); zero points as
+    for qconv2d_nhwc_s8_requant_zp."""
+    if X.dtype != torch.int8 or W.dtype != torch.int8:
+        raise TypeError("X and W must be int8")
+    if X.dim() != 4 or W.dim() != 3 or not X.is_contiguous() or not W.is_contiguous():
+        raise ValueError("X [B,H,W,C] and W [KH,KW,C] must be contiguous")
+    _on_device(X, "X")
+    _on_device(W, "W")
+    batch, H, Wd, C = X.shape
+    KH, KW, C2 = W.shape
+    if C2 != C:
+        raise ValueError("X and W disagree on C")
+    Ho, Wo = conv_out_hw(H, Wd, KH, KW, stride, pad)
+    if Y is None:
+        Y = torch.empty((batch, max(Ho, 0), max(Wo, 0), C), dtype=torch.int8, device=X.device)
+    if not Y.is_contiguous() or Y.dtype != torch.int8 or tuple(Y.shape) != (batch, Ho, Wo, C):
+        raise ValueError("Y must be a contiguous int8 [batch, H_out, W_out, C] tensor")
+    _on_device(Y, "Y")
+    ws = _workspace(workspace, int(lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size(C)), X.device)
+    st = lib.qdwconv2d_nhwc_s8_requant_zp(_ptr(X), _ptr(W), _ptr(_vec(bias, C, "bias")),
+                                          _ptr(_vec(mult, C, "mult")),
+                                          _ptr(_vec(shift, C, "shift")), int(a_zero),
+                                          int(b_zero), int(out_zero), _ptr(Y), batch, H, Wd, C,
+                                          KH, KW, stride[0], stride[1], pad[0], pad[1],
+                                          _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "qdwconv2d_nhwc_s8_requant_zp")
+    return Y

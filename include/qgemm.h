@@ -55,6 +55,7 @@
 #ifndef QGEMM_H
 #define QGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -189,6 +190,59 @@ qg_status qdwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W,
 qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, int64_t ldq,
                            float *scale, int64_t M, int64_t K, float clip, int32_t bits,
                            void *stream);
+
+/*
+ * Asymmetric (zero-point) forms.  A code Q stands for (Q - zero_point) *
+ * scale (Voyager quantization article, www.dpshk.com/news/2695434, §1.1), so
+ * with per-tensor zero points a_zero (activations), b_zero (weights) and
+ * out_zero (output), all in [-128, 127]:
+ *   acc = sum_k (A[m][k] - a_zero) * (B[n][k] - b_zero)        (GEMM)
+ *   acc = sum over taps and input channels of (X - a_zero) * (W - b_zero),
+ *         positions outside the image holding a_zero             (convs)
+ *   out = clamp(((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero
+ *         saturated to int8 (the add before the saturation)
+ * (INT4 GEMM article §4.1 for zero points on both operands; MCU conv
+ * front-end article §2.3 for padding with the input zero point and §3.3 for
+ * the output zero point.)  Layouts, strides, alignment and the other
+ * requirements are those of the symmetric call of the same name.
+ * Precondition: acc + bias fits in int32.
+ *
+ * Each call takes a caller-owned device workspace of at least the bytes its
+ * *_workspace_size function returns for the same shape (16-byte aligned);
+ * the library writes per-row / per-column compensation sums there on the
+ * call's stream, ahead of the main kernel, and keeps nothing between calls.
+ * Calls that share a workspace must be ordered (one stream).  The size
+ * functions return 0 for shapes the call rejects.  Errors as above;
+ * QG_ERR_NULLPTR for a NULL workspace, QG_ERR_INVALID for a zero point out
+ * of range or a workspace that is too small or misaligned.
+ */
+size_t qgemm_s8s8_requant_zp_workspace_size(int64_t M, int64_t N);
+qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                                const int32_t *bias, const int32_t *mult, const int32_t *shift,
+                                int32_t a_zero, int32_t b_zero, int32_t out_zero, int8_t *C,
+                                int64_t ldc, int64_t M, int64_t N, int64_t K, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32_t Wd,
+                                                 int32_t C_out, int32_t KH, int32_t KW,
+                                                 int32_t stride_h, int32_t stride_w,
+                                                 int32_t pad_h, int32_t pad_w);
+qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
+                                     const int32_t *mult, const int32_t *shift, int32_t a_zero,
+                                     int32_t b_zero, int32_t out_zero, int8_t *Y, int32_t batch,
+                                     int32_t H, int32_t Wd, int32_t C_in, int32_t C_out,
+                                     int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
+                                     int32_t pad_h, int32_t pad_w, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+size_t qdwconv2d_nhwc_s8_requant_zp_workspace_size(int32_t C);
+qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
+                                       const int32_t *mult, const int32_t *shift,
+                                       int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                       int8_t *Y, int32_t batch, int32_t H, int32_t Wd,
+                                       int32_t C, int32_t KH, int32_t KW, int32_t stride_h,
+                                       int32_t stride_w, int32_t pad_h, int32_t pad_w,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *qg_status_string(qg_status s);

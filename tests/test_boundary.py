@@ -88,6 +88,28 @@ def qt(qg, X=P, dtype=0, ldx=64, Q=P, ldq=64, scale=P, M=8, K=64, clip=1.0, bits
     return qg.lib.qquant_per_token(X, dtype, ldx, Q, ldq, scale, M, K, clip, bits, None)
 
 
+WS = 0x20000  # fake workspace address
+
+
+def s8z(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, C=P, ldc=64,
+        M=32, N=64, K=64, ws=WS, wsb=1 << 20):
+    return qg.lib.qgemm_s8s8_requant_zp(A, lda, B, ldb, bias, mult, shift, za, zb, zo, C, ldc, M,
+                                        N, K, ws, wsb, None)
+
+
+def cvz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, Y=P, batch=1, H=8, Wd=8,
+        C_in=16, C_out=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
+    return qg.lib.qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, Y, batch, H,
+                                             Wd, C_in, C_out, KH, KW, sh, sw, ph, pw, ws, wsb,
+                                             None)
+
+
+def dwz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, Y=P, batch=1, H=8, Wd=8,
+        C=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
+    return qg.lib.qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, Y, batch, H,
+                                               Wd, C, KH, KW, sh, sw, ph, pw, ws, wsb, None)
+
+
 def test_nullptr(qg):
     E = qg.QG_ERR_NULLPTR
     for kw in ("A", "B", "C", "mult", "shift"):
@@ -100,6 +122,11 @@ def test_nullptr(qg):
         assert dw(qg, **{kw: NULL}) == E, kw
     for kw in ("X", "Q", "scale"):
         assert qt(qg, **{kw: NULL}) == E, kw
+    for kw in ("A", "B", "C", "mult", "shift", "ws"):
+        assert s8z(qg, **{kw: NULL}) == E, kw
+    for kw in ("X", "W", "Y", "mult", "shift", "ws"):
+        assert cvz(qg, **{kw: NULL}) == E, kw
+        assert dwz(qg, **{kw: NULL}) == E, kw
 
 
 def test_invalid_gemm_sizes(qg):
@@ -189,6 +216,33 @@ def test_invalid_quant(qg):
     assert qt(qg, scale=P + 2) == E
 
 
+def test_invalid_zero_point_forms(qg):
+    E = qg.QG_ERR_INVALID
+    for f in (s8z, cvz, dwz):
+        for kw in ("za", "zb", "zo"):
+            assert f(qg, **{kw: 128}) == E, (f.__name__, kw)
+            assert f(qg, **{kw: -129}) == E, (f.__name__, kw)
+        assert f(qg, ws=WS + 8) == E             # misaligned workspace
+    # workspace smaller than the size function asks for
+    need = qg.lib.qgemm_s8s8_requant_zp_workspace_size(32, 64)
+    assert need == 256 + 256
+    assert s8z(qg, wsb=need - 1) == E
+    need = qg.lib.qconv2d_nhwc_s8_requant_zp_workspace_size(1, 8, 8, 16, 3, 3, 1, 1, 1, 1)
+    assert need == 256 + 256                    # 16 channels, 64 pixels
+    assert cvz(qg, wsb=need - 4) == E
+    need = qg.lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size(16)
+    assert need == 256
+    assert dwz(qg, wsb=need - 1) == E
+    # the symmetric calls' own rules still apply
+    assert s8z(qg, K=40) == E
+    assert cvz(qg, C_in=24) == E
+    assert dwz(qg, C=24) == E
+    # size functions reject what the calls reject
+    assert qg.lib.qgemm_s8s8_requant_zp_workspace_size(0, 5) == 0
+    assert qg.lib.qconv2d_nhwc_s8_requant_zp_workspace_size(1, 2, 8, 16, 5, 3, 1, 1, 1, 1) == 0
+    assert qg.lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size(0) == 0
+
+
 def test_valid_call_without_gpu_reports_no_device(qg):
     import torch
     if torch.cuda.is_available():
@@ -199,6 +253,10 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert cv(qg) == qg.QG_ERR_NO_DEVICE
     assert dw(qg) == qg.QG_ERR_NO_DEVICE
     assert qt(qg) == qg.QG_ERR_NO_DEVICE
+    assert s8z(qg) == qg.QG_ERR_NO_DEVICE
+    assert cvz(qg) == qg.QG_ERR_NO_DEVICE
+    assert dwz(qg) == qg.QG_ERR_NO_DEVICE
+    assert s8z(qg, za=-128, zb=127, zo=-128, wsb=512) == qg.QG_ERR_NO_DEVICE
     assert qt(qg, dtype=2, bits=4, ldx=72, ldq=80, scale=P + 4, clip=0.25) == qg.QG_ERR_NO_DEVICE
 
 

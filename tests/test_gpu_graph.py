@@ -141,6 +141,43 @@ def test_graph_dwconv(qg, KH):
         pad=(KH // 2, KH // 2), Y=d["out"]))
 
 
+@pytest.mark.parametrize("M", [70, 4096])
+def test_graph_gemm_zp(qg, M):
+    """The compensation-term pass and the GEMM, both captured; the workspace
+    is part of the graph's inputs.  M 4096 takes the ring kernel."""
+    import torch
+
+    def make(seed):
+        h = datagen.gemm_s8s8(M, 2048 if M > 70 else 96, 256, seed, shift=(40, 46))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        n = d["B"].shape[0]
+        d["out"] = torch.empty((M, n), dtype=torch.int8, device="cuda")
+        d["ws"] = torch.empty(qg.lib.qgemm_s8s8_requant_zp_workspace_size(M, n),
+                              dtype=torch.uint8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_s8s8_requant_zp(
+        d["A"], d["B"], d["bias"], d["mult"], d["shift"], -9, 4, 7, C=d["out"],
+        workspace=d["ws"]))
+
+
+@pytest.mark.parametrize("C_in", [64, 32])
+def test_graph_conv_zp(qg, C_in):
+    import torch
+
+    def make(seed):
+        h = datagen.conv_nhwc(2, 9, 11, C_in, 64, 3, 3, seed, shift=(36, 42))
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((2, 9, 11, 64), dtype=torch.int8, device="cuda")
+        d["ws"] = torch.empty(qg.lib.qconv2d_nhwc_s8_requant_zp_workspace_size(
+            2, 9, 11, 64, 3, 3, 1, 1, 1, 1), dtype=torch.uint8, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qconv2d_nhwc_s8_requant_zp(
+        d["X"], d["W"], d["bias"], d["mult"], d["shift"], 13, -2, -5, Y=d["out"],
+        workspace=d["ws"]))
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 def test_graph_quant(qg, bits):
     import torch
