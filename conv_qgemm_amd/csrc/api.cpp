@@ -215,6 +215,27 @@ qg_status qgemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int
     return launched(qg::launch_w4a8_tiled(d, (hipStream_t)stream));
 }
 
+qg_status qgemm_w4a8_requant_msb(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                 const int32_t *bias, const int32_t *mult,
+                                 const int32_t *shift, int8_t *C, int64_t ldc, int64_t M,
+                                 int64_t N, int64_t K, void *stream)
+{
+    if (!A || !B || !C || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    qg_status st = check_gemm(A, lda, false, B, ldb, true, C, ldc, 1, M, N, K, QG_W4A8_MAX_K);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::GemmDesc d{A, lda, B, ldb / 2, bias, mult, shift, C, ldc, M, N, K, cus, nullptr, 0, true};
+    if (M <= qg::kSkinnyMaxM)
+        return launched(qg::launch_w4a8_skinny(d, (hipStream_t)stream));
+    return launched(qg::launch_w4a8_tiled(d, (hipStream_t)stream));
+}
+
 qg_status qconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *W, const int32_t *bias,
                                   const int32_t *mult, const int32_t *shift, int8_t *Y,
                                   int32_t batch, int32_t H, int32_t Wd, int32_t C_in,

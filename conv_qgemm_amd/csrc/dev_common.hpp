@@ -48,13 +48,20 @@ __device__ __forceinline__ v4i widen_int4_x16(v2u p)
 // 16 int8 bytes in natural order -> the same permutation widen_int4_x16
 // produces: [0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15].
 // v_perm_b32 picks bytes of the 64-bit {src0, src1} (src1 = bytes 0..3).
+// MSB: the int4 operand is packed high nibble first (INT4 GEMM article §3.2's
+// other order), so widen_int4_x16's low-nibble dwords hold the odd elements;
+// the int8 side then takes [1,3,5,7 | 0,2,4,6 | ...] instead, which costs
+// nothing.
+template <bool MSB = false>
 __device__ __forceinline__ v4i even_odd_split(v4i q)
 {
+    constexpr unsigned kFirst = MSB ? 0x07050301u : 0x06040200u;
+    constexpr unsigned kSecond = MSB ? 0x06040200u : 0x07050301u;
     v4i r;
-    r[0] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], 0x06040200u);
-    r[1] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], 0x07050301u);
-    r[2] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], 0x06040200u);
-    r[3] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], 0x07050301u);
+    r[0] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], kFirst);
+    r[1] = (int)__builtin_amdgcn_perm((unsigned)q[1], (unsigned)q[0], kSecond);
+    r[2] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], kFirst);
+    r[3] = (int)__builtin_amdgcn_perm((unsigned)q[3], (unsigned)q[2], kSecond);
     return r;
 }
 

@@ -82,7 +82,7 @@ __device__ __forceinline__ void drain_and_barrier()
 }
 
 // ONE: K fits one chunk, so the activations are loaded once.
-template <bool ONE>
+template <bool ONE, bool MSB>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
             v4i q = af[s];
             for (int e = 0; e < 4; ++e)
                 q[e] &= keep;
-            af[s] = even_odd_split(q);
+            af[s] = even_odd_split<MSB>(q);
         }
     };
 
@@ -284,10 +284,17 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
         grid_x = a.ngroups;
     const int grid_y = (int)((d.M + 15) / 16);
     const dim3 grid(grid_x, grid_y), block(kWaves * 64);
-    if (d.K <= kChunk)
-        hipLaunchKernelGGL((k_skinny_w4a8<true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((k_skinny_w4a8<false>), grid, block, 0, s, a);
+    if (d.msb_first) {
+        if (d.K <= kChunk)
+            hipLaunchKernelGGL((k_skinny_w4a8<true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_skinny_w4a8<false, true>), grid, block, 0, s, a);
+    } else {
+        if (d.K <= kChunk)
+            hipLaunchKernelGGL((k_skinny_w4a8<true, false>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_skinny_w4a8<false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -68,7 +68,9 @@ __device__ __forceinline__ int swz(int row, int kb)
     return row * RB + ((((kb >> 4) ^ (row & (NC - 1)))) << 4) + (kb & 15);
 }
 
-template <int KA, int KB, int EPI, int AL, int BM, int BN, int KT, int WGM, int WGN>
+// MSB: the int4 B operand is packed high nibble first (int8 A only)
+template <int KA, int KB, int EPI, int AL, int BM, int BN, int KT, int WGM, int WGN,
+          bool MSB = false>
 __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
 {
     constexpr int RBA = KA == OP_S8 ? KT : KT / 2;  // LDS bytes per A row
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
                 const int row = arow0 + i * 32;
                 if constexpr (KA == OP_S8) {
                     v4i q = *(const v4i *)(sA + swz<RBA, NCA>(row, ks * 32 + khalf * 16));
-                    af[i] = KB == OP_S4 ? even_odd_split(q) : q;
+                    af[i] = KB == OP_S4 ? even_odd_split<MSB>(q) : q;
                 } else {
                     v2u q = *(const v2u *)(sA + swz<RBA, NCA>(row, ks * 16 + khalf * 8));
                     af[i] = widen_int4_x16(q);
@@ -320,13 +322,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
 // ---------------------------------------------------------------------------
 // host side
 
-template <int KA, int KB, int EPI, int AL, int BM, int BN, int KT, int WGM, int WGN>
+template <int KA, int KB, int EPI, int AL, int BM, int BN, int KT, int WGM, int WGN,
+          bool MSB = false>
 static hipError_t run_tile(TileArgs a, hipStream_t s)
 {
     a.tiles_m = (int)((a.M + BM - 1) / BM);
     a.tiles_n = (int)((a.N + BN - 1) / BN);
     const int tiles = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((k_tile<KA, KB, EPI, AL, BM, BN, KT, WGM, WGN>), dim3(tiles),
+    hipLaunchKernelGGL((k_tile<KA, KB, EPI, AL, BM, BN, KT, WGM, WGN, MSB>), dim3(tiles),
                        dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
@@ -364,17 +367,17 @@ static TileSize pick_tile(int64_t M, int64_t N)
     return TS_64;
 }
 
-template <int KA, int KB, int EPI, int KT>
+template <int KA, int KB, int EPI, int KT, bool MSB = false>
 static hipError_t run_gemm(const GemmDesc &d, hipStream_t s)
 {
     const TileArgs a = gemm_args(d);
     switch (pick_tile(d.M, d.N)) {
     case TS_256:
-        return run_tile<KA, KB, EPI, AL_DENSE, 256, 256, KT, 2, 2>(a, s);
+        return run_tile<KA, KB, EPI, AL_DENSE, 256, 256, KT, 2, 2, MSB>(a, s);
     case TS_128:
-        return run_tile<KA, KB, EPI, AL_DENSE, 128, 128, KT, 2, 2>(a, s);
+        return run_tile<KA, KB, EPI, AL_DENSE, 128, 128, KT, 2, 2, MSB>(a, s);
     default:
-        return run_tile<KA, KB, EPI, AL_DENSE, 64, 64, KT, 2, 2>(a, s);
+        return run_tile<KA, KB, EPI, AL_DENSE, 64, 64, KT, 2, 2, MSB>(a, s);
     }
 }
 
@@ -394,6 +397,8 @@ hipError_t launch_s4s4_i32(const GemmDesc &d, hipStream_t s)
 
 hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s)
 {
+    if (d.msb_first)
+        return run_gemm<OP_S8, OP_S4, EPI_REQUANT, 128, true>(d, s);
     return run_gemm<OP_S8, OP_S4, EPI_REQUANT, 128>(d, s);
 }
 

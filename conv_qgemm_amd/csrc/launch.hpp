@@ -25,6 +25,8 @@ struct GemmDesc {
     // term, rterm the per-row term (or null), out_zero the output zero point
     const int32_t *rterm;
     int out_zero;
+    // W4A8: the int4 weights are packed high nibble first
+    bool msb_first;
 };
 
 // One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,

@@ -53,6 +53,8 @@ def _load():
     lib.qgemm_s4s4_i32.restype = S
     lib.qgemm_w4a8_requant.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
     lib.qgemm_w4a8_requant.restype = S
+    lib.qgemm_w4a8_requant_msb.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
+    lib.qgemm_w4a8_requant_msb.restype = S
     lib.qconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 11 + [P]
     lib.qconv2d_nhwc_s8_requant.restype = S
     lib.qdwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 10 + [P]
@@ -83,7 +85,7 @@ def _load():
 
 
 lib = _load()
-EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
+EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant", "qgemm_w4a8_requant_msb",
            "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qquant_per_token",
            "qgemm_s8s8_requant_zp_workspace_size", "qgemm_s8s8_requant_zp",
            "qconv2d_nhwc_s8_requant_zp_workspace_size", "qconv2d_nhwc_s8_requant_zp",
@@ -182,8 +184,10 @@ def qgemm_s4s4_i32(A, B, C=None, K=None, stream=None):
     return C
 
 
-def qgemm_w4a8_requant(A, B, bias, mult, shift, C=None, K=None, stream=None):
-    """int8 activations A [M, K] x packed int4 weights B uint8 [N, K/2] -> int8."""
+def qgemm_w4a8_requant(A, B, bias, mult, shift, C=None, K=None, stream=None, msb_first=False):
+    """int8 activations A [M, K] x packed int4 weights B uint8 [N, K/2] -> int8.
+    msb_first: the weights hold element 2i in the high nibble of byte i
+    (qgemm_w4a8_requant_msb)."""
     _mat(A, torch.int8, "A")
     _mat(B, torch.uint8, "B")
     M = A.shape[0]
@@ -195,11 +199,11 @@ def qgemm_w4a8_requant(A, B, bias, mult, shift, C=None, K=None, stream=None):
     if C is None:
         C = torch.empty((M, N), dtype=torch.int8, device=A.device)
     _mat(C, torch.int8, "C")
-    st = lib.qgemm_w4a8_requant(_ptr(A), A.stride(0), _ptr(B), 2 * B.stride(0),
-                                _ptr(_vec(bias, N, "bias")), _ptr(_vec(mult, N, "mult")),
-                                _ptr(_vec(shift, N, "shift")), _ptr(C), C.stride(0), M, N, K,
-                                _stream(stream))
-    _check(st, "qgemm_w4a8_requant")
+    f = lib.qgemm_w4a8_requant_msb if msb_first else lib.qgemm_w4a8_requant
+    st = f(_ptr(A), A.stride(0), _ptr(B), 2 * B.stride(0), _ptr(_vec(bias, N, "bias")),
+           _ptr(_vec(mult, N, "mult")), _ptr(_vec(shift, N, "shift")), _ptr(C), C.stride(0), M, N,
+           K, _stream(stream))
+    _check(st, "qgemm_w4a8_requant_msb" if msb_first else "qgemm_w4a8_requant")
     return C
 
 

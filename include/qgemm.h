@@ -125,6 +125,19 @@ qg_status qgemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int
                              void *stream);
 
 /*
+ * qgemm_w4a8_requant_msb -- qgemm_w4a8_requant with the int4 weights packed
+ * high nibble first: element 2i of a row in the high nibble of byte i, 2i+1
+ * in the low one (INT4 GEMM article §3.2 names this order as the one some
+ * NPUs use; its §4.1 conversion script packs that way).  Same arguments and
+ * rules as qgemm_w4a8_requant.  (qgemm_s4s4_i32 needs no such variant: with
+ * both operands in the same order the sum over K is the same either way.)
+ */
+qg_status qgemm_w4a8_requant_msb(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                 const int32_t *bias, const int32_t *mult,
+                                 const int32_t *shift, int8_t *C, int64_t ldc, int64_t M,
+                                 int64_t N, int64_t K, void *stream);
+
+/*
  * qconv2d_nhwc_s8_requant -- int8 NHWC conv, zero-point-0 padding, requant.
  *   X     int8 [batch][H][Wd][C_in]  (NHWC, dense)
  *   W     int8 [C_out][KH][KW][C_in] (OHWI, dense)

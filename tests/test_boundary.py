@@ -29,7 +29,9 @@ def test_exports_every_declared_symbol(qg):
     names = _declared_functions()
     assert set(names) >= {"qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
                           "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant",
-                          "qquant_per_token", "qg_status_string", "qg_version"}
+                          "qquant_per_token", "qgemm_s8s8_requant_zp", "qgemm_w4a8_requant_msb",
+                          "qconv2d_nhwc_s8_requant_zp", "qdwconv2d_nhwc_s8_requant_zp",
+                          "qg_status_string", "qg_version"}
     raw = ctypes.CDLL(qg._LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -70,6 +72,11 @@ def s4(qg, A=P, lda=64, B=P, ldb=64, C=P, ldc=64, M=32, N=64, K=64):
 
 def w4(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=16, N=64, K=64):
     return qg.lib.qgemm_w4a8_requant(A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, None)
+
+
+def w4m(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=16, N=64, K=64):
+    return qg.lib.qgemm_w4a8_requant_msb(A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K,
+                                         None)
 
 
 def cv(qg, X=P, W=P, bias=P, mult=P, shift=P, Y=P, batch=1, H=8, Wd=8, C_in=16, C_out=16,
@@ -115,6 +122,7 @@ def test_nullptr(qg):
     for kw in ("A", "B", "C", "mult", "shift"):
         assert s8(qg, **{kw: NULL}) == E, kw
         assert w4(qg, **{kw: NULL}) == E, kw
+        assert w4m(qg, **{kw: NULL}) == E, kw
     for kw in ("A", "B", "C"):
         assert s4(qg, **{kw: NULL}) == E, kw
     for kw in ("X", "W", "Y", "mult", "shift"):
@@ -131,7 +139,7 @@ def test_nullptr(qg):
 
 def test_invalid_gemm_sizes(qg):
     E = qg.QG_ERR_INVALID
-    for f in (s8, s4, w4):
+    for f in (s8, s4, w4, w4m):
         assert f(qg, M=0) == E
         assert f(qg, N=0) == E
         assert f(qg, K=0) == E
@@ -144,6 +152,7 @@ def test_invalid_gemm_sizes(qg):
     assert s8(qg, K=40, lda=64, ldb=64) == E
     assert s4(qg, K=48, lda=64, ldb=64) == E
     assert w4(qg, K=48, lda=64, ldb=64) == E
+    assert w4m(qg, K=48, lda=64, ldb=64) == E
     # row strides: multiples of 16 bytes
     assert s8(qg, lda=72) == E
     assert s4(qg, lda=80) == E              # 80 nibbles = 40 bytes
@@ -152,6 +161,7 @@ def test_invalid_gemm_sizes(qg):
     big = qg.QG_S4S4_MAX_K + 32
     assert s4(qg, K=big, lda=big, ldb=big) == E
     assert w4(qg, K=big, lda=big, ldb=big) == E
+    assert w4m(qg, K=big, lda=big, ldb=big) == E
 
 
 def test_invalid_alignment(qg):
@@ -250,6 +260,7 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert s8(qg) == qg.QG_ERR_NO_DEVICE
     assert s4(qg) == qg.QG_ERR_NO_DEVICE
     assert w4(qg) == qg.QG_ERR_NO_DEVICE
+    assert w4m(qg) == qg.QG_ERR_NO_DEVICE
     assert cv(qg) == qg.QG_ERR_NO_DEVICE
     assert dw(qg) == qg.QG_ERR_NO_DEVICE
     assert qt(qg) == qg.QG_ERR_NO_DEVICE

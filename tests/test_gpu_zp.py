@@ -199,3 +199,39 @@ def test_dwconv_zp_workload_full(qg, orc):
         want = orc.dwconv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
                                                za, zb, zo)
         assert np.array_equal(Y.cpu().numpy(), want), (za, zb, zo)
+
+
+# ---------------------------------------------------------------- MSB-first INT4
+
+@pytest.mark.parametrize("M,N,K", [(16, 512, 1024), (5, 100, 8224), (64, 96, 16416),
+                                   (100, 160, 512), (300, 260, 1024)])
+def test_w4a8_msb_first(qg, orc, M, N, K):
+    """Skinny kernel for M <= 64 (including K tails), tile kernel above."""
+    _say("w4a8 msb", M, N, K)
+    d = datagen.gemm_w4a8(M, N, K, seed=M + N, shift=(37, 43))
+    C = qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]), msb_first=True)
+    want = orc.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"],
+                                 msb_first=True)
+    assert np.array_equal(C.cpu().numpy(), want)
+    # the same bytes read low nibble first give a different result
+    lsb = orc.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert not np.array_equal(want, lsb)
+
+
+def test_w4a8_msb_workload_full(qg, orc):
+    _say("w4a8 msb workload")
+    d = datagen.workload("w4a8", unsaturated=True)
+    C = qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                              dev(d["shift"]), msb_first=True)
+    want = orc.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"],
+                                 msb_first=True)
+    assert np.array_equal(C.cpu().numpy(), want)
+
+
+def test_s4s4_msb_first_operands(qg, orc):
+    """Both operands high nibble first: qgemm_s4s4_i32 gives the MSB-first
+    product as it stands."""
+    d = datagen.gemm_s4s4(130, 70, 512, seed=12)
+    C = qg.qgemm_s4s4_i32(dev(d["A"]), dev(d["B"]))
+    assert np.array_equal(C.cpu().numpy(), orc.gemm_s4s4_i32(d["A"], d["B"], msb_first=True))
