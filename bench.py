@@ -10,6 +10,10 @@ One step is one call of every entry point on its workload:
   quant_a8   qquant_per_token    8192 tokens x 8192 channels, bfloat16 -> int8
              codes + float32 scales (the s8s8 A operand; no integer ops)
   s8s8       qgemm_s8s8_requant  M=N=K=8192
+  conv3x3_zp, s8s8_zp  the asymmetric calls (qconv2d_nhwc_s8_requant_zp,
+             qgemm_s8s8_requant_zp) on the same arrays with zero points on
+             the input, the weights and the output; their time includes the
+             compensation-sum pass
 Inputs are seeded synthetic arrays resident in HBM before timing starts.
 Each workload rotates through enough copies of its buffers that every call
 reads HBM rather than the 256 MB Infinity Cache (the pointwise case is
@@ -36,10 +40,11 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
-ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "s4s4", "s8s8"]
+ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "conv3x3_zp", "s4s4", "s8s8",
+         "s8s8_zp"]
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
-ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "dw3x3": 40, "quant_a8": 3, "w4a8": 5,
-          "s8s8": 3}
+ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "conv3x3_zp": 40, "dw3x3": 40,
+          "quant_a8": 3, "w4a8": 5, "s8s8": 3, "s8s8_zp": 3}
 KERNEL_SOURCES = {
     "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
@@ -48,6 +53,8 @@ KERNEL_SOURCES = {
     "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
     "dw3x3": "conv_qgemm_amd/csrc/k_dwconv.hip",
     "quant_a8": "conv_qgemm_amd/csrc/k_quant.hip",
+    "s8s8_zp": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
+    "conv3x3_zp": "conv_qgemm_amd/csrc/k_conv_halo.hip",
 }
 
 
@@ -148,6 +155,14 @@ class Case:
                 s["C"] = torch.empty((w["M"], w["N"]), dtype=torch.int32, device="cuda")
             else:
                 s["C"] = torch.empty((w["M"], w["N"]), dtype=torch.int8, device="cuda")
+            if "zp" in w:
+                if w["kind"] == "conv":
+                    nb = qgemm.lib.qconv2d_nhwc_s8_requant_zp_workspace_size(
+                        w["batch"], w["H"], w["W"], w["C_out"], w["KH"], w["KW"],
+                        w["stride"][0], w["stride"][1], w["pad"][0], w["pad"][1])
+                else:
+                    nb = qgemm.lib.qgemm_s8s8_requant_zp_workspace_size(w["M"], w["N"])
+                s["ws"] = torch.empty(nb, dtype=torch.uint8, device="cuda")
             self.sets.append(s)
         self.ops, self.bytes = ops_and_bytes(name)
 
@@ -158,6 +173,15 @@ class Case:
             return q.qgemm_s4s4_i32(s["A"], s["B"], C=s["C"])
         if self.name == "w4a8":
             return q.qgemm_w4a8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
+        if self.name == "s8s8_zp":
+            za, zb, zo = shape_of(self.name)["zp"]
+            return q.qgemm_s8s8_requant_zp(s["A"], s["B"], s["bias"], s["mult"], s["shift"], za,
+                                           zb, zo, C=s["C"], workspace=s["ws"])
+        if self.name == "conv3x3_zp":
+            za, zb, zo = shape_of(self.name)["zp"]
+            return q.qconv2d_nhwc_s8_requant_zp(s["X"], s["W"], s["bias"], s["mult"], s["shift"],
+                                                za, zb, zo, stride=(1, 1), pad=(1, 1), Y=s["Y"],
+                                                workspace=s["ws"])
         if self.name == "quant_a8":
             return q.qquant_per_token(s["X"], bits=shape_of("quant_a8")["bits"], Q=s["Q"],
                                       scale=s["scale"])
@@ -186,7 +210,12 @@ def cpu_baseline(names, frac=16):
         w = shape_of(name)
         ops, _ = ops_and_bytes(name)
         t0 = time.perf_counter()
-        if w["kind"] == "s8s8":
+        if w["kind"] == "s8s8" and "zp" in w:
+            rows = np.arange(0, w["M"], frac)
+            oracle.gemm_s8s8_requant_zp(d["A"], d["B"], d["bias"], d["mult"], d["shift"],
+                                        *w["zp"], rows=rows)
+            part = len(rows) / w["M"]
+        elif w["kind"] == "s8s8":
             rows = np.arange(0, w["M"], frac)
             oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
             part = len(rows) / w["M"]
@@ -215,6 +244,12 @@ def cpu_baseline(names, frac=16):
             pix = np.arange(0, npix, frac)
             oracle.dwconv2d_nhwc_s8_requant(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
                                             pix=pix)
+            part = len(pix) / npix
+        elif "zp" in w:
+            npix = w["batch"] * w["H"] * w["W"]
+            pix = np.arange(0, npix, frac)
+            oracle.conv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                             *w["zp"], pix=pix)
             part = len(pix) / npix
         else:
             npix = w["batch"] * w["H"] * w["W"]
@@ -405,8 +440,12 @@ def main():
     ms_per_step = gpu_step * 1e3
     value = total_ops / gpu_step / 1e12
 
-    dom = max(per, key=lambda n: per[n]["us_avg"])
-    mfma_bound = dom in ("s8s8", "s4s4", "conv3x3", "pointwise")
+    # the roofline describes the dominant single kernel: the longest of the
+    # workloads that are one kernel launch (the asymmetric calls add a
+    # compensation-sum pass in front of theirs)
+    single = [n for n in per if not n.endswith("_zp")] or list(per)
+    dom = max(single, key=lambda n: per[n]["us_avg"])
+    mfma_bound = dom in ("s8s8", "s8s8_zp", "s4s4", "conv3x3", "conv3x3_zp", "pointwise")
     if mfma_bound:
         achieved = per[dom]["tops"]
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
@@ -436,7 +475,9 @@ def main():
              "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
              "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
              "quant_a8": "per-token quant bf16 8192x8192 -> int8",
-             "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3"}[n] for n in names),
+             "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3",
+             "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}[n]
+            for n in names),
                    "parallelism": "single GPU", "seeds": "numpy PCG64 1..7",
                    "timing": f"per workload: {args.warmup} warm-up calls, then "
                              f"{args.steps} back-to-back calls captured in a HIP graph "

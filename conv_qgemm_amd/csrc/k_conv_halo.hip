@@ -67,9 +67,8 @@ struct HaloArgs {
     int H, Wd, C_out, ph, pw, Ho, Wo;
     int tiles_per_img;
     int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
-    int pad4;              // padding byte (the input zero point) x4
-    const int32_t *rterm;  // ZP: per-pixel term, or null
-    int out_zero;          // ZP: output zero point
+    int pad4;                  // padding byte (the input zero point) x4
+    int a_zero, b_zero, out_zero;  // ZP: the zero points
 };
 
 __device__ __forceinline__ void drain_and_barrier()
@@ -77,8 +76,11 @@ __device__ __forceinline__ void drain_and_barrier()
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// ZP: the asymmetric form -- `bias` holds the per-channel term, rterm the
-// per-pixel one, and the output zero point joins before the saturation
+// ZP: the asymmetric form.  The kernel forms both compensation terms itself:
+// the per-pixel sum of its im2col row (padding counted as za) from the
+// operand fragments it multiplies, and the per-channel weight sum from the
+// weight rows in LDS; x = acc - zb * rowsum + (bias - za * wsum + K za zb),
+// modulo 2^32.  The output zero point joins before the saturation.
 template <int KH, int KW, bool ZP>
 __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 {
@@ -180,18 +182,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 
     // ---- this lane's pixel in each of the wave's 4 M tiles, as the LDS
     //      offset of its (0, 0) tap; pixels past the tile reuse the last one ----
-    int abase[4], rt[4] = {0, 0, 0, 0};
+    int abase[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = min(64 * wave + 16 * i + col, npix - 1);
-        if constexpr (ZP) {
-            if (p.rterm)
-                rt[i] = p.rterm[(int64_t)b * HW + p0 + q];
-        }
         const int pp = p0 + q;
         const int oh = pp / p.Wo;
         const int ow = pp - oh * p.Wo;
         abase[i] = (oh - oh_first) * rowL + ow * kPixL + 16 * g;
+    }
+
+    // ZP: per-channel weight sums of the 64 weight rows in LDS, four threads
+    // per row; the bias slot of prm becomes bias - za * wsum + K * za * zb
+    if constexpr (ZP) {
+        const int oc = tid >> 2, part = tid & 3;
+        unsigned ws = 0;
+        for (int G = part; G < KK * 4; G += 4) {
+            const v4i v = *(const v4i *)(WT + oc * kRowW + 16 * G);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ws = (unsigned)__builtin_amdgcn_sdot4(v[e], 0x01010101, (int)ws, false);
+        }
+        ws += (unsigned)__shfl_xor((int)ws, 1);
+        ws += (unsigned)__shfl_xor((int)ws, 2);
+        if (part == 0)
+            prm[oc] = (int)((unsigned)prm[oc] - (unsigned)p.a_zero * ws +
+                            (unsigned)(KK * kCin) * (unsigned)(p.a_zero * p.b_zero));
     }
 
     v4i acc[4][4];
@@ -200,6 +216,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             acc[i][n] = (v4i){0, 0, 0, 0};
+    unsigned rs[4] = {0, 0, 0, 0};  // ZP: this lane's 16 channels of each pixel's im2col row
 
     v4i a[2][4], w[2][4];
     auto read_tap = [&](int t, v4i(&at)[4], v4i(&wt)[4]) {
@@ -226,6 +243,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
             for (int n = 0; n < 4; ++n)
                 acc[i][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[t & 1][n], a[t & 1][i],
                                                                  acc[i][n], 0, 0, 0);
+        if constexpr (ZP) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rs[i] = (unsigned)__builtin_amdgcn_sdot4(a[t & 1][i][e], 0x01010101,
+                                                             (int)rs[i], false);
+        }
+    }
+    // ZP: the four K groups of a pixel sit in lanes col, col + 16, col + 32,
+    // col + 48; after the sum every one of them holds zb * (its im2col row sum)
+    int rt[4] = {0, 0, 0, 0};
+    if constexpr (ZP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unsigned v = rs[i];
+            v += (unsigned)__shfl_xor((int)v, 16);
+            v += (unsigned)__shfl_xor((int)v, 32);
+            rt[i] = (int)((unsigned)p.b_zero * v);
+        }
     }
 
     // ---- requantize into LDS (the input rows are no longer needed) ----
@@ -353,7 +390,8 @@ hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s)
     a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
     a.in_bytes = (int)halo_in_bytes(d);
     a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
-    a.rterm = d.rterm;
+    a.a_zero = d.a_zero;
+    a.b_zero = d.b_zero;
     a.out_zero = d.out_zero;
     const int lds = (int)halo_lds_bytes(d);
     if (d.asym) {

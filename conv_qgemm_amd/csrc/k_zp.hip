@@ -16,13 +16,15 @@
 // true x whenever that fits in int32, which the API requires.
 // For a conv the rows of A are im2col rows whose padding holds the input
 // zero point (MCU conv front-end article, news.rkmt.cn/news/16638, §2.3);
-// the conv kernels pad with za, and rterm sums those rows the same way.
+// the conv kernels pad with za, and rterm sums those rows the same way.  The
+// LDS-staged conv kernel (stride 1, 64 input channels) forms both sums
+// itself from data it already holds and needs no pass here.
 // The depthwise 3x3 kernel takes zb = 0 and cterm only; other depthwise
 // shapes multiply (x - za)(w - zb) directly.
 //
 // Row sums use v_dot4_i32_i8 against 0x01010101 (four bytes per
-// instruction), one wave per row, 16-byte loads; they are memory-bound
-// passes over A and B.
+// instruction), one wave per row, 16-byte loads with eight in flight per
+// lane; they are memory-bound passes over A and B.
 #include "dev_common.hpp"
 #include "launch.hpp"
 
@@ -47,12 +49,20 @@ struct RowTermArgs {
 // 2^32, reduced over the wave
 __device__ __forceinline__ unsigned row_sum_s8(const int8_t *row, int nv, int lane)
 {
+    constexpr int kBatch = 8;  // loads in flight per lane
     unsigned s = 0;
-    for (int i = lane; i < nv; i += 64) {
-        const v4i v = *(const v4i *)(row + (int64_t)i * 16);
+    for (int i0 = 0; i0 < nv; i0 += 64 * kBatch) {
+        v4i v[kBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            s = (unsigned)__builtin_amdgcn_sdot4(v[e], 0x01010101, (int)s, false);
+        for (int j = 0; j < kBatch; ++j) {
+            const int i = i0 + 64 * j + lane;
+            v[j] = i < nv ? *(const v4i *)(row + (int64_t)i * 16) : (v4i){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s = (unsigned)__builtin_amdgcn_sdot4(v[j][e], 0x01010101, (int)s, false);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
@@ -205,10 +215,13 @@ hipError_t run_s8s8_requant_zp(GemmDesc d, int za, int zb, void *ws, hipStream_t
 
 hipError_t run_conv_zp(ConvDesc d, void *ws, hipStream_t s)
 {
-    int32_t *cterm = (int32_t *)ws;
-    int32_t *rterm = (int32_t *)((uint8_t *)ws + align256(4 * (int64_t)d.C_out));
     d.asym = true;
     d.rterm = nullptr;
+    // the LDS-staged kernel forms both terms itself
+    if (conv_halo_fits(d))
+        return launch_conv_halo(d, s);
+    int32_t *cterm = (int32_t *)ws;
+    int32_t *rterm = (int32_t *)((uint8_t *)ws + align256(4 * (int64_t)d.C_out));
     if (d.a_zero != 0 || d.b_zero != 0) {
         const int64_t Kc = (int64_t)d.KH * d.KW * d.C_in;
         hipError_t e = launch_zp_gemm_terms(nullptr, 0, d.W, Kc, d.bias, 0, d.C_out, Kc, d.a_zero,
@@ -223,8 +236,6 @@ hipError_t run_conv_zp(ConvDesc d, void *ws, hipStream_t s)
             return e;
         d.rterm = rterm;
     }
-    if (conv_halo_fits(d))
-        return launch_conv_halo(d, s);
     return launch_conv_nhwc(d, s);
 }
 
