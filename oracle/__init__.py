@@ -83,21 +83,21 @@ def _load():
     lib.orc_dwconv2d_acc.restype = ctypes.c_int
     lib.orc_dwconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I64] * 10 + [P, I64]
     lib.orc_dwconv2d_nhwc_s8_requant.restype = ctypes.c_int
-    lib.orc_requant_zp.argtypes = [I64, I32, I32, I32, I32, P]
+    lib.orc_requant_zp.argtypes = [I64, I32, I32, I32, I32, I32, I32, P]
     lib.orc_requant_zp.restype = ctypes.c_int
     lib.orc_gemm_s8s8_acc_zp.argtypes = [P, I64, P, I64, I32, I32, I64, I64, P, I64, P]
     lib.orc_gemm_s8s8_acc_zp.restype = ctypes.c_int
-    lib.orc_gemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, P, I64,
-                                             I64, I64, P, I64]
+    lib.orc_gemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32,
+                                             P, I64, I64, I64, P, I64]
     lib.orc_gemm_s8s8_requant_zp.restype = ctypes.c_int
     lib.orc_conv2d_acc_zp.argtypes = [P, P] + [I64] * 11 + [I32, I32, P, I64, P]
     lib.orc_conv2d_acc_zp.restype = ctypes.c_int
-    lib.orc_conv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+    lib.orc_conv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P] + \
         [I64] * 11 + [P, I64]
     lib.orc_conv2d_nhwc_s8_requant_zp.restype = ctypes.c_int
     lib.orc_dwconv2d_acc_zp.argtypes = [P, P] + [I64] * 10 + [I32, I32, P, I64, P]
     lib.orc_dwconv2d_acc_zp.restype = ctypes.c_int
-    lib.orc_dwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+    lib.orc_dwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P] + \
         [I64] * 10 + [P, I64]
     lib.orc_dwconv2d_nhwc_s8_requant_zp.restype = ctypes.c_int
     lib.orc_int4_at_msb.argtypes = [P, I64]
@@ -179,11 +179,13 @@ def int4_at_msb(packed_row: np.ndarray, i: int) -> int:
     return int(_load().orc_int4_at_msb(row.ctypes.data, int(i)))
 
 
-def requant_zp(acc: int, bias: int, mult: int, shift: int, out_zero: int) -> int:
-    """clamp((((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero)."""
+def requant_zp(acc: int, bias: int, mult: int, shift: int, out_zero: int,
+               act=(-128, 127)) -> int:
+    """clamp((((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero) to
+    [act[0], act[1]] (the int8 range by default; (out_zero, 127) is ReLU)."""
     out = np.zeros(1, dtype=np.int8)
     st = _load().orc_requant_zp(int(acc), int(bias), int(mult), int(shift), int(out_zero),
-                                out.ctypes.data)
+                                int(act[0]), int(act[1]), out.ctypes.data)
     _check(st, "requant_zp")
     return int(out[0])
 
@@ -442,7 +444,8 @@ def gemm_s8s8_acc_zp(A, B, a_zero, b_zero, rows=None):
     return out
 
 
-def gemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, rows=None):
+def gemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, rows=None,
+                         act=(-128, 127)):
     A = _c(A, np.int8)
     B = _c(B, np.int8)
     M, K = A.shape
@@ -455,8 +458,8 @@ def gemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, rows
     C = np.zeros((nr, N), dtype=np.int8)
     st = _load().orc_gemm_s8s8_requant_zp(A.ctypes.data, K, B.ctypes.data, K, _ptr(bias_c),
                                           mult.ctypes.data, shift.ctypes.data, int(a_zero),
-                                          int(b_zero), int(out_zero), C.ctypes.data, N, N, K,
-                                          _ptr(r), nr)
+                                          int(b_zero), int(out_zero), int(act[0]), int(act[1]),
+                                          C.ctypes.data, N, N, K, _ptr(r), nr)
     _check(st, "gemm_s8s8_requant_zp")
     return C
 
@@ -475,7 +478,7 @@ def conv2d_acc_zp(X, Wt, a_zero, b_zero, stride=(1, 1), pad=(1, 1), pix=None):
 
 
 def conv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_zero,
-                              stride=(1, 1), pad=(1, 1), pix=None):
+                              stride=(1, 1), pad=(1, 1), pix=None, act=(-128, 127)):
     X, Wt, g, Ho, Wo = _conv_geom(X, Wt, stride, pad)
     batch, C_out = g[0], g[4]
     bias_c = None if bias is None else _c(bias, np.int32)
@@ -486,7 +489,8 @@ def conv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_zero
     st = _load().orc_conv2d_nhwc_s8_requant_zp(X.ctypes.data, Wt.ctypes.data, _ptr(bias_c),
                                                mult.ctypes.data, shift.ctypes.data,
                                                int(a_zero), int(b_zero), int(out_zero),
-                                               Y.ctypes.data, *g, _ptr(r), nr)
+                                               int(act[0]), int(act[1]), Y.ctypes.data, *g,
+                                               _ptr(r), nr)
     _check(st, "conv2d_nhwc_s8_requant_zp")
     if pix is None:
         return Y.reshape(batch, Ho, Wo, C_out)
@@ -507,7 +511,7 @@ def dwconv2d_acc_zp(X, Wt, a_zero, b_zero, stride=(1, 1), pad=(1, 1), pix=None):
 
 
 def dwconv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_zero,
-                                stride=(1, 1), pad=(1, 1), pix=None):
+                                stride=(1, 1), pad=(1, 1), pix=None, act=(-128, 127)):
     X, Wt, g, Ho, Wo = _dw_geom(X, Wt, stride, pad)
     batch, C = g[0], g[3]
     bias_c = None if bias is None else _c(bias, np.int32)
@@ -518,7 +522,8 @@ def dwconv2d_nhwc_s8_requant_zp(X, Wt, bias, mult, shift, a_zero, b_zero, out_ze
     st = _load().orc_dwconv2d_nhwc_s8_requant_zp(X.ctypes.data, Wt.ctypes.data, _ptr(bias_c),
                                                  mult.ctypes.data, shift.ctypes.data,
                                                  int(a_zero), int(b_zero), int(out_zero),
-                                                 Y.ctypes.data, *g, _ptr(r), nr)
+                                                 int(act[0]), int(act[1]), Y.ctypes.data, *g,
+                                                 _ptr(r), nr)
     _check(st, "dwconv2d_nhwc_s8_requant_zp")
     if pix is None:
         return Y.reshape(batch, Ho, Wo, C)

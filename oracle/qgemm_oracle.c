@@ -395,21 +395,27 @@ int orc_dwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
  * is scale_a * scale_b * (A - za) * (B - zb), so the integer accumulator is
  * sum_k (A[m][k] - za) * (B[n][k] - zb), written out below term by term. ---- */
 
-/* Q31 requantize with an output zero point: the shifted value plus
- * out_zero, saturated to int8. */
+/* Q31 requantize with an output zero point and a fused activation: the
+ * shifted value plus out_zero, clamped to [act_min, act_max] inside the int8
+ * range.  [VOYAGER] §3.1 fuses the activation into the GEMM and requantize
+ * (Conv -> DQ -> ReLU -> Q becomes one operator); on codes with zero point
+ * out_zero, ReLU is the clamp at act_min = out_zero, and (-128, 127) is the
+ * plain int8 saturation. */
 int orc_requant_zp(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int32_t out_zero,
-                   int8_t *out)
+                   int32_t act_min, int32_t act_max, int8_t *out)
 {
     const int64_t x = acc + bias;
     if (x < INT32_MIN || x > INT32_MAX)
         return ORC_E_RANGE;
     if (shift < 1 || shift > 63 || mult < 0 || out_zero < -128 || out_zero > 127)
         return ORC_E_DOMAIN;
+    if (act_min < -128 || act_max > 127 || act_min > act_max)
+        return ORC_E_DOMAIN;
     int64_t t = (int64_t)mult * x;          /* |t| < 2^62 */
     t += (int64_t)1 << (shift - 1);         /* half an LSB */
     t >>= shift;                            /* arithmetic shift (gcc) */
     t += out_zero;                          /* output zero point */
-    *out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));
+    *out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));
     return ORC_OK;
 }
 
@@ -446,6 +452,7 @@ int orc_gemm_s8s8_acc_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t 
 int orc_gemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
                              const int32_t *bias, const int32_t *mult, const int32_t *shift,
                              int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                             int32_t act_min, int32_t act_max,
                              int8_t *C, int64_t ldc, int64_t N, int64_t K,
                              const int64_t *rows, int64_t nrows)
 {
@@ -458,7 +465,8 @@ int orc_gemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int6
         for (int64_t n = 0; n < N; ++n) {
             int64_t acc = dot_s8_s8_zp(A + m * lda, B + n * ldb, K, a_zero, b_zero);
             int8_t y = 0;
-            status |= orc_requant_zp(acc, bias ? bias[n] : 0, mult[n], shift[n], out_zero, &y);
+            status |= orc_requant_zp(acc, bias ? bias[n] : 0, mult[n], shift[n], out_zero,
+                                     act_min, act_max, &y);
             C[r * ldc + n] = y;
         }
     }
@@ -517,7 +525,7 @@ int orc_conv2d_acc_zp(const int8_t *X, const int8_t *Wt,
 int orc_conv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
                                   const int32_t *bias, const int32_t *mult,
                                   const int32_t *shift, int32_t a_zero, int32_t b_zero,
-                                  int32_t out_zero, int8_t *Y,
+                                  int32_t out_zero, int32_t act_min, int32_t act_max, int8_t *Y,
                                   int64_t batch, int64_t H, int64_t W, int64_t C_in,
                                   int64_t C_out, int64_t KH, int64_t KW, int64_t sh,
                                   int64_t sw, int64_t ph, int64_t pw,
@@ -540,7 +548,7 @@ int orc_conv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
                                          a_zero, b_zero, b, oh, ow, oc);
             int8_t y = 0;
             status |= orc_requant_zp(acc, bias ? bias[oc] : 0, mult[oc], shift[oc], out_zero,
-                                     &y);
+                                     act_min, act_max, &y);
             Y[r * C_out + oc] = y;
         }
     }
@@ -594,7 +602,8 @@ int orc_dwconv2d_acc_zp(const int8_t *X, const int8_t *Wt,
 int orc_dwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
                                     const int32_t *bias, const int32_t *mult,
                                     const int32_t *shift, int32_t a_zero, int32_t b_zero,
-                                    int32_t out_zero, int8_t *Y,
+                                    int32_t out_zero, int32_t act_min, int32_t act_max,
+                                    int8_t *Y,
                                     int64_t batch, int64_t H, int64_t W, int64_t C,
                                     int64_t KH, int64_t KW, int64_t sh, int64_t sw,
                                     int64_t ph, int64_t pw, const int64_t *pix, int64_t npix)
@@ -615,7 +624,8 @@ int orc_dwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *Wt,
             int64_t acc = dwconv_acc_zp_at(X, Wt, H, W, C, KH, KW, sh, sw, ph, pw,
                                            a_zero, b_zero, b, oh, ow, c);
             int8_t y = 0;
-            status |= orc_requant_zp(acc, bias ? bias[c] : 0, mult[c], shift[c], out_zero, &y);
+            status |= orc_requant_zp(acc, bias ? bias[c] : 0, mult[c], shift[c], out_zero,
+                                     act_min, act_max, &y);
             Y[r * C + c] = y;
         }
     }

@@ -50,8 +50,11 @@ MUTANTS = {
                           "if (k % 2 == 1)\n                    *byte"),
     "zp_out_zero_dropped": ("t += out_zero;", "t += 0;"),
     "zp_out_zero_after_clamp": ("t += out_zero;                          /* output zero point */\n"
-                                "    *out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));",
-                                "*out = (int8_t)((t > 127 ? 127 : (t < -128 ? -128 : t)) + out_zero);"),
+                                "    *out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));",
+                                "*out = (int8_t)((t > act_max ? act_max : (t < act_min ? act_min : t))"
+                                " + out_zero);"),
+    "act_clamp_ignored": ("*out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));",
+                          "*out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));"),
     "zp_a_zero_dropped": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",
                           "acc += ((int64_t)a[k]) * ((int64_t)b[k] - zb);"),
     "zp_b_zero_sign": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",

@@ -66,6 +66,39 @@ def test_requant_zp_reduces_and_shifts(orc):
         orc.requant_zp(1, 0, 2 ** 30, 31, 128)
 
 
+# acc, bias, mult, shift, out_zero, (act_min, act_max), expected
+HAND_ACT = [
+    (200, 0, 2 ** 30, 31, 10, (-128, 100), 100),   # 110 capped by the upper bound
+    (-300, 0, 2 ** 30, 31, 0, (0, 127), 0),         # ReLU of -150
+    (-300, 0, 2 ** 30, 31, -20, (-20, 127), -20),   # ReLU at a nonzero zero point
+    (3, 0, 2 ** 30, 31, -2, (-2, 127), 0),          # above the ReLU bound: unchanged
+    (200, 0, 2 ** 30, 31, -128, (-50, 50), -28),    # inside the bounds: unchanged
+    (2 ** 31 - 1, 0, 2 ** 31 - 1, 1, 5, (5, 17), 17),
+]
+
+
+@pytest.mark.parametrize("acc,bias,mult,shift,zo,act,want", HAND_ACT)
+def test_requant_act_hand(orc, acc, bias, mult, shift, zo, act, want):
+    assert orc.requant_zp(acc, bias, mult, shift, zo, act=act) == want
+
+
+def test_requant_act_is_a_clamp_of_the_plain_result(orc):
+    g = np.random.default_rng(11)
+    for _ in range(2000):
+        acc = int(g.integers(-2 ** 22, 2 ** 22))
+        mult = int(g.integers(2 ** 30, 2 ** 31))
+        shift = int(g.integers(25, 40))
+        zo = int(g.integers(-128, 128))
+        lo = int(g.integers(-128, 128))
+        hi = int(g.integers(lo, 128))
+        y = orc.requant_zp(acc, 0, mult, shift, zo)
+        assert orc.requant_zp(acc, 0, mult, shift, zo, act=(lo, hi)) == min(max(y, lo), hi)
+        assert orc.requant_zp(acc, 0, mult, shift, zo, act=(zo, 127)) == max(y, zo)  # ReLU
+    for bad in ((5, 4), (-129, 0), (0, 128)):
+        with pytest.raises(orc.OracleDomainError):
+            orc.requant_zp(1, 0, 2 ** 30, 31, 0, act=bad)
+
+
 # ---------------------------------------------------------------- GEMM
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 7, 16), (33, 9, 100), (17, 40, 257)])
@@ -123,6 +156,10 @@ def test_gemm_zp_requant_composition(orc):
     rows = np.array([0, 7, 20])
     assert np.array_equal(orc.gemm_s8s8_requant_zp(d["A"], d["B"], d["bias"], d["mult"],
                                                    d["shift"], za, zb, zo, rows=rows), C[rows])
+    relu = orc.gemm_s8s8_requant_zp(d["A"], d["B"], d["bias"], d["mult"], d["shift"], za, zb, zo,
+                                    act=(zo, 127))
+    assert np.array_equal(relu, np.maximum(C, zo))
+    assert (C < zo).any()  # the ReLU case is not vacuous
 
 
 def test_gemm_zp_domain(orc):
@@ -203,6 +240,9 @@ def test_conv_zp_reduces_and_composes(orc):
     pix = np.array([3, 50, 83])
     assert np.array_equal(orc.conv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"],
                                                         d["shift"], za, zb, zo, pix=pix), Y[pix])
+    act = orc.conv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"], za, zb,
+                                        zo, act=(-40, 60)).reshape(-1, 8)
+    assert np.array_equal(act, np.clip(Y, -40, 60))
 
 
 def test_conv_zp_shift_invariance(orc):
@@ -267,6 +307,9 @@ def test_dwconv_zp_requant_composition(orc):
         for c in range(16):
             assert Y[p, c] == orc.requant_zp(int(acc[p, c]), int(d["bias"][c]),
                                              int(d["mult"][c]), int(d["shift"][c]), zo)
+    relu = orc.dwconv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"],
+                                           za, zb, zo, act=(zo, 127)).reshape(-1, 16)
+    assert np.array_equal(relu, np.maximum(Y, zo))
 
 
 # ---------------------------------------------------------------- MSB-first INT4
