@@ -146,6 +146,8 @@ qg_status check_dwconv(const int8_t *X, const int8_t *W, const int8_t *Y, int32_
 
 bool zero_point_ok(int32_t z) { return z >= -128 && z <= 127; }
 
+bool act_ok(int32_t lo, int32_t hi) { return -128 <= lo && lo <= hi && hi <= 127; }
+
 // a workspace of at least `need` bytes, 16-byte aligned
 qg_status check_workspace(const void *ws, size_t bytes, int64_t need)
 {
@@ -325,8 +327,9 @@ size_t qgemm_s8s8_requant_zp_workspace_size(int64_t M, int64_t N)
 
 qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
                                 const int32_t *bias, const int32_t *mult, const int32_t *shift,
-                                int32_t a_zero, int32_t b_zero, int32_t out_zero, int8_t *C,
-                                int64_t ldc, int64_t M, int64_t N, int64_t K, void *workspace,
+                                int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                int32_t act_min, int32_t act_max, int8_t *C, int64_t ldc,
+                                int64_t M, int64_t N, int64_t K, void *workspace,
                                 size_t workspace_bytes, void *stream)
 {
     if (!A || !B || !C || !mult || !shift)
@@ -336,7 +339,8 @@ qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, i
         st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero) ||
+        !act_ok(act_min, act_max))
         return QG_ERR_INVALID;
     if ((st = check_workspace(workspace, workspace_bytes, qg::zp_gemm_workspace_bytes(M, N))) !=
         QG_OK)
@@ -344,7 +348,8 @@ qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, i
     int cus = 0;
     if ((st = check_device(&cus)) != QG_OK)
         return st;
-    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, cus, nullptr, out_zero};
+    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, cus, nullptr, out_zero,
+                   false, act_min, act_max};
     return launched(qg::run_s8s8_requant_zp(d, a_zero, b_zero, workspace, (hipStream_t)stream));
 }
 
@@ -368,7 +373,8 @@ size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32
 
 qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
                                      const int32_t *mult, const int32_t *shift, int32_t a_zero,
-                                     int32_t b_zero, int32_t out_zero, int8_t *Y, int32_t batch,
+                                     int32_t b_zero, int32_t out_zero, int32_t act_min,
+                                     int32_t act_max, int8_t *Y, int32_t batch,
                                      int32_t H, int32_t Wd, int32_t C_in, int32_t C_out,
                                      int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
                                      int32_t pad_h, int32_t pad_w, void *workspace,
@@ -383,7 +389,8 @@ qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int
         st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero) ||
+        !act_ok(act_min, act_max))
         return QG_ERR_INVALID;
     const int64_t pixels = (int64_t)batch * Ho * Wo;
     if ((st = check_workspace(workspace, workspace_bytes,
@@ -394,7 +401,7 @@ qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int
         return st;
     qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C_in, C_out, KH, KW,
                    stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo,
-                   true, a_zero, b_zero, out_zero, nullptr};
+                   true, a_zero, b_zero, out_zero, nullptr, act_min, act_max};
     return launched(qg::run_conv_zp(d, workspace, (hipStream_t)stream));
 }
 
@@ -408,6 +415,7 @@ size_t qdwconv2d_nhwc_s8_requant_zp_workspace_size(int32_t C)
 qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
                                        const int32_t *mult, const int32_t *shift,
                                        int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                       int32_t act_min, int32_t act_max,
                                        int8_t *Y, int32_t batch, int32_t H, int32_t Wd,
                                        int32_t C, int32_t KH, int32_t KW, int32_t stride_h,
                                        int32_t stride_w, int32_t pad_h, int32_t pad_w,
@@ -422,7 +430,8 @@ qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const i
         st = check_params(bias, mult, shift);
     if (st != QG_OK)
         return st;
-    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero))
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero) ||
+        !act_ok(act_min, act_max))
         return QG_ERR_INVALID;
     if ((st = check_workspace(workspace, workspace_bytes, qg::zp_dw_workspace_bytes(C))) != QG_OK)
         return st;
@@ -431,7 +440,7 @@ qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const i
         return st;
     qg::ConvDesc d{X, W, bias, mult, shift, Y, batch, H, Wd, C, C, KH, KW,
                    stride_h, stride_w, pad_h, pad_w, (int)Ho, (int)Wo,
-                   true, a_zero, b_zero, out_zero, nullptr};
+                   true, a_zero, b_zero, out_zero, nullptr, act_min, act_max};
     return launched(qg::run_dwconv_zp(d, workspace, (hipStream_t)stream));
 }
 

@@ -68,11 +68,13 @@ __device__ __forceinline__ v4i even_odd_split(v4i q)
 // Q31 requantize of one accumulator (MCU conv front-end article,
 // news.rkmt.cn/news/16638, §2.3): x = acc + bias, t = x * mult (64-bit),
 // t += 2^(shift-1), t >>= shift (arithmetic), then the output zero point zo
-// (that article's §3.3; 0 for symmetric outputs) and saturation to int8.
+// (that article's §3.3; 0 for symmetric outputs) and saturation to
+// [lo, hi]: the int8 range, or tighter bounds for a fused activation (ReLU is
+// lo = zo; Voyager quantization article, www.dpshk.com/news/2695434, §3.1).
 // `rnd` is 2^(shift-1), computed once per channel by the caller.  acc + bias
 // is formed modulo 2^32: the asymmetric forms pass accumulators whose
 // compensation terms may wrap, and the true x fits in int32.  y + zo is
-// saturated as y clamped to [-128 - zo, 127 - zo], plus zo.
+// saturated as y clamped to [lo - zo, hi - zo], plus zo.
 // The 64-bit quotient is saturated from its two halves: when the high word is
 // not the sign extension of the low word, |y| >= 2^31 and the result is the
 // bound on y's side whatever zo is.
@@ -87,23 +89,24 @@ __device__ __forceinline__ int wrap_sub(int a, int b)
 }
 
 __device__ __forceinline__ int requant_one(int acc, int bias, int mult, int shift, long long rnd,
-                                           int zo = 0)
+                                           int zo = 0, int lo = -128, int hi = 127)
 {
     const int x = wrap_add(acc, bias);
     const long long y = ((long long)x * (long long)mult + rnd) >> shift;
-    const int lo = (int)y, hi = (int)(y >> 32);
-    const int c = min(max(lo, -128 - zo), 127 - zo) + zo;
-    return hi == (lo >> 31) ? c : ((hi >> 31) ^ 127);
+    const int ylo = (int)y, yhi = (int)(y >> 32);
+    const int c = min(max(ylo, lo - zo), hi - zo) + zo;
+    return yhi == (ylo >> 31) ? c : (yhi < 0 ? lo : hi);
 }
 
 // The same when shift >= 31: |x * mult| < 2^62 then keeps y inside int32, so
 // the low word of the 64-bit shift is y itself.
 __device__ __forceinline__ int requant_one_s31(int acc, int bias, int mult, int shift,
-                                               long long rnd, int zo = 0)
+                                               long long rnd, int zo = 0, int lo = -128,
+                                               int hi = 127)
 {
     const int x = wrap_add(acc, bias);
     const int y = (int)(((long long)x * (long long)mult + rnd) >> shift);
-    return min(max(y, -128 - zo), 127 - zo) + zo;
+    return min(max(y, lo - zo), hi - zo) + zo;
 }
 
 // The same when shift >= 33: with x * mult = H * 2^32 + L (0 <= L < 2^32,
@@ -111,12 +114,13 @@ __device__ __forceinline__ int requant_one_s31(int acc, int bias, int mult, int 
 // (H + 2^(shift-33) + L / 2^32) / 2^(shift-32), and the fraction L / 2^32
 // never changes the floor, so y = (H + 2^(shift-33)) >> (shift-32) exactly.
 // |H| <= 2^30, so the sum stays inside int32.
-__device__ __forceinline__ int requant_one_s33(int acc, int bias, int mult, int shift, int zo = 0)
+__device__ __forceinline__ int requant_one_s33(int acc, int bias, int mult, int shift, int zo = 0,
+                                               int lo = -128, int hi = 127)
 {
     const int x = wrap_add(acc, bias);
     const int h = __mulhi(x, mult);
     const int y = (h + (1 << ((shift - 33) & 31))) >> ((shift - 32) & 31);
-    return min(max(y, -128 - zo), 127 - zo) + zo;
+    return min(max(y, lo - zo), hi - zo) + zo;
 }
 
 __device__ __forceinline__ unsigned pack4_i8(int a, int b, int c, int d)

@@ -69,6 +69,7 @@ struct HaloArgs {
     int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
     int pad4;                  // padding byte (the input zero point) x4
     int a_zero, b_zero, out_zero;  // ZP: the zero points
+    int act_min, act_max;          // ZP: output clamp bounds
 };
 
 __device__ __forceinline__ void drain_and_barrier()
@@ -285,13 +286,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
                 for (int e = 0; e < 4; ++e) {
                     const int x = ZP ? wrap_sub(acc[i][n][e], rt[i]) : acc[i][n][e];
                     const int zo = ZP ? p.out_zero : 0;
+                    const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo);
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo, lo, hi);
                     else if constexpr (TIER == 1)
                         y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
-                                               zo);
+                                               zo, lo, hi);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo);
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
+                                           lo, hi);
                 }
                 const int q = 64 * wave + 16 * i + col;
                 *(unsigned *)(IN + q * 64 + c0) = pack4_i8(y[0], y[1], y[2], y[3]);
@@ -393,6 +396,8 @@ hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s)
     a.a_zero = d.a_zero;
     a.b_zero = d.b_zero;
     a.out_zero = d.out_zero;
+    a.act_min = d.act_min;
+    a.act_max = d.act_max;
     const int lds = (int)halo_lds_bytes(d);
     if (d.asym) {
         if (d.KH == 3)

@@ -54,6 +54,7 @@ struct DwArgs {
     // asymmetric form: the padding byte x4 and the zero points; the 3x3 path
     // takes zb = 0 with `bias` holding bias - za * sum_t w[t][c]
     int pad4, a_zero, b_zero, out_zero;
+    int act_min, act_max;  // output clamp bounds (the int8 range when symmetric)
 };
 
 __device__ __forceinline__ void drain_and_barrier()
@@ -230,13 +231,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
                 for (int e = 0; e < 4; ++e) {
                     const int x = acc[i][n][e];
                     const int zo = ZP ? p.out_zero : 0;
+                    const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo);
+                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo, lo, hi);
                     else if constexpr (TIER == 1)
                         y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
-                                               zo);
+                                               zo, lo, hi);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo);
+                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
+                                           lo, hi);
                 }
                 const int q = 64 * wave + 16 * i + col;
                 *(unsigned *)(IN + q * 64 + cc) = pack4_i8(y[0], y[1], y[2], y[3]);
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
     for (int e = 0; e < 4; ++e) {
         const int s = p.shift[c + e];
         y[e] = requant_one(acc[e], p.bias ? p.bias[c + e] : 0, p.mult[c + e], s,
-                           1ll << ((s - 1) & 63), p.out_zero);
+                           1ll << ((s - 1) & 63), p.out_zero, p.act_min, p.act_max);
     }
     *(unsigned *)(p.Y + pix * p.C + c) = pack4_i8(y[0], y[1], y[2], y[3]);
 }
@@ -379,11 +382,15 @@ hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s)
     a.pw = d.pw;
     a.Ho = d.Ho;
     a.Wo = d.Wo;
+    a.act_min = -128;
+    a.act_max = 127;
     if (d.asym) {
         a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
         a.a_zero = d.a_zero;
         a.b_zero = d.b_zero;
         a.out_zero = d.out_zero;
+        a.act_min = d.act_min;
+        a.act_max = d.act_max;
     }
     if (dw_takes_mfma(d)) {
         a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;

@@ -80,6 +80,7 @@ struct DmaArgs {
     int tiles_m, tiles_n;
     const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
     int out_zero;          // EPI_REQUANT_ZP: output zero point
+    int act_min, act_max;  // EPI_REQUANT_ZP: output clamp bounds
 };
 
 // A 16-byte LDS read is served 16 lanes per cycle over 64 4-byte banks; the
@@ -331,6 +332,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                         const int ml = wm * 128 + i * 32 + (lane & 31);
                         const int rt = ZP ? prm[3][ml] : 0;
                         const int zo = ZP ? p.out_zero : 0;
+                        const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                         int y[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -338,13 +340,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                             if constexpr (ZP)
                                 a = wrap_sub(a, rt);
                             if constexpr (TIER == 2)
-                                y[e] = requant_one_s33(a, b4[e], m4[e], s4[e], zo);
+                                y[e] = requant_one_s33(a, b4[e], m4[e], s4[e], zo, lo, hi);
                             else if constexpr (TIER == 1)
                                 y[e] = requant_one_s31(a, b4[e], m4[e], s4[e],
-                                                       1ll << ((s4[e] - 1) & 63), zo);
+                                                       1ll << ((s4[e] - 1) & 63), zo, lo, hi);
                             else
                                 y[e] = requant_one(a, b4[e], m4[e], s4[e],
-                                                   1ll << ((s4[e] - 1) & 63), zo);
+                                                   1ll << ((s4[e] - 1) & 63), zo, lo, hi);
                         }
                         *(unsigned *)(otile + ml * kOutStride + nl) =
                             pack4_i8(y[0], y[1], y[2], y[3]);
@@ -431,6 +433,8 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     a.tiles_n = (int)((d.N + kBN - 1) / kBN);
     a.rterm = d.rterm;
     a.out_zero = d.out_zero;
+    a.act_min = d.act_min;
+    a.act_max = d.act_max;
     hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     return hipGetLastError();
 }

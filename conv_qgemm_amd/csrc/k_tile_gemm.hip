@@ -56,6 +56,7 @@ struct TileArgs {
     int pad4;              // AL_CONV: padding byte (the input zero point) x4
     const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
     int out_zero;          // EPI_REQUANT_ZP: output zero point
+    int act_min, act_max;  // EPI_REQUANT_ZP: output clamp bounds
 };
 
 constexpr int kThreads = 256;
@@ -279,10 +280,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
                     const v16i &a = acc[j * TM + i];
                     const int rt = ZP && p.rterm ? p.rterm[min(m, p.M - 1)] : 0;
                     const int zo = ZP ? p.out_zero : 0;
+                    const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                     int y[4];
                     for (int e = 0; e < 4; ++e)
                         y[e] = requant_one(wrap_sub(a[4 * q + e] >> ACC_SHIFT, rt), bia[e], mul[e],
-                                           shf[e], rnd[e], zo);
+                                           shf[e], rnd[e], zo, lo, hi);
                     if (m < p.M) {
                         int8_t *dst = C + (int64_t)m * p.ldc + n;
                         if (vec) {
@@ -351,6 +353,8 @@ static TileArgs gemm_args(const GemmDesc &d)
     a.K = (int)d.K;
     a.rterm = d.rterm;
     a.out_zero = d.out_zero;
+    a.act_min = d.act_min;
+    a.act_max = d.act_max;
     return a;
 }
 
@@ -437,6 +441,8 @@ hipError_t launch_conv_nhwc(const ConvDesc &d, hipStream_t s)
     a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
     a.rterm = d.rterm;
     a.out_zero = d.out_zero;
+    a.act_min = d.act_min;
+    a.act_max = d.act_max;
     if (d.asym) {
         if (d.C_out <= 64)
             return run_tile<OP_S8, OP_S8, EPI_REQUANT_ZP, AL_CONV, 256, 64, 64, 4, 1>(a, s);

@@ -27,6 +27,8 @@ struct GemmDesc {
     int out_zero;
     // W4A8: the int4 weights are packed high nibble first
     bool msb_first;
+    // asymmetric form: output clamp bounds (fused activation)
+    int act_min, act_max;
 };
 
 // One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,
@@ -45,6 +47,7 @@ struct ConvDesc {
     bool asym;
     int a_zero, b_zero, out_zero;
     const int32_t *rterm;
+    int act_min, act_max;  // asymmetric form: output clamp bounds
 };
 
 hipError_t launch_s8s8_requant(const GemmDesc &d, hipStream_t s);

@@ -64,17 +64,17 @@ def _load():
     Z = ctypes.c_size_t
     lib.qgemm_s8s8_requant_zp_workspace_size.argtypes = [I64, I64]
     lib.qgemm_s8s8_requant_zp_workspace_size.restype = Z
-    lib.qgemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, P, I64, I64,
-                                          I64, I64, P, Z, P]
+    lib.qgemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, P,
+                                          I64, I64, I64, I64, P, Z, P]
     lib.qgemm_s8s8_requant_zp.restype = S
     lib.qconv2d_nhwc_s8_requant_zp_workspace_size.argtypes = [I32] * 10
     lib.qconv2d_nhwc_s8_requant_zp_workspace_size.restype = Z
-    lib.qconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + [I32] * 11 + \
-        [P, Z, P]
+    lib.qconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P] + \
+        [I32] * 11 + [P, Z, P]
     lib.qconv2d_nhwc_s8_requant_zp.restype = S
     lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size.argtypes = [I32]
     lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size.restype = Z
-    lib.qdwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, P] + \
+    lib.qdwconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P] + \
         [I32] * 10 + [P, Z, P]
     lib.qdwconv2d_nhwc_s8_requant_zp.restype = S
     lib.qg_status_string.argtypes = [S]
@@ -331,9 +331,10 @@ def _workspace(ws, need, device):
 
 
 def qgemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, C=None,
-                          workspace=None, stream=None):
+                          workspace=None, stream=None, act=(-128, 127)):
     """Asymmetric int8 GEMM: C = requant(sum_k (A - a_zero)(B - b_zero)) +
-    out_zero, saturated to int8.  A int8 [M, K], B int8 [N, K]."""
+    out_zero, saturated to [act[0], act[1]] (the int8 range by default;
+    (out_zero, 127) is a fused ReLU).  A int8 [M, K], B int8 [N, K]."""
     _mat(A, torch.int8, "A")
     _mat(B, torch.int8, "B")
     M, K = A.shape
@@ -347,17 +348,18 @@ def qgemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, C=N
     st = lib.qgemm_s8s8_requant_zp(_ptr(A), A.stride(0), _ptr(B), B.stride(0),
                                    _ptr(_vec(bias, N, "bias")), _ptr(_vec(mult, N, "mult")),
                                    _ptr(_vec(shift, N, "shift")), int(a_zero), int(b_zero),
-                                   int(out_zero), _ptr(C), C.stride(0), M, N, K, _ptr(ws),
-                                   ws.numel(), _stream(stream))
+                                   int(out_zero), int(act[0]), int(act[1]), _ptr(C), C.stride(0),
+                                   M, N, K, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "qgemm_s8s8_requant_zp")
     return C
 
 
 def qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero, stride=(1, 1),
-                               pad=(1, 1), Y=None, workspace=None, stream=None):
+                               pad=(1, 1), Y=None, workspace=None, stream=None, act=(-128, 127)):
     """Asymmetric NHWC int8 conv: padding holds a_zero, products are
-    (X - a_zero)(W - b_zero), the output gets out_zero before the int8
-    saturation.  X [batch, H, W, C_in], W [C_out, KH, KW, C_in]."""
+    (X - a_zero)(W - b_zero), the output gets out_zero before the
+    saturation to [act[0], act[1]].  X [batch, H, W, C_in],
+    W [C_out, KH, KW, C_in]."""
     if X.dtype != torch.int8 or W.dtype != torch.int8:
         raise TypeError("X and W must be int8")
     if X.dim() != 4 or W.dim() != 4 or not X.is_contiguous() or not W.is_contiguous():
@@ -382,7 +384,8 @@ def qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero
     st = lib.qconv2d_nhwc_s8_requant_zp(_ptr(X), _ptr(W), _ptr(_vec(bias, C_out, "bias")),
                                         _ptr(_vec(mult, C_out, "mult")),
                                         _ptr(_vec(shift, C_out, "shift")), int(a_zero),
-                                        int(b_zero), int(out_zero), _ptr(Y), batch, H, Wd, C_in,
+                                        int(b_zero), int(out_zero), int(act[0]), int(act[1]),
+                                        _ptr(Y), batch, H, Wd, C_in,
                                         C_out, KH, KW, stride[0], stride[1], pad[0], pad[1],
                                         _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "qconv2d_nhwc_s8_requant_zp")
@@ -390,7 +393,8 @@ def qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero
 
 
 def qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_zero,
-                                 stride=(1, 1), pad=(1, 1), Y=None, workspace=None, stream=None):
+                                 stride=(1, 1), pad=(1, 1), Y=None, workspace=None, stream=None,
+                                 act=(-128, 127)):
     """Asymmetric depthwise NHWC int8 conv (W [KH, KW, C]); zero points as
     for qconv2d_nhwc_s8_requant_zp."""
     if X.dtype != torch.int8 or W.dtype != torch.int8:
@@ -413,7 +417,8 @@ def qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, a_zero, b_zero, out_ze
     st = lib.qdwconv2d_nhwc_s8_requant_zp(_ptr(X), _ptr(W), _ptr(_vec(bias, C, "bias")),
                                           _ptr(_vec(mult, C, "mult")),
                                           _ptr(_vec(shift, C, "shift")), int(a_zero),
-                                          int(b_zero), int(out_zero), _ptr(Y), batch, H, Wd, C,
+                                          int(b_zero), int(out_zero), int(act[0]), int(act[1]),
+                                          _ptr(Y), batch, H, Wd, C,
                                           KH, KW, stride[0], stride[1], pad[0], pad[1],
                                           _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "qdwconv2d_nhwc_s8_requant_zp")

@@ -205,15 +205,18 @@ qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, i
                            void *stream);
 
 /*
- * Asymmetric (zero-point) forms.  A code Q stands for (Q - zero_point) *
- * scale (Voyager quantization article, www.dpshk.com/news/2695434, §1.1), so
- * with per-tensor zero points a_zero (activations), b_zero (weights) and
- * out_zero (output), all in [-128, 127]:
+ * Asymmetric (zero-point) forms with a fused activation clamp.  A code Q
+ * stands for (Q - zero_point) * scale (Voyager quantization article,
+ * www.dpshk.com/news/2695434, §1.1), so with per-tensor zero points a_zero
+ * (activations), b_zero (weights) and out_zero (output), all in [-128, 127]:
  *   acc = sum_k (A[m][k] - a_zero) * (B[n][k] - b_zero)        (GEMM)
  *   acc = sum over taps and input channels of (X - a_zero) * (W - b_zero),
  *         positions outside the image holding a_zero             (convs)
- *   out = clamp(((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero
- *         saturated to int8 (the add before the saturation)
+ *   out = (((acc + bias) * mult + 2^(shift-1)) >> shift) + out_zero,
+ *         saturated to [act_min, act_max] (the zero point added first)
+ * with -128 <= act_min <= act_max <= 127: (-128, 127) is the plain int8
+ * saturation and (out_zero, 127) a fused ReLU (the Voyager article's §3.1
+ * fuses GEMM + bias + activation into one operator).
  * (INT4 GEMM article §4.1 for zero points on both operands; MCU conv
  * front-end article §2.3 for padding with the input zero point and §3.3 for
  * the output zero point.)  Layouts, strides, alignment and the other
@@ -226,14 +229,15 @@ qg_status qquant_per_token(const void *X, int32_t dtype, int64_t ldx, void *Q, i
  * call's stream, ahead of the main kernel, and keeps nothing between calls.
  * Calls that share a workspace must be ordered (one stream).  The size
  * functions return 0 for shapes the call rejects.  Errors as above;
- * QG_ERR_NULLPTR for a NULL workspace, QG_ERR_INVALID for a zero point out
- * of range or a workspace that is too small or misaligned.
+ * QG_ERR_NULLPTR for a NULL workspace, QG_ERR_INVALID for a zero point or
+ * clamp bound out of range or a workspace that is too small or misaligned.
  */
 size_t qgemm_s8s8_requant_zp_workspace_size(int64_t M, int64_t N);
 qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
                                 const int32_t *bias, const int32_t *mult, const int32_t *shift,
-                                int32_t a_zero, int32_t b_zero, int32_t out_zero, int8_t *C,
-                                int64_t ldc, int64_t M, int64_t N, int64_t K, void *workspace,
+                                int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                int32_t act_min, int32_t act_max, int8_t *C, int64_t ldc,
+                                int64_t M, int64_t N, int64_t K, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
 size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32_t Wd,
@@ -242,7 +246,8 @@ size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32
                                                  int32_t pad_h, int32_t pad_w);
 qg_status qconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
                                      const int32_t *mult, const int32_t *shift, int32_t a_zero,
-                                     int32_t b_zero, int32_t out_zero, int8_t *Y, int32_t batch,
+                                     int32_t b_zero, int32_t out_zero, int32_t act_min,
+                                     int32_t act_max, int8_t *Y, int32_t batch,
                                      int32_t H, int32_t Wd, int32_t C_in, int32_t C_out,
                                      int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
                                      int32_t pad_h, int32_t pad_w, void *workspace,
@@ -252,6 +257,7 @@ size_t qdwconv2d_nhwc_s8_requant_zp_workspace_size(int32_t C);
 qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const int32_t *bias,
                                        const int32_t *mult, const int32_t *shift,
                                        int32_t a_zero, int32_t b_zero, int32_t out_zero,
+                                       int32_t act_min, int32_t act_max,
                                        int8_t *Y, int32_t batch, int32_t H, int32_t Wd,
                                        int32_t C, int32_t KH, int32_t KW, int32_t stride_h,
                                        int32_t stride_w, int32_t pad_h, int32_t pad_w,

@@ -98,23 +98,24 @@ def qt(qg, X=P, dtype=0, ldx=64, Q=P, ldq=64, scale=P, M=8, K=64, clip=1.0, bits
 WS = 0x20000  # fake workspace address
 
 
-def s8z(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, C=P, ldc=64,
-        M=32, N=64, K=64, ws=WS, wsb=1 << 20):
-    return qg.lib.qgemm_s8s8_requant_zp(A, lda, B, ldb, bias, mult, shift, za, zb, zo, C, ldc, M,
-                                        N, K, ws, wsb, None)
+def s8z(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, lo=-128,
+        hi=127, C=P, ldc=64, M=32, N=64, K=64, ws=WS, wsb=1 << 20):
+    return qg.lib.qgemm_s8s8_requant_zp(A, lda, B, ldb, bias, mult, shift, za, zb, zo, lo, hi, C,
+                                        ldc, M, N, K, ws, wsb, None)
 
 
-def cvz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, Y=P, batch=1, H=8, Wd=8,
-        C_in=16, C_out=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
-    return qg.lib.qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, Y, batch, H,
-                                             Wd, C_in, C_out, KH, KW, sh, sw, ph, pw, ws, wsb,
-                                             None)
+def cvz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, lo=-128, hi=127, Y=P, batch=1,
+        H=8, Wd=8, C_in=16, C_out=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
+    return qg.lib.qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, lo, hi, Y,
+                                             batch, H, Wd, C_in, C_out, KH, KW, sh, sw, ph, pw,
+                                             ws, wsb, None)
 
 
-def dwz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, Y=P, batch=1, H=8, Wd=8,
-        C=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
-    return qg.lib.qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, Y, batch, H,
-                                               Wd, C, KH, KW, sh, sw, ph, pw, ws, wsb, None)
+def dwz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, lo=-128, hi=127, Y=P, batch=1,
+        H=8, Wd=8, C=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
+    return qg.lib.qdwconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, lo, hi, Y,
+                                               batch, H, Wd, C, KH, KW, sh, sw, ph, pw, ws, wsb,
+                                               None)
 
 
 def test_nullptr(qg):
@@ -233,6 +234,9 @@ def test_invalid_zero_point_forms(qg):
             assert f(qg, **{kw: 128}) == E, (f.__name__, kw)
             assert f(qg, **{kw: -129}) == E, (f.__name__, kw)
         assert f(qg, ws=WS + 8) == E             # misaligned workspace
+        assert f(qg, lo=10, hi=9) == E           # empty clamp range
+        assert f(qg, lo=-129) == E
+        assert f(qg, hi=128) == E
     # workspace smaller than the size function asks for
     need = qg.lib.qgemm_s8s8_requant_zp_workspace_size(32, 64)
     assert need == 256 + 256
@@ -268,6 +272,7 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert cvz(qg) == qg.QG_ERR_NO_DEVICE
     assert dwz(qg) == qg.QG_ERR_NO_DEVICE
     assert s8z(qg, za=-128, zb=127, zo=-128, wsb=512) == qg.QG_ERR_NO_DEVICE
+    assert cvz(qg, zo=7, lo=7, hi=7) == qg.QG_ERR_NO_DEVICE
     assert qt(qg, dtype=2, bits=4, ldx=72, ldq=80, scale=P + 4, clip=0.25) == qg.QG_ERR_NO_DEVICE
 
 

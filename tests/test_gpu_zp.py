@@ -62,6 +62,22 @@ def test_gemm_zp(qg, orc, M, N, K, za, zb, zo):
     assert np.array_equal(got if rows is None else got[rows], want)
 
 
+@pytest.mark.parametrize("M,N,K", [(70, 90, 160), (4096, 2048, 256)])
+@pytest.mark.parametrize("act", [(5, 127), (-40, 60), (-128, -100), (9, 9)])
+def test_gemm_zp_fused_activation(qg, orc, M, N, K, act):
+    """ReLU at the output zero point (5, 127), a bounded clamp, a range at
+    the low end, and a single value; on the tile and the ring kernel."""
+    _say("gemm zp act", M, N, K, act)
+    d = datagen.gemm_s8s8(M, N, K, seed=M + K, shift=(38, 44))
+    C = qg.qgemm_s8s8_requant_zp(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                 dev(d["shift"]), -9, 4, 5, act=act)
+    rows = None if M <= 512 else np.array([0, 77, 2048, 4095])
+    want = orc.gemm_s8s8_requant_zp(d["A"], d["B"], d["bias"], d["mult"], d["shift"], -9, 4, 5,
+                                    rows=rows, act=act)
+    got = C.cpu().numpy()
+    assert np.array_equal(got if rows is None else got[rows], want)
+
+
 def test_gemm_zp_saturating_and_no_bias(qg, orc):
     d = datagen.gemm_s8s8(70, 90, 160, seed=5, shift=(31, 40))
     C = qg.qgemm_s8s8_requant_zp(dev(d["A"]), dev(d["B"]), None, dev(d["mult"]), dev(d["shift"]),
@@ -148,6 +164,20 @@ def test_conv_zp(qg, orc, geom, za, zb, zo):
     assert np.array_equal(Y.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("geom", [CONV_GEOMS[0], CONV_GEOMS[3]])
+@pytest.mark.parametrize("act", [(-30, 127), (-60, 20)])
+def test_conv_zp_fused_activation(qg, orc, geom, act):
+    b, H, W, C_in, C_out, KH, KW, stride, pad = geom
+    _say("conv zp act", geom, act)
+    d = datagen.conv_nhwc(b, H, W, C_in, C_out, KH, KW, seed=H + W, shift=(38, 45))
+    Y = qg.qconv2d_nhwc_s8_requant_zp(dev(d["X"]), dev(d["W"]), dev(d["bias"]), dev(d["mult"]),
+                                      dev(d["shift"]), 11, -3, -30, stride=stride, pad=pad,
+                                      act=act)
+    want = orc.conv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"], 11, -3,
+                                         -30, stride=stride, pad=pad, act=act)
+    assert np.array_equal(Y.cpu().numpy(), want)
+
+
 def test_conv_zp_workload_full(qg, orc):
     """The 32x56x56x64 -> 64 3x3 layer with zero points on input, weights and
     output, every output compared."""
@@ -187,6 +217,19 @@ def test_dwconv_zp(qg, orc, geom, za, zb, zo):
                                         dev(d["shift"]), za, zb, zo, stride=stride, pad=pad)
     want = orc.dwconv2d_nhwc_s8_requant_zp(X, Wt, d["bias"], d["mult"], d["shift"], za, zb, zo,
                                            stride=stride, pad=pad)
+    assert np.array_equal(Y.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("geom", [DW_GEOMS[0], DW_GEOMS[3]])
+def test_dwconv_zp_relu(qg, orc, geom):
+    """ReLU at the output zero point on the matrix-core and the direct path."""
+    b, H, W, C, KH, KW, stride, pad = geom
+    d = datagen.dwconv_nhwc(b, H, W, C, KH, KW, seed=C, shift=(30, 37))
+    Y = qg.qdwconv2d_nhwc_s8_requant_zp(dev(d["X"]), dev(d["W"]), dev(d["bias"]), dev(d["mult"]),
+                                        dev(d["shift"]), 6, 0, -12, stride=stride, pad=pad,
+                                        act=(-12, 127))
+    want = orc.dwconv2d_nhwc_s8_requant_zp(d["X"], d["W"], d["bias"], d["mult"], d["shift"], 6, 0,
+                                           -12, stride=stride, pad=pad, act=(-12, 127))
     assert np.array_equal(Y.cpu().numpy(), want)
 
 
