@@ -106,6 +106,10 @@ def _load():
     lib.orc_gemm_s4s4_i32_msb.restype = ctypes.c_int
     lib.orc_gemm_w4a8_requant_msb.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, P, I64]
     lib.orc_gemm_w4a8_requant_msb.restype = ctypes.c_int
+    lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_f32_to_f16.restype = ctypes.c_uint16
+    lib.orc_gemm_s4s4_f16.argtypes = [P, I64, P, I64, P, P, P, I64, I64, I64, P, I64]
+    lib.orc_gemm_s4s4_f16.restype = ctypes.c_int
     lib.orc_quant_per_token.argtypes = [P, ctypes.c_int, I64, I64, I64, ctypes.c_float,
                                          ctypes.c_int, P, I64, P]
     lib.orc_quant_per_token.restype = ctypes.c_int
@@ -279,6 +283,31 @@ def gemm_s4s4_i32(Ap, Bp, rows=None, msb_first=False):
                                    N, K, _ptr(r), nr)
     _check(st, "gemm_s4s4_i32")
     return C
+
+
+def f32_to_f16(x) -> int:
+    """binary16 bit pattern of binary32 x, rounded to nearest, ties to even."""
+    return int(_load().orc_f32_to_f16(float(np.float32(x))))
+
+
+def gemm_s4s4_f16(Ap, Bp, scale_a=None, scale_b=None, rows=None):
+    """packed int4 A [M][K/2] x packed int4 B [N][K/2] -> binary16 C (as a
+    float16 array): fp16(fp32(acc) * scale_a[m] * scale_b[n]), scales
+    optional."""
+    Ap = _c(Ap, np.uint8)
+    Bp = _c(Bp, np.uint8)
+    M, Kh = Ap.shape
+    N = Bp.shape[0]
+    assert Bp.shape[1] == Kh
+    K = 2 * Kh
+    sa = None if scale_a is None else _c(scale_a, np.float32)
+    sb = None if scale_b is None else _c(scale_b, np.float32)
+    r, nr = _rows(rows, M)
+    C = np.zeros((nr, N), dtype=np.uint16)
+    st = _load().orc_gemm_s4s4_f16(Ap.ctypes.data, K, Bp.ctypes.data, K, _ptr(sa), _ptr(sb),
+                                   C.ctypes.data, N, N, K, _ptr(r), nr)
+    _check(st, "gemm_s4s4_f16")
+    return C.view(np.float16)
 
 
 def conv_out_size(n, k, stride, pad) -> int:

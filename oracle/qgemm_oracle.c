@@ -54,6 +54,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
+#include <string.h>
 #include <omp.h>
 
 #define ORC_OK 0
@@ -685,6 +686,70 @@ int orc_gemm_w4a8_requant_msb(const int8_t *A, int64_t lda, const uint8_t *B, in
             int8_t y = 0;
             status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[n], &y);
             C[r * ldc + n] = y;
+        }
+    }
+    return status;
+}
+
+/* ---- INT4 x INT4 with a binary16 output ([INT4-GEMM] §6: a variant of
+ * the GEMM whose C is FP16, converted from the int32 accumulator).  The
+ * accumulator goes to binary32 (exact: |acc| < 2^24 under the int4 K
+ * bound), is multiplied by the optional per-row and per-column scales in
+ * that order, each product rounded to binary32, and is rounded to binary16
+ * to nearest, ties to even; magnitudes from 65520 up become infinities.
+ * Without scales this is the page's plain conversion of the accumulator. ---- */
+
+/* binary32 -> binary16, round to nearest, ties to even (bit patterns). */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x7F800000u)                       /* infinity or NaN */
+        return (uint16_t)(sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u));
+    if (a >= 0x477FF000u)                       /* >= 65520: rounds past 65504 */
+        return (uint16_t)(sign | 0x7C00u);
+    const int e = (int)(a >> 23) - 127;         /* unbiased exponent */
+    const uint32_t full = (a & 0x7FFFFFu) | 0x800000u;  /* 24-bit significand */
+    int shift;                                  /* significand bits to drop */
+    uint32_t base;                              /* exponent field of the result */
+    if (e >= -14) {                             /* normal binary16 */
+        shift = 13;
+        base = (uint32_t)(e + 15) << 10;
+    } else {                                    /* subnormal: units of 2^-24 */
+        if (e < -25)
+            return sign;                        /* below half the smallest step */
+        shift = -e - 1;                         /* 14 .. 24 */
+        base = 0;
+    }
+    uint32_t h = (full >> shift) & (e >= -14 ? 0x3FFu : 0xFFFFFFu);
+    const uint32_t rem = full & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    uint32_t r = base + h;
+    if (rem > half || (rem == half && (r & 1u)))
+        r += 1;                                 /* a carry moves into the exponent */
+    return (uint16_t)(sign | r);
+}
+
+int orc_gemm_s4s4_f16(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                      const float *scale_a, const float *scale_b, uint16_t *C, int64_t ldc,
+                      int64_t N, int64_t K, const int64_t *rows, int64_t nrows)
+{
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = dot_any(4, A, lda, m, 4, B, ldb, n, K);
+            if (acc <= -(1 << 24) || acc >= (1 << 24))
+                status |= ORC_E_RANGE;
+            float t = (float)acc;
+            if (scale_a)
+                t = t * scale_a[m];
+            if (scale_b)
+                t = t * scale_b[n];
+            C[r * ldc + n] = orc_f32_to_f16(t);
         }
     }
     return status;

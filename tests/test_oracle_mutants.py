@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_int4.py", "tests/test_oracle_requant.py",
              "tests/test_oracle_gemm.py", "tests/test_oracle_conv.py",
              "tests/test_oracle_dwconv.py", "tests/test_oracle_quant.py",
-             "tests/test_oracle_zp.py"]
+             "tests/test_oracle_zp.py", "tests/test_oracle_f16.py"]
 
 MUTANTS = {
     "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
@@ -67,6 +67,11 @@ MUTANTS = {
                              "const int64_t w = Wt[t * C + c];\n        acc += (x - za) * w;"),
     "msb_nibble_order": ("const int code = (i % 2 == 0) ? (byte >> 4) : (byte & 0x0F);",
                          "const int code = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);"),
+    "f16_ties_up": ("if (rem > half || (rem == half && (r & 1u)))", "if (rem >= half)"),
+    "f16_truncate": ("if (rem > half || (rem == half && (r & 1u)))", "if (0)"),
+    "f16_scale_b_dropped": ("            if (scale_b)\n                t = t * scale_b[n];",
+                            "            if (scale_b)\n                t = t;"),
+    "f16_overflow_check_dropped": ("if (a >= 0x477FF000u)", "if (0)"),
     "dw_tap_dropped": ("for (int64_t kw = 0; kw < KW; ++kw) {\n            const int64_t iw",
                        "for (int64_t kw = 0; kw + 1 < KW; ++kw) {\n            const int64_t iw"),
 }
@@ -108,6 +113,6 @@ def test_ubsan_build_runs_clean(tmp_path):
     env = dict(os.environ, QG_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_requant.py", "tests/test_oracle_conv.py",
-                        "tests/test_oracle_zp.py"],
+                        "tests/test_oracle_zp.py", "tests/test_oracle_f16.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
