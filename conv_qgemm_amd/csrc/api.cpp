@@ -196,6 +196,25 @@ qg_status qgemm_s4s4_i32(const uint8_t *A, int64_t lda, const uint8_t *B, int64_
     return launched(qg::launch_s4s4_i32(d, (hipStream_t)stream));
 }
 
+qg_status qgemm_s4s4_f16(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                         const float *scale_a, const float *scale_b, uint16_t *C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!A || !B || !C)
+        return QG_ERR_NULLPTR;
+    qg_status st = check_gemm(A, lda, true, B, ldb, true, C, ldc, 2, M, N, K, QG_S4S4_MAX_K);
+    if (st != QG_OK)
+        return st;
+    if ((scale_a && !aligned16(scale_a)) || (scale_b && !aligned16(scale_b)))
+        return QG_ERR_INVALID;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    qg::GemmDesc d{A, lda / 2, B, ldb / 2, nullptr, nullptr, nullptr, C, ldc, M, N, K, cus,
+                   nullptr, 0, false, 0, 0, scale_a, scale_b};
+    return launched(qg::launch_s4s4_f16(d, (hipStream_t)stream));
+}
+
 qg_status qgemm_w4a8_requant(const int8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                              const int32_t *bias, const int32_t *mult, const int32_t *shift,
                              int8_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,

@@ -123,6 +123,16 @@ __device__ __forceinline__ int requant_one_s33(int acc, int bias, int mult, int 
     return min(max(y, lo - zo), hi - zo) + zo;
 }
 
+// binary16 bits of a binary32 value, rounded to nearest even.  The empty asm
+// pins u as a binary32 register value: without it the compiler folds the
+// product that produced u into v_fma_mixlo_f16, which rounds once (to
+// binary16) where the definition rounds twice (to binary32, then binary16).
+__device__ __forceinline__ unsigned short f32_to_f16_bits(float u)
+{
+    asm volatile("" : "+v"(u));
+    return __builtin_bit_cast(unsigned short, (_Float16)u);
+}
+
 __device__ __forceinline__ unsigned pack4_i8(int a, int b, int c, int d)
 {
     return (unsigned)(a & 0xFF) | ((unsigned)(b & 0xFF) << 8) | ((unsigned)(c & 0xFF) << 16) |

@@ -64,7 +64,10 @@ enum { OP_S8 = 8, OP_S4 = 4 };
 // (or null when zb = 0), and the output zero point is added before the int8
 // saturation; all of it modulo 2^32, which gives the true value whenever
 // sum (A - za)(B - zb) + bias fits in int32.
-enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2 };
+// EPI_F16: binary16 output (INT4 GEMM article §6): fp16(fp32(acc) *
+// scale_a[m] * scale_b[n]), the scales optional, each product rounded to
+// binary32, the conversion to nearest even.
+enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2, EPI_F16 = 3 };
 
 struct DmaArgs {
     const uint8_t *A;
@@ -81,6 +84,8 @@ struct DmaArgs {
     const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
     int out_zero;          // EPI_REQUANT_ZP: output zero point
     int act_min, act_max;  // EPI_REQUANT_ZP: output clamp bounds
+    const float *scale_a;  // EPI_F16: per-row scales, or null
+    const float *scale_b;  // EPI_F16: per-column scales, or null
 };
 
 // A 16-byte LDS read is served 16 lanes per cycle over 64 4-byte banks; the
@@ -107,8 +112,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     constexpr int STEPS_PER_READ = KIND == OP_S8 ? 1 : 2;
     constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : 0;
     constexpr int MG = 16 * STEPS_PER_READ;  // MFMAs per read group
-    constexpr bool RQ = EPI != EPI_I32;
+    constexpr bool RQ = EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP;
     constexpr bool ZP = EPI == EPI_REQUANT_ZP;
+    constexpr bool F16 = EPI == EPI_F16;
 
     // one LDS object: the operand ring, then the per-column bias / multiplier
     // / shift of this tile's 256 output columns and the per-row term of its
@@ -146,6 +152,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     if constexpr (ZP) {
         if (p.rterm)
             pr = p.rterm[min(m0 + tid, p.M - 1)];
+    }
+    if constexpr (F16) {
+        // column and row scales of the tile, as bit patterns (1.0 if absent)
+        pb = __float_as_int(p.scale_b ? p.scale_b[min(n0 + tid, p.N - 1)] : 1.0f);
+        pr = __float_as_int(p.scale_a ? p.scale_a[min(m0 + tid, p.M - 1)] : 1.0f);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -250,6 +261,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     }
     if constexpr (ZP)
         prm[3][tid] = pr;
+    if constexpr (F16) {
+        prm[0][tid] = pb;
+        prm[3][tid] = pr;
+    }
     wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage + kEarlyLoads>();
     read_group(0, 0, fa[0], fb[0]);
 
@@ -381,6 +396,44 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 }
             }
         }
+    } else if constexpr (F16) {
+        // binary16: 4 adjacent columns of one row per 8-byte store
+        uint16_t *C = (uint16_t *)p.C;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                const int n = n0 + nl;
+                const bool vec = n + 3 < p.N && (p.ldc & 3) == 0;
+                const v4i sb4 = *(const v4i *)&prm[0][nl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ml = wm * 128 + i * 32 + (lane & 31);
+                    const int m = m0 + ml;
+                    const float sa = __int_as_float(prm[3][ml]);
+                    const v16i &a = acc[j * 4 + i];
+                    unsigned short h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
+                        h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
+                    }
+                    if (m < p.M) {
+                        uint16_t *dst = C + (int64_t)m * p.ldc + n;
+                        if (vec) {
+                            v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
+                                     (unsigned)h[2] | ((unsigned)h[3] << 16)};
+                            *(v2u *)dst = w;
+                        } else {
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    dst[e] = h[e];
+                        }
+                    }
+                }
+            }
+        }
     } else {
         // raw int32: 4 adjacent columns of one row per 16-byte store
         int32_t *C = (int32_t *)p.C;
@@ -435,6 +488,8 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     a.out_zero = d.out_zero;
     a.act_min = d.act_min;
     a.act_max = d.act_max;
+    a.scale_a = d.scale_a;
+    a.scale_b = d.scale_b;
     hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -467,6 +522,11 @@ hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s)
 hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s)
 {
     return run<OP_S8, EPI_REQUANT_ZP>(d, s);
+}
+
+hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
+{
+    return run<OP_S4, EPI_F16>(d, s);
 }
 
 }  // namespace qg

@@ -36,7 +36,8 @@ enum { OP_S8 = 8, OP_S4 = 4 };
 // (bias - za * sum_k B + K * za * zb), `rterm` the per-row zb * sum_k A (null
 // when zb = 0), and the output zero point joins before the saturation; the
 // sums wrap modulo 2^32 and give the true value whenever it fits in int32.
-enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2 };
+// EPI_F16: binary16 output, fp16(fp32(acc) * scale_a[m] * scale_b[n]).
+enum { EPI_REQUANT = 0, EPI_I32 = 1, EPI_REQUANT_ZP = 2, EPI_F16 = 3 };
 enum { AL_DENSE = 0, AL_CONV = 1 };
 
 struct TileArgs {
@@ -57,6 +58,8 @@ struct TileArgs {
     const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
     int out_zero;          // EPI_REQUANT_ZP: output zero point
     int act_min, act_max;  // EPI_REQUANT_ZP: output clamp bounds
+    const float *scale_a;  // EPI_F16: per-row scales, or null
+    const float *scale_b;  // EPI_F16: per-column scales, or null
 };
 
 constexpr int kThreads = 256;
@@ -296,6 +299,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
                         }
                     }
                 }
+            } else if constexpr (EPI == EPI_F16) {
+                float sb[4];
+                for (int e = 0; e < 4; ++e)
+                    sb[e] = p.scale_b ? p.scale_b[min(n + e, p.N - 1)] : 1.0f;
+                uint16_t *C = (uint16_t *)p.C;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+                    const float sa = p.scale_a ? p.scale_a[min(m, p.M - 1)] : 1.0f;
+                    const v16i &a = acc[j * TM + i];
+                    unsigned short h[4];
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
+                        h[e] = f32_to_f16_bits(t * sb[e]);
+                    }
+                    if (m < p.M) {
+                        uint16_t *dst = C + (int64_t)m * p.ldc + n;
+                        if (vec) {
+                            v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
+                                     (unsigned)h[2] | ((unsigned)h[3] << 16)};
+                            *(v2u *)dst = w;
+                        } else {
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    dst[e] = h[e];
+                        }
+                    }
+                }
             } else {
                 int32_t *C = (int32_t *)p.C;
 #pragma unroll
@@ -355,6 +386,8 @@ static TileArgs gemm_args(const GemmDesc &d)
     a.out_zero = d.out_zero;
     a.act_min = d.act_min;
     a.act_max = d.act_max;
+    a.scale_a = d.scale_a;
+    a.scale_b = d.scale_b;
     return a;
 }
 
@@ -397,6 +430,13 @@ hipError_t launch_s4s4_i32(const GemmDesc &d, hipStream_t s)
     if (dma_gemm_fits(d, true))
         return launch_s4s4_i32_dma(d, s);
     return run_gemm<OP_S4, OP_S4, EPI_I32, 256>(d, s);
+}
+
+hipError_t launch_s4s4_f16(const GemmDesc &d, hipStream_t s)
+{
+    if (dma_gemm_fits(d, true))
+        return launch_s4s4_f16_dma(d, s);
+    return run_gemm<OP_S4, OP_S4, EPI_F16, 256>(d, s);
 }
 
 hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s)

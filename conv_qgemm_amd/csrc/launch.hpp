@@ -29,6 +29,9 @@ struct GemmDesc {
     bool msb_first;
     // asymmetric form: output clamp bounds (fused activation)
     int act_min, act_max;
+    // binary16 output (launch_s4s4_f16): per-row / per-column scales or null
+    const float *scale_a;
+    const float *scale_b;
 };
 
 // One NHWC conv as an implicit GEMM: M = batch*Ho*Wo pixels, N = C_out,
@@ -61,6 +64,11 @@ bool dma_gemm_fits(const GemmDesc &d, bool int4);
 hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s);
+hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s);
+
+// INT4 x INT4 with a binary16 output: C = fp16(fp32(acc) * scale_a[m] *
+// scale_b[n]) (C is [M][ldc] binary16 bit patterns)
+hipError_t launch_s4s4_f16(const GemmDesc &d, hipStream_t s);
 
 // asymmetric int8 GEMM: the terms come from launch_zp_gemm_terms
 hipError_t launch_s8s8_requant_zp(const GemmDesc &d, hipStream_t s);

@@ -53,6 +53,8 @@ def _load():
     lib.qgemm_s4s4_i32.restype = S
     lib.qgemm_w4a8_requant.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
     lib.qgemm_w4a8_requant.restype = S
+    lib.qgemm_s4s4_f16.argtypes = [P, I64, P, I64, P, P, P, I64, I64, I64, I64, P]
+    lib.qgemm_s4s4_f16.restype = S
     lib.qgemm_w4a8_requant_msb.argtypes = [P, I64, P, I64, P, P, P, P, I64, I64, I64, I64, P]
     lib.qgemm_w4a8_requant_msb.restype = S
     lib.qconv2d_nhwc_s8_requant.argtypes = [P, P, P, P, P, P] + [I32] * 11 + [P]
@@ -85,7 +87,8 @@ def _load():
 
 
 lib = _load()
-EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant", "qgemm_w4a8_requant_msb",
+EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_s4s4_f16", "qgemm_w4a8_requant",
+           "qgemm_w4a8_requant_msb",
            "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qquant_per_token",
            "qgemm_s8s8_requant_zp_workspace_size", "qgemm_s8s8_requant_zp",
            "qconv2d_nhwc_s8_requant_zp_workspace_size", "qconv2d_nhwc_s8_requant_zp",
@@ -181,6 +184,37 @@ def qgemm_s4s4_i32(A, B, C=None, K=None, stream=None):
     st = lib.qgemm_s4s4_i32(_ptr(A), 2 * A.stride(0), _ptr(B), 2 * B.stride(0), _ptr(C),
                             C.stride(0), M, N, K, _stream(stream))
     _check(st, "qgemm_s4s4_i32")
+    return C
+
+
+def _fvec(t, n, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.dim() != 1 or t.numel() < n or t.stride(0) != 1:
+        raise ValueError(f"{name} must be a contiguous float32 vector of length >= {n}")
+    _on_device(t, name)
+    return t
+
+
+def qgemm_s4s4_f16(A, B, scale_a=None, scale_b=None, C=None, K=None, stream=None):
+    """packed int4 A uint8 [M, K/2] x packed int4 B uint8 [N, K/2] -> float16
+    C = fp16(fp32(acc) * scale_a[m] * scale_b[n]); the scales are optional
+    float32 vectors."""
+    _mat(A, torch.uint8, "A")
+    _mat(B, torch.uint8, "B")
+    M = A.shape[0]
+    N = B.shape[0]
+    if K is None:
+        K = 2 * A.shape[1]
+    if 2 * A.shape[1] < K or 2 * B.shape[1] < K:
+        raise ValueError("packed rows shorter than K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    _mat(C, torch.float16, "C")
+    st = lib.qgemm_s4s4_f16(_ptr(A), 2 * A.stride(0), _ptr(B), 2 * B.stride(0),
+                            _ptr(_fvec(scale_a, M, "scale_a")), _ptr(_fvec(scale_b, N, "scale_b")),
+                            _ptr(C), C.stride(0), M, N, K, _stream(stream))
+    _check(st, "qgemm_s4s4_f16")
     return C
 
 

@@ -110,6 +110,24 @@ qg_status qgemm_s4s4_i32(const uint8_t *A, int64_t lda, const uint8_t *B, int64_
                          void *stream);
 
 /*
+ * qgemm_s4s4_f16 -- packed int4 x packed int4 with a binary16 output:
+ *   C[m][n] = fp16(fp32(acc) * scale_a[m] * scale_b[n]),
+ *   acc = sum_k A[m][k] * B[n][k] (exact in binary32 under the K bound), the
+ *   products taken in that order, each rounded to binary32, the result
+ *   rounded to binary16 to nearest, ties to even (65520 and up become
+ *   infinities).  scale_a [M] and scale_b [N] are optional (NULL = 1): with
+ *   neither, C is the accumulator converted to FP16, as the INT4 GEMM
+ *   article's §6 variant does; with them, C is the dequantized product
+ *   (per-token activation scales, per-channel weight scales).
+ *   C     binary16 bit patterns [M][ldc], ldc >= N
+ *   A, B, lda, ldb, M, N, K as for qgemm_s4s4_i32; scale_a / scale_b
+ *   16-byte aligned when given.
+ */
+qg_status qgemm_s4s4_f16(const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                         const float *scale_a, const float *scale_b, uint16_t *C, int64_t ldc,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * qgemm_w4a8_requant -- int8 activations x packed int4 weights, requantized.
  *   A     int8  [M][lda], lda >= K
  *   B     packed int4 [N][ldb/2 bytes], ldb >= K (nibbles)

@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol(qg):
     assert set(names) >= {"qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_w4a8_requant",
                           "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant",
                           "qquant_per_token", "qgemm_s8s8_requant_zp", "qgemm_w4a8_requant_msb",
+                          "qgemm_s4s4_f16",
                           "qconv2d_nhwc_s8_requant_zp", "qdwconv2d_nhwc_s8_requant_zp",
                           "qg_status_string", "qg_version"}
     raw = ctypes.CDLL(qg._LIB_PATH)
@@ -68,6 +69,10 @@ def s8(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=32,
 
 def s4(qg, A=P, lda=64, B=P, ldb=64, C=P, ldc=64, M=32, N=64, K=64):
     return qg.lib.qgemm_s4s4_i32(A, lda, B, ldb, C, ldc, M, N, K, None)
+
+
+def s4h(qg, A=P, lda=64, B=P, ldb=64, sa=P, sb=P, C=P, ldc=64, M=32, N=64, K=64):
+    return qg.lib.qgemm_s4s4_f16(A, lda, B, ldb, sa, sb, C, ldc, M, N, K, None)
 
 
 def w4(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, C=P, ldc=64, M=16, N=64, K=64):
@@ -126,6 +131,7 @@ def test_nullptr(qg):
         assert w4m(qg, **{kw: NULL}) == E, kw
     for kw in ("A", "B", "C"):
         assert s4(qg, **{kw: NULL}) == E, kw
+        assert s4h(qg, **{kw: NULL}) == E, kw
     for kw in ("X", "W", "Y", "mult", "shift"):
         assert cv(qg, **{kw: NULL}) == E, kw
         assert dw(qg, **{kw: NULL}) == E, kw
@@ -140,7 +146,7 @@ def test_nullptr(qg):
 
 def test_invalid_gemm_sizes(qg):
     E = qg.QG_ERR_INVALID
-    for f in (s8, s4, w4, w4m):
+    for f in (s8, s4, s4h, w4, w4m):
         assert f(qg, M=0) == E
         assert f(qg, N=0) == E
         assert f(qg, K=0) == E
@@ -161,6 +167,11 @@ def test_invalid_gemm_sizes(qg):
     # int4 K bounds keep the scaled int32 sums exact
     big = qg.QG_S4S4_MAX_K + 32
     assert s4(qg, K=big, lda=big, ldb=big) == E
+    assert s4h(qg, K=big, lda=big, ldb=big) == E
+    assert s4h(qg, K=48, lda=64, ldb=64) == E
+    assert s4h(qg, sa=P + 4) == E           # scales 16-byte aligned
+    assert s4h(qg, sb=P + 8) == E
+    assert s4h(qg, C=P + 2) == E
     assert w4(qg, K=big, lda=big, ldb=big) == E
     assert w4m(qg, K=big, lda=big, ldb=big) == E
 
@@ -265,6 +276,8 @@ def test_valid_call_without_gpu_reports_no_device(qg):
     assert s4(qg) == qg.QG_ERR_NO_DEVICE
     assert w4(qg) == qg.QG_ERR_NO_DEVICE
     assert w4m(qg) == qg.QG_ERR_NO_DEVICE
+    assert s4h(qg) == qg.QG_ERR_NO_DEVICE
+    assert s4h(qg, sa=NULL, sb=NULL, ldc=66) == qg.QG_ERR_NO_DEVICE  # scales optional
     assert cv(qg) == qg.QG_ERR_NO_DEVICE
     assert dw(qg) == qg.QG_ERR_NO_DEVICE
     assert qt(qg) == qg.QG_ERR_NO_DEVICE

@@ -31,8 +31,8 @@ def _kernels(asm):
     return out
 
 
-# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize
-N_INSTANTIATIONS = 3
+# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize, s4s4 binary16
+N_INSTANTIATIONS = 4
 
 
 def _nonempty(ks):
@@ -73,3 +73,18 @@ def test_accumulators_not_spilled(asm):
         m = re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", body)
         if m:
             assert int(m.group(1)) < 256, name
+
+
+@pytest.mark.parametrize("src", ["k_gemm_dma.hip", "k_tile_gemm.hip"])
+def test_binary16_output_rounds_twice(tmp_path, src):
+    """The binary16 epilogue rounds the scaled product to binary32 and then
+    to binary16.  A mixed-precision FMA (v_fma_mix*/v_mad_mix*) would round
+    once and differ from the definition in rare cases."""
+    from conv_qgemm_amd import build
+    out = tmp_path / (src + ".s")
+    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S",
+           os.path.join(ROOT, "conv_qgemm_amd", "csrc", src), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = out.read_text()
+    assert "v_cvt_f16_f32" in text
+    assert not re.search(r"v_(fma|mad)_mix", text)

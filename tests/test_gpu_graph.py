@@ -178,6 +178,21 @@ def test_graph_conv_zp(qg, C_in):
         workspace=d["ws"]))
 
 
+def test_graph_s4s4_f16(qg):
+    import torch
+    g = np.random.default_rng(0)
+    sa = torch.from_numpy(g.uniform(1e-3, 1e-2, 64).astype(np.float32)).cuda()
+    sb = torch.from_numpy(g.uniform(1e-3, 1e-2, 80).astype(np.float32)).cuda()
+
+    def make(seed):
+        h = datagen.gemm_s4s4(64, 80, 256, seed)
+        d = {k: torch.from_numpy(v).cuda() for k, v in h.items()}
+        d["out"] = torch.empty((64, 80), dtype=torch.float16, device="cuda")
+        return d
+
+    _run_graph_case(torch, make, lambda d: qg.qgemm_s4s4_f16(d["A"], d["B"], sa, sb, C=d["out"]))
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 def test_graph_quant(qg, bits):
     import torch
