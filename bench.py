@@ -6,6 +6,7 @@ One step is one call of every entry point on its workload:
   s4s4       qgemm_s4s4_i32      M=N=K=4096, raw int32 out
   conv3x3    qconv2d_nhwc_s8_requant  batch 32, 56x56, 64->64, 3x3 s1 p1
   w4a8       qgemm_w4a8_requant  M=16 tokens, K=8192, N=28672 (skinny)
+  w4a8_prefill  qgemm_w4a8_requant  M=2048 tokens, same weights (tiled)
   dw3x3      qdwconv2d_nhwc_s8_requant  batch 32, 56x56, 64 channels, 3x3 s1 p1
   quant_a8   qquant_per_token    8192 tokens x 8192 channels, bfloat16 -> int8
              codes + float32 scales (the s8s8 A operand; no integer ops)
@@ -40,11 +41,11 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
-ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "conv3x3_zp", "s4s4", "s8s8",
-         "s8s8_zp"]
+ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "conv3x3_zp", "s4s4",
+         "w4a8_prefill", "s8s8", "s8s8_zp"]
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
 ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "conv3x3_zp": 40, "dw3x3": 40,
-          "quant_a8": 3, "w4a8": 5, "s8s8": 3, "s8s8_zp": 3}
+          "quant_a8": 3, "w4a8": 5, "w4a8_prefill": 3, "s8s8": 3, "s8s8_zp": 3}
 KERNEL_SOURCES = {
     "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
@@ -54,6 +55,7 @@ KERNEL_SOURCES = {
     "dw3x3": "conv_qgemm_amd/csrc/k_dwconv.hip",
     "quant_a8": "conv_qgemm_amd/csrc/k_quant.hip",
     "s8s8_zp": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
+    "w4a8_prefill": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
     "conv3x3_zp": "conv_qgemm_amd/csrc/k_conv_halo.hip",
 }
 
@@ -171,7 +173,7 @@ class Case:
         q = self.q
         if self.name == "s4s4":
             return q.qgemm_s4s4_i32(s["A"], s["B"], C=s["C"])
-        if self.name == "w4a8":
+        if self.name in ("w4a8", "w4a8_prefill"):
             return q.qgemm_w4a8_requant(s["A"], s["B"], s["bias"], s["mult"], s["shift"], C=s["C"])
         if self.name == "s8s8_zp":
             za, zb, zo = shape_of(self.name)["zp"]
@@ -222,6 +224,10 @@ def cpu_baseline(names, frac=16):
         elif w["kind"] == "s4s4":
             rows = np.arange(0, w["M"], frac)
             oracle.gemm_s4s4_i32(d["A"], d["B"], rows=rows)
+            part = len(rows) / w["M"]
+        elif w["kind"] == "w4a8" and w["M"] > 64:
+            rows = np.arange(0, w["M"], frac * 16)
+            oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
             part = len(rows) / w["M"]
         elif w["kind"] == "w4a8":
             cols = np.arange(0, w["N"], frac)
@@ -445,7 +451,8 @@ def main():
     # compensation-sum pass in front of theirs)
     single = [n for n in per if not n.endswith("_zp")] or list(per)
     dom = max(single, key=lambda n: per[n]["us_avg"])
-    mfma_bound = dom in ("s8s8", "s8s8_zp", "s4s4", "conv3x3", "conv3x3_zp", "pointwise")
+    mfma_bound = dom in ("s8s8", "s8s8_zp", "s4s4", "conv3x3", "conv3x3_zp", "pointwise",
+                         "w4a8_prefill")
     if mfma_bound:
         achieved = per[dom]["tops"]
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
@@ -476,6 +483,7 @@ def main():
              "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
              "quant_a8": "per-token quant bf16 8192x8192 -> int8",
              "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3",
+             "w4a8_prefill": "w4a8 prefill 2048x28672x8192",
              "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}[n]
             for n in names),
                    "parallelism": "single GPU", "seeds": "numpy PCG64 1..7",

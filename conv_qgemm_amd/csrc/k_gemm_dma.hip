@@ -58,7 +58,25 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 constexpr int kGroupM = 4;
 constexpr int kOutStride = kBN + 16;          // LDS row stride of the int8 output tile
 
-enum { OP_S8 = 8, OP_S4 = 4 };
+// OP_MIX: int8 A x packed int4 B (W4A8); OP_MIXM: the same with B packed
+// high nibble first
+enum { OP_S8 = 8, OP_S4 = 4, OP_MIX = 3, OP_MIXM = 5 };
+
+// Per operand kind: A bytes per row per stage, ring depth, direct-to-LDS
+// loads per wave per stage.  A stage always covers 64 bytes of each B row;
+// with int8 A facing int4 B that is 128 K values, so A rows take 128 bytes
+// and the ring drops to three 48 KB stages.
+template <int KIND>
+struct Geo {
+    static constexpr bool kMix = KIND == OP_MIX || KIND == OP_MIXM;
+    static constexpr int kRowA = kMix ? 128 : kRowB;
+    static constexpr int kStageA = kBM * kRowA;
+    static constexpr int kStage = kStageA + kBN * kRowB;
+    static constexpr int kStages = kMix ? 3 : QG_DMA_STAGES;
+    static constexpr int kLoadsA = 64 * kRowA / 1024;  // per wave: 64 rows
+    static constexpr int kLoads = kLoadsA + 4;
+    static constexpr int kDsPerGroup = kMix ? 12 : 8;  // LDS fragment reads per read group
+};
 // EPI_REQUANT_ZP: the asymmetric form.  `bias` then holds the per-column
 // term bias - za * sum_k B + K * za * zb, `rterm` the per-row zb * sum_k A
 // (or null when zb = 0), and the output zero point is added before the int8
@@ -93,6 +111,10 @@ struct DmaArgs {
 // same logical chunk.  XOR-ing the chunk with row bits 2..3 puts those 16
 // reads on 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// 128-byte rows (int8 A facing int4 B): row r starts at bank group
+// 8 * (r & 1); XOR-ing the chunk (0..7) with row bits 1..3 spreads 16
+// consecutive rows over all 16 groups.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 // Wait until at most N of this wave's direct-to-LDS loads are in flight and
 // all of its LDS reads have returned, then meet the other waves.  After it,
@@ -108,10 +130,20 @@ __device__ __forceinline__ void wait_loads_and_barrier()
 template <int KIND, int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 {
+    using G = Geo<KIND>;
+    constexpr bool MIX = G::kMix;
+    constexpr bool MSB = KIND == OP_MIXM;
+    constexpr int kStages = G::kStages;
+    constexpr int kStage = G::kStage;
+    constexpr int kStageA = G::kStageA;
+    constexpr int kRowA = G::kRowA;
+    constexpr int kLoadsPerStage = G::kLoads;
     // int8: a 16-byte fragment is one 32-value K step; int4: two steps
+    // (int8 A facing int4 B reads two A fragments per B fragment)
     constexpr int STEPS_PER_READ = KIND == OP_S8 ? 1 : 2;
-    constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : 0;
+    constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : (MIX ? 4 : 0);
     constexpr int MG = 16 * STEPS_PER_READ;  // MFMAs per read group
+    constexpr int DSG = G::kDsPerGroup;
     constexpr bool RQ = EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP;
     constexpr bool ZP = EPI == EPI_REQUANT_ZP;
     constexpr bool F16 = EPI == EPI_F16;
@@ -137,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     const int tn = (t % group) / gsz;
     const int m0 = tm * kBM, n0 = tn * kBN;
 
-    const int nkt = (KIND == OP_S8 ? p.K : p.K / 2) / kRowB;
+    const int nkt = (KIND == OP_S8 ? p.K : p.K / 2) / kRowB;  // B bytes per row / 64
 
     // requantize parameters of column n0 + tid, fetched now and parked in LDS
     // (the barrier of the prologue publishes them) so the epilogue reads
@@ -162,22 +194,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 
     // ---- direct-to-LDS sources: this wave fills rows [wave*64, wave*64+64)
     //      of the A and B stage tiles, 16 rows per load ----
+    constexpr int LA = G::kLoadsA;
     uint32_t src[kLoadsPerStage];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        if constexpr (MIX) {
+            // 8 rows of 128 bytes per load
+            const int r = wave * 64 + i * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz8(r);
+            src[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.lda_b) + c * 16;
+        } else {
+            const int r = wave * 64 + i * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ swz(r);
+            src[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.lda_b) + c * 16;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wave * 64 + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
-        src[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.lda_b) + c * 16;
-        src[4 + i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.ldb_b) + c * 16;
+        src[LA + i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.ldb_b) + c * 16;
     }
-    // load l (0..3: A, 4..7: B) of K stage `s` into ring slot s % kStages; a
-    // stage past the last one re-reads the last into a slot no later stage
-    // uses
+    // load l (0..LA-1: A, LA..LA+3: B) of K stage `s` into ring slot
+    // s % kStages; a stage past the last one re-reads the last into a slot
+    // no later stage uses
     auto issue = [&](int s, int l) {
         const int kt = min(s, nkt - 1);
-        uint8_t *dst = lds + (s % kStages) * kStage + (l >= 4 ? kStageA : 0) + wave * 4096 +
-                       (l & 3) * 1024;
-        const uint8_t *g = (l >= 4 ? p.B : p.A) + (int64_t)kt * kRowB;
+        const bool isb = l >= LA;
+        uint8_t *dst = lds + (s % kStages) * kStage +
+                       (isb ? kStageA + wave * 4096 + (l - LA) * 1024
+                            : wave * (64 * kRowA) + l * 1024);
+        const uint8_t *g = isb ? p.B + (int64_t)kt * kRowB : p.A + (int64_t)kt * kRowA;
         __builtin_amdgcn_global_load_lds((const glb_void_t *)(g + src[l]), (lds_void_t *)dst, 16,
                                          0, 0);
     };
@@ -185,13 +232,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     // ---- fragment addresses inside a stage: read group g covers chunk
     //      2g + (lane >> 5) of rows (lane & 31) + 32 * sub-tile.  The swizzle
     //      only sees row bits 2..3, so sub-tile i is a fixed offset i*2048 ----
-    int a_rd[2], b_rd[2];
+    //      With 128-byte A rows the K values of B chunk c (16 bytes = 32
+    //      int4 values) are A chunks 2c and 2c + 1; the swizzle sees row bits
+    //      1..3, so sub-tile i is again a fixed offset (i*4096) ----
+    int a_rd[2][2], b_rd[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
         const int ra = wm * 128 + (lane & 31);
         const int rb = wn * 128 + (lane & 31);
         const int c = 2 * g + (lane >> 5);
-        a_rd[g] = ra * kRowB + ((c ^ swz(ra)) << 4);
+        if constexpr (MIX) {
+            a_rd[g][0] = ra * kRowA + (((2 * c) ^ swz8(ra)) << 4);
+            a_rd[g][1] = ra * kRowA + (((2 * c + 1) ^ swz8(ra)) << 4);
+        } else {
+            a_rd[g][0] = a_rd[g][1] = ra * kRowA + ((c ^ swz(ra)) << 4);
+        }
         b_rd[g] = kStageA + rb * kRowB + ((c ^ swz(rb)) << 4);
     }
 
@@ -201,23 +256,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         for (int e = 0; e < 16; ++e)
             acc[i][e] = 0;
 
-    v4i fa[2][4], fb[2][4];  // raw fragments of read groups 0 and 1
+    // raw fragments of read groups 0 and 1 (int8 A facing int4 B: two A
+    // fragments per sub-tile, [i] and [4 + i])
+    constexpr int NA = MIX ? 8 : 4;
+    v4i fa[2][NA], fb[2][4];
 
-    auto read_group = [&](int kt, int g, v4i (&ra)[4], v4i (&rb)[4]) {
-        const uint8_t *sa = lds + (kt % kStages) * kStage + a_rd[g];
-        const uint8_t *sb = lds + (kt % kStages) * kStage + b_rd[g];
+    auto read_group = [&](int kt, int g, v4i (&ra)[NA], v4i (&rb)[4]) {
+        const uint8_t *st = lds + (kt % kStages) * kStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            ra[i] = *(const v4i *)(sa + i * 32 * kRowB);
+            ra[i] = *(const v4i *)(st + a_rd[g][0] + i * 32 * kRowA);
+        if constexpr (MIX) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ra[4 + i] = *(const v4i *)(st + a_rd[g][1] + i * 32 * kRowA);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            rb[i] = *(const v4i *)(sb + i * 32 * kRowB);
+            rb[i] = *(const v4i *)(st + b_rd[g] + i * 32 * kRowB);
     };
 
     // MFMAs of one read group over sub-tiles (j, i) in [j0, j1) x [0, 4)
-    auto mma_group = [&](const v4i (&ra)[4], const v4i (&rb)[4], int j0, int j1) {
+    auto mma_group = [&](const v4i (&ra)[NA], const v4i (&rb)[4], int j0, int j1) {
 #pragma unroll
         for (int h = 0; h < STEPS_PER_READ; ++h) {
+            // int8 A facing int4 B: K step h of this group is A fragment
+            // [4h + i], byte-permuted to the widened-int4 order once
+            v4i as[MIX ? 4 : 1];
+            if constexpr (MIX) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    as[i] = even_odd_split<MSB>(ra[4 * h + i]);
+            }
 #pragma unroll
             for (int j = j0; j < j1; ++j) {
                 v4i bq;
@@ -232,6 +302,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                     v4i aq;
                     if constexpr (KIND == OP_S8) {
                         aq = ra[i];
+                    } else if constexpr (MIX) {
+                        aq = as[i];
                     } else {
                         v2u w = {(unsigned)ra[i][2 * h], (unsigned)ra[i][2 * h + 1]};
                         aq = widen_int4_x16(w);
@@ -278,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         mma_group(fa[0], fb[0], 0, 4);
         mma_group(fa[1], fb[1], 0, 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < DSG; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
@@ -287,7 +359,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MG + MG / 2 - 8 - 2 * 6, 0);
+        __builtin_amdgcn_sched_group_barrier(
+            0x008, MG + MG / 2 - DSG - 2 * (kLoadsPerStage - kEarlyLoads), 0);
         // nothing crosses the barrier: the MFMAs before it keep the matrix
         // pipe busy while the waves meet
         __builtin_amdgcn_sched_barrier(0);
@@ -307,11 +380,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < DSG / 2 - 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MG / 2 - 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MG / 2 - DSG / 2, 0);
     }
     // the re-issued loads past the last stage must land before the LDS is
     // reused for the output tile, and every wave must be done reading it
@@ -527,6 +600,24 @@ hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s)
 hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
 {
     return run<OP_S4, EPI_F16>(d, s);
+}
+
+// int8 A x int4 B: whole 128-value K stages and 32-bit source offsets
+bool dma_w4a8_fits(const GemmDesc &d)
+{
+    if (d.K % 128 != 0)
+        return false;
+    const int64_t lim = (int64_t)1 << 32;
+    if ((d.M - 1) * d.lda_b + d.K >= lim || (d.N - 1) * d.ldb_b + d.K / 2 >= lim)
+        return false;
+    return ((d.M + kBM - 1) / kBM) * ((d.N + kBN - 1) / kBN) >= 128;
+}
+
+hipError_t launch_w4a8_requant_dma(const GemmDesc &d, hipStream_t s)
+{
+    if (d.msb_first)
+        return run<OP_MIXM, EPI_REQUANT>(d, s);
+    return run<OP_MIX, EPI_REQUANT>(d, s);
 }
 
 }  // namespace qg

@@ -441,6 +441,8 @@ hipError_t launch_s4s4_f16(const GemmDesc &d, hipStream_t s)
 
 hipError_t launch_w4a8_tiled(const GemmDesc &d, hipStream_t s)
 {
+    if (dma_w4a8_fits(d))
+        return launch_w4a8_requant_dma(d, s);
     if (d.msb_first)
         return run_gemm<OP_S8, OP_S4, EPI_REQUANT, 128, true>(d, s);
     return run_gemm<OP_S8, OP_S4, EPI_REQUANT, 128>(d, s);

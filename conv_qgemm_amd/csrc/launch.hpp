@@ -65,6 +65,8 @@ hipError_t launch_s8s8_requant_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s4s4_i32_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s8s8_requant_zp_dma(const GemmDesc &d, hipStream_t s);
 hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s);
+bool dma_w4a8_fits(const GemmDesc &d);
+hipError_t launch_w4a8_requant_dma(const GemmDesc &d, hipStream_t s);
 
 // INT4 x INT4 with a binary16 output: C = fp16(fp32(acc) * scale_a[m] *
 // scale_b[n]) (C is [M][ldc] binary16 bit patterns)

@@ -23,6 +23,7 @@ bias in [-2^15, 2^15], Q31 multiplier in [2^30, 2^31), shift in 31..40):
               weights [3][3][64] (the MCU front-end page's depthwise layout)
   quant_a8    per-token quantization of bfloat16 activations [8192][8192]
               to int8 codes and float32 scales: the A operand of s8s8
+  w4a8_prefill  W4A8 with M=2048 tokens (a prefill chunk), N=28672, K=8192
   s8s8_zp     s8s8 with zero points a=-11, b=6, out=20 (same arrays)
   conv3x3_zp  conv3x3 with zero points a=-5, b=3, out=11 (same arrays)
 
@@ -54,6 +55,7 @@ WORKLOADS = {
     "dw3x3": dict(kind="dwconv", batch=32, H=56, W=56, C=64, KH=3, KW=3,
                   stride=(1, 1), pad=(1, 1), shift=(31, 40), seed=6),
     "quant_a8": dict(kind="quant", M=8192, K=8192, dtype="bfloat16", bits=8, seed=7),
+    "w4a8_prefill": dict(kind="w4a8", M=2048, N=28672, K=8192, shift=(31, 40), seed=8),
     "s8s8_zp": dict(kind="s8s8", M=8192, N=8192, K=8192, shift=(35, 44), seed=5,
                     zp=(-11, 6, 20)),
     "conv3x3_zp": dict(kind="conv", batch=32, H=56, W=56, C_in=64, C_out=64, KH=3, KW=3,
@@ -63,6 +65,7 @@ WORKLOADS = {
 # Variants whose shift windows keep most outputs inside [-128, 127], so that
 # parity is also exercised away from saturation.
 UNSATURATED_SHIFT = {"pointwise": (38, 44), "conv3x3": (39, 45), "w4a8": (37, 43),
+                     "w4a8_prefill": (37, 43),
                      "s8s8": (41, 47), "dw3x3": (39, 45)}
 
 

@@ -31,8 +31,9 @@ def _kernels(asm):
     return out
 
 
-# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize, s4s4 binary16
-N_INSTANTIATIONS = 4
+# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize, s4s4 binary16,
+# w4a8 requantize (int4 weights low or high nibble first)
+N_INSTANTIATIONS = 6
 
 
 def _nonempty(ks):
@@ -62,8 +63,10 @@ def test_main_loop_shape(asm):
         waits = [ln for ln in loop if ln.startswith("s_waitcnt")]
         assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (name, waits)
         assert sum("s_barrier" in ln for ln in loop) == 1, name
-        assert sum("global_load_lds_dwordx4" in ln for ln in loop) == 8, name
-        kind = 8 if "ILi8E" in name else 4
+        # operand kind: 8 int8 x int8, 4 int4 x int4, 3 / 5 int8 x int4
+        kind = int(re.search(r"k_gemm_dmaILi(\d)E", name).group(1))
+        loads = 12 if kind in (3, 5) else 8
+        assert sum("global_load_lds_dwordx4" in ln for ln in loop) == loads, name
         assert sum("v_mfma_i32_32x32x32_i8" in ln for ln in loop) == (32 if kind == 8 else 64), name
 
 

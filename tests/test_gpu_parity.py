@@ -371,6 +371,56 @@ def test_workload_w4a8_full(qg, unsat):
     assert np.array_equal(C, want)
 
 
+W4A8_RING = [(2048, 4096, 256), (2048, 4096, 1152), (2000, 4100, 640), (1025, 8200, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", W4A8_RING)
+@pytest.mark.parametrize("msb", [False, True])
+def test_w4a8_ring_kernel(qg, M, N, K, msb):
+    """Shapes with enough 256 x 256 tiles and K % 128 == 0 take the
+    direct-to-LDS ring kernel (int8 A rows of 128 bytes per stage); ragged M
+    and N included."""
+    _say("w4a8 ring", M, N, K, msb)
+    d = datagen.gemm_w4a8(M, N, K, seed=M + K, shift=(37, 43))
+    C = host(qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"]), msb_first=msb))
+    rows = _sample_rows(M, 10, seed=K)
+    want = oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows,
+                                    msb_first=msb)
+    assert np.array_equal(C[rows], want)
+
+
+def test_w4a8_ring_kernel_max_k(qg):
+    """The largest K of whole 128-value stages under the int4 bound, with
+    operands at the ends of their ranges, so that the x16 widened sums sit at
+    the int32 edge."""
+    M, N, K = 2048, 4096, 130944
+    A = np.full((M, K), -128, np.int8)
+    A[1::2] = 127
+    B = np.full((N, K // 2), 0x88, np.uint8)  # every weight -8
+    B[1::3] = 0x77                            # every weight 7
+    mult = np.full(N, 2 ** 30, np.int32)
+    shift = np.full(N, 44, np.int32)
+    bias = np.zeros(N, np.int32)
+    C = host(qg.qgemm_w4a8_requant(dev(A), dev(B), dev(bias), dev(mult), dev(shift)))
+    rows = np.array([0, 1, 2046, 2047])
+    want = oracle.gemm_w4a8_requant(A, B, bias, mult, shift, rows=rows)
+    assert np.array_equal(C[rows], want)
+    assert len(np.unique(want)) > 1
+
+
+@pytest.mark.parametrize("unsat", [False, True])
+def test_workload_w4a8_prefill_sampled(qg, unsat):
+    """2048 tokens x 28672 x 8192 (the prefill shape), sampled rows."""
+    _say("workload w4a8 prefill", unsat)
+    d = datagen.workload("w4a8_prefill", unsaturated=unsat)
+    C = host(qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    rows = _sample_rows(2048, 6, seed=31)
+    want = oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
+    assert np.array_equal(C[rows], want)
+
+
 @pytest.mark.parametrize("unsat", [False, True])
 def test_workload_s8s8_sampled(qg, unsat):
     _say("workload s8s8 8192^3", unsat)
