@@ -50,12 +50,12 @@ KERNEL_SOURCES = {
     "s8s8": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "s4s4": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "pointwise": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
-    "conv3x3": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "conv3x3": "conv_qgemm_amd/csrc/k_conv_halo.hip",
     "w4a8": "conv_qgemm_amd/csrc/k_skinny_w4a8.hip",
     "dw3x3": "conv_qgemm_amd/csrc/k_dwconv.hip",
     "quant_a8": "conv_qgemm_amd/csrc/k_quant.hip",
     "s8s8_zp": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
-    "w4a8_prefill": "conv_qgemm_amd/csrc/k_tile_gemm.hip",
+    "w4a8_prefill": "conv_qgemm_amd/csrc/k_gemm_dma.hip",
     "conv3x3_zp": "conv_qgemm_amd/csrc/k_conv_halo.hip",
 }
 
