@@ -61,6 +61,8 @@ def _load():
     lib.orc_int4_at.restype = ctypes.c_int
     lib.orc_requant.argtypes = [I64, I32, I32, I32, P]
     lib.orc_requant.restype = ctypes.c_int
+    lib.orc_requant_many.argtypes = [P, P, P, P, P, I64]
+    lib.orc_requant_many.restype = ctypes.c_int
     lib.orc_gemm_acc.argtypes = [ctypes.c_int, P, I64, ctypes.c_int, P, I64, I64, I64, P, I64, P]
     lib.orc_gemm_acc.restype = ctypes.c_int
     for name in ("orc_gemm_s8s8_requant", "orc_gemm_w4a8_requant"):
@@ -200,6 +202,19 @@ def requant(acc: int, bias: int, mult: int, shift: int) -> int:
     st = _load().orc_requant(int(acc), int(bias), int(mult), int(shift), out.ctypes.data)
     _check(st, "requant")
     return int(out[0])
+
+
+def requant_many(acc, bias, mult, shift):
+    """The requantize applied case by case to equal-length arrays."""
+    acc = _c(acc, np.int64)
+    bias = _c(bias, np.int32)
+    mult = _c(mult, np.int32)
+    shift = _c(shift, np.int32)
+    out = np.zeros(acc.size, dtype=np.int8)
+    st = _load().orc_requant_many(acc.ctypes.data, bias.ctypes.data, mult.ctypes.data,
+                                  shift.ctypes.data, out.ctypes.data, acc.size)
+    _check(st, "requant_many")
+    return out
 
 
 def _kind(a):

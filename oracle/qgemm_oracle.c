@@ -88,6 +88,17 @@ int orc_requant(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int8_t *
     return ORC_OK;
 }
 
+/* The requantize over arrays of cases (test convenience: one call instead
+ * of one per case); status is the OR of the cases' statuses. */
+int orc_requant_many(const int64_t *acc, const int32_t *bias, const int32_t *mult,
+                     const int32_t *shift, int8_t *out, int64_t n)
+{
+    int status = ORC_OK;
+    for (int64_t i = 0; i < n; ++i)
+        status |= orc_requant(acc[i], bias[i], mult[i], shift[i], &out[i]);
+    return status;
+}
+
 /* ---- O2: plain dot products over K, int64 sums ---- */
 static int64_t dot_s8_s8(const int8_t *a, const int8_t *b, int64_t K)
 {

@@ -51,6 +51,29 @@ def test_random_against_rational_spec(orc):
         assert orc.requant(x, 0, M, s) == _spec(x, M, s), (x, M, s)
 
 
+def test_million_against_bigint(orc):
+    """10^6 random cases (full-range x and M, every shift, plus the extremes)
+    against the rounding written with Python integers, whose floor division
+    does not depend on C's 64-bit arithmetic: y = floor((x M + 2^(s-1)) / 2^s),
+    saturated."""
+    g = np.random.default_rng(17)
+    n = 1_000_000
+    x = g.integers(-2 ** 31, 2 ** 31, size=n, dtype=np.int64)
+    x[: n // 2] = g.integers(-2 ** 26, 2 ** 26, size=n // 2)
+    M = g.integers(0, 2 ** 31, size=n, dtype=np.int64)
+    s = g.integers(1, 64, size=n, dtype=np.int64)
+    s[: n // 3] = g.integers(28, 46, size=n // 3)
+    ext = [(xv, mv, sv) for xv in (2 ** 31 - 1, -2 ** 31, 0, 1, -1)
+           for mv in (2 ** 31 - 1, 2 ** 30, 0) for sv in (1, 31, 44, 63)]
+    x[: len(ext)] = [e[0] for e in ext]
+    M[: len(ext)] = [e[1] for e in ext]
+    s[: len(ext)] = [e[2] for e in ext]
+    got = orc.requant_many(x, np.zeros(n, np.int32), M.astype(np.int32), s.astype(np.int32))
+    want = [max(-128, min(127, (xi * mi + (1 << (si - 1))) >> si))
+            for xi, mi, si in zip(x.tolist(), M.tolist(), s.tolist())]
+    assert np.array_equal(got, np.array(want, np.int8))
+
+
 def test_exact_ties_round_up(orc):
     # x*M/2^s = k + 1/2 exactly for k in a range: result must be k + 1
     s = 35
