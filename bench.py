@@ -198,7 +198,10 @@ class Case:
 
 def cpu_baseline(names, frac=16):
     """The CPU oracle, as it stands, on 1/frac of every workload of the step:
-    every frac-th output row (GEMMs), pixel (conv) or weight row (w4a8)."""
+    every frac-th output row (GEMMs), pixel (conv), weight row (w4a8) or
+    token (quantizer); every (16 frac)-th row of the W4A8 prefill.  Wall
+    seconds and GMAC/s per workload, and the step's ops over the total
+    seconds as `value`."""
     import numpy as np
 
     import oracle
@@ -206,7 +209,7 @@ def cpu_baseline(names, frac=16):
 
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
-    total_ops, total_t, parts = 0, 0.0, []
+    total_ops, total_t, parts, per = 0, 0.0, [], {}
     for name in names:
         d = datagen.workload(name)
         w = shape_of(name)
@@ -267,8 +270,10 @@ def cpu_baseline(names, frac=16):
         total_ops += ops * part
         total_t += dt
         parts.append(f"{name}:{part:.4f}")
+        per[name] = {"seconds": round(dt, 3), "fraction": round(part, 4),
+                     "gmac_s": round(ops / 2 * part / dt / 1e9, 2)}
     return {"value": total_ops / total_t / 1e12, "unit": "TOPS", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": round(total_t, 2),
+            "kind": "oracle", "seconds": round(total_t, 2), "per_config": per,
             "sample": f"every {frac}th output row/pixel/weight row/token of each workload of one "
                       f"step ({', '.join(parts)} of the outputs)"}
 
@@ -377,12 +382,14 @@ def main():
     # that a workload is not measured in the power state a heavier one leaves
     # behind.  A phase is W warm-up calls, then K back-to-back eager calls
     # between two HIP events on the launch stream, then the same K calls
-    # captured once in a HIP graph and replayed (one untimed replay, one timed
-    # between events).  The graph replay is the per-launch GPU time without
-    # the Python binding's per-call host cost, which decides the launch-bound
-    # pointwise case and is hidden behind the GPU for the others.
+    # captured in a HIP graph, replayed once untimed and then 20 times with
+    # an event between replays.  The first timed replay (exactly K calls) is
+    # the per-launch GPU time without the Python binding's per-call host cost,
+    # which decides the launch-bound pointwise case and is hidden behind the
+    # GPU for the others; all 20 give the median and p99 over batches.
     stream = torch.cuda.current_stream()
     eager, graphed, spread = {}, {}, {}
+    nb = 20  # timed replays of the K-call graph
 
     def timed(fn):
         s0 = torch.cuda.current_stream()
@@ -405,7 +412,12 @@ def main():
             for i in range(args.steps):
                 c(i)
         g.replay()
-        graphed[c.name] = timed(g.replay)
+        bmarks = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+        bmarks[0].record(stream)
+        for r in range(nb):
+            g.replay()
+            bmarks[r + 1].record(stream)
+        graphed[c.name] = bmarks
         # 20 more eager calls with an event after each give the spread of
         # single launches (median, max); they enter no average
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
@@ -417,13 +429,16 @@ def main():
         torch.cuda.synchronize()
         del g
     wall = time.perf_counter() - t0
-    gpu_step = sum(a.elapsed_time(b) for a, b in graphed.values()) * 1e-3 / args.steps
+    gpu_step = sum(m[0].elapsed_time(m[1]) for m in graphed.values()) * 1e-3 / args.steps
 
     per = {}
     total_ops = 0
     for c in cases:
-        a, b = graphed[c.name]
-        avg = a.elapsed_time(b) * 1e-3 / args.steps
+        bm = graphed[c.name]
+        avg = bm[0].elapsed_time(bm[1]) * 1e-3 / args.steps
+        bt = sorted(bm[r].elapsed_time(bm[r + 1]) * 1e-3 / args.steps for r in range(nb))
+        b_med = bt[len(bt) // 2]
+        b_p99 = bt[min(len(bt) - 1, int(0.99 * len(bt)))]
         a, b = eager[c.name]
         avg_eager = a.elapsed_time(b) * 1e-3 / args.steps
         m = spread[c.name]
@@ -433,6 +448,8 @@ def main():
         tops = c.ops / avg / 1e12
         gbs = c.bytes / avg / 1e9
         per[c.name] = {"us_avg": round(avg * 1e6, 2),
+                       "us_batch_median": round(b_med * 1e6, 2),
+                       "us_batch_p99": round(b_p99 * 1e6, 2),
                        "us_avg_eager": round(avg_eager * 1e6, 2),
                        "us_single_median": round(med * 1e6, 2),
                        "us_single_max": round(p99 * 1e6, 2), "tops": round(tops, 2),
@@ -487,13 +504,14 @@ def main():
              "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}[n]
             for n in names),
                    "parallelism": "single GPU", "seeds": "numpy PCG64 1..7",
-                   "timing": f"per workload: {args.warmup} warm-up calls, then "
-                             f"{args.steps} back-to-back calls captured in a HIP graph "
-                             f"and replayed between two HIP events (us_avg; value and "
-                             f"roofline use it), and the same {args.steps} calls issued "
-                             f"eagerly from Python (us_avg_eager); single-launch spread "
-                             f"from 20 more eager calls; wall {wall:.3f} s for all "
-                             f"phases"},
+                   "timing": f"per workload: {args.warmup} warm-up calls; "
+                             f"{args.steps} back-to-back calls issued eagerly from Python "
+                             f"(us_avg_eager); the same {args.steps} calls captured in a "
+                             f"HIP graph, replayed once untimed and {nb} times between "
+                             f"HIP events (us_avg: the first timed replay, which value "
+                             f"and roofline use; us_batch_median / us_batch_p99: per "
+                             f"call over the {nb} replays); single-launch spread from "
+                             f"20 more eager calls; wall {wall:.3f} s for all phases"},
         "per_config": per,
         "roofline": roof,
     }
@@ -501,6 +519,11 @@ def main():
         out["hbm_copy_gb_s"] = round(hbm_copy_gbs(torch), 1)
     except RuntimeError:
         out["hbm_copy_gb_s"] = None
+    if out["hbm_copy_gb_s"]:
+        # the HBM-bound workloads against the rate a plain device copy reaches
+        for n in ("w4a8", "quant_a8"):
+            if n in per:
+                per[n]["pct_of_copy_rate"] = round(100 * per[n]["gb_s"] / out["hbm_copy_gb_s"], 1)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(names, args.cpu_frac)
     print(json.dumps(out))
