@@ -127,6 +127,23 @@ __device__ __forceinline__ void wait_loads_and_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// The lane id, computed afresh.  The asm is volatile so that it is not
+// merged with a lane id kept from the start of the kernel: across the main
+// loop such a value is spilled, and its reload would wait for every load in
+// flight, the next tile's ring stages included.
+__device__ __forceinline__ int fresh_lane()
+{
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
+}
+
+// One 4-byte direct-to-LDS load per lane: lane L's dword lands at dst + 4L.
+__device__ __forceinline__ void dma_dword(const void *src, void *dst)
+{
+    __builtin_amdgcn_global_load_lds((const glb_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
+}
+
 template <int KIND, int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 {
@@ -148,12 +165,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     constexpr bool ZP = EPI == EPI_REQUANT_ZP;
     constexpr bool F16 = EPI == EPI_F16;
 
-    // one LDS object: the operand ring, then the per-column bias / multiplier
-    // / shift of this tile's 256 output columns and the per-row term of its
-    // 256 rows (a second __shared__ object makes the compiler wait for every
-    // direct-to-LDS load before any read)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage + 4 * kBN * 4];
-    int(*prm)[kBN] = (int(*)[kBN])(lds + kStages * kStage);
+    // one LDS object: the operand ring, then two buffers of per-tile
+    // parameters (a second __shared__ object makes the compiler wait for
+    // every direct-to-LDS load before any read).  Buffer b holds, for its
+    // tile's 256 columns / rows: [0] bias (EPI_F16: column scales), [1]
+    // multiplier, [2] shift, [3] per-row term (EPI_F16: row scales).
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStage + 2 * 4 * kBN * 4];
+    int(*prm_buf)[4][kBN] = (int(*)[4][kBN])(lds + kStages * kStage);
     static_assert(kBM == kBN, "the row terms share the column-parameter layout");
 
     const int tid = threadIdx.x;
@@ -161,70 +179,120 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int group = kGroupM * p.tiles_n;
-    const int first_m = (t / group) * kGroupM;
-    const int gsz = min(p.tiles_m - first_m, kGroupM);
-    const int tm = first_m + (t % group) % gsz;
-    const int tn = (t % group) / gsz;
-    const int m0 = tm * kBM, n0 = tn * kBN;
-
+    const int ntiles = p.tiles_m * p.tiles_n;
     const int nkt = (KIND == OP_S8 ? p.K : p.K / 2) / kRowB;  // B bytes per row / 64
 
-    // requantize parameters of column n0 + tid, fetched now and parked in LDS
-    // (the barrier of the prologue publishes them) so the epilogue reads
-    // them without global-memory latency
-    int pb = 0, pm = 0, ps = 0, pr = 0;
-    if constexpr (RQ) {
-        const int n = min(n0 + tid, p.N - 1);
-        pb = p.bias ? p.bias[n] : 0;
-        pm = p.mult[n];
-        ps = p.shift[n];
-    }
-    if constexpr (ZP) {
-        if (p.rterm)
-            pr = p.rterm[min(m0 + tid, p.M - 1)];
-    }
-    if constexpr (F16) {
-        // column and row scales of the tile, as bit patterns (1.0 if absent)
-        pb = __float_as_int(p.scale_b ? p.scale_b[min(n0 + tid, p.N - 1)] : 1.0f);
-        pr = __float_as_int(p.scale_a ? p.scale_a[min(m0 + tid, p.M - 1)] : 1.0f);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // tile v of the persistent walk -> its first row and column.  Virtual
+    // tile v runs on XCD v % 8 (the grid is a multiple of 8 on MI355X), so
+    // xcd_remap gives each XCD a contiguous run of tile ids, and groups of
+    // kGroupM tile rows share their B panels in that XCD's L2.  A tile at
+    // the bottom or right edge is moved inward to end at row M / column N
+    // (M, N >= 256): it then overlaps its neighbour, whose outputs it
+    // recomputes bit for bit, and no row or column is ever out of range.
+    auto coords = [&](int v, int &m0, int &n0) __attribute__((always_inline)) {
+        const int t = xcd_remap(v, ntiles);
+        const int group = kGroupM * p.tiles_n;
+        const int first_m = (t / group) * kGroupM;
+        const int gsz = min(p.tiles_m - first_m, kGroupM);
+        m0 = min((first_m + (t % group) % gsz) * kBM, p.M - kBM);
+        n0 = min(((t % group) / gsz) * kBN, p.N - kBN);
+    };
 
     // ---- direct-to-LDS sources: this wave fills rows [wave*64, wave*64+64)
-    //      of the A and B stage tiles, 16 rows per load ----
+    //      of the A and B stage tiles, 16 rows per load (8 rows of 128 bytes
+    //      for the int8 A facing int4 B).  The per-lane offsets inside a
+    //      tile are the same for every tile; a tile adds a scalar base ----
     constexpr int LA = G::kLoadsA;
     uint32_t src[kLoadsPerStage];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
         if constexpr (MIX) {
-            // 8 rows of 128 bytes per load
             const int r = wave * 64 + i * 8 + (lane >> 3);
             const int c = (lane & 7) ^ swz8(r);
-            src[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.lda_b) + c * 16;
+            src[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
         } else {
             const int r = wave * 64 + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ swz(r);
-            src[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.lda_b) + c * 16;
+            src[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
         }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wave * 64 + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
-        src[LA + i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.ldb_b) + c * 16;
+        src[LA + i] = (uint32_t)r * (uint32_t)p.ldb_b + c * 16;
     }
-    // load l (0..LA-1: A, LA..LA+3: B) of K stage `s` into ring slot
-    // s % kStages; a stage past the last one re-reads the last into a slot
-    // no later stage uses
-    auto issue = [&](int s, int l) {
-        const int kt = min(s, nkt - 1);
+
+    // ---- per-tile parameters: this wave's 64 columns (and rows) of the
+    //      tile, one 4-byte direct-to-LDS load per array; absent arrays are
+    //      constants written once ----
+    auto load_prm = [&](int buf, int m0, int n0) __attribute__((always_inline)) {
+        const int ln = fresh_lane();
+        const int n = n0 + wave * 64 + ln;
+        const int m = m0 + wave * 64 + ln;
+        int(*pb)[kBN] = prm_buf[buf];
+        if constexpr (RQ) {
+            if (p.bias)
+                dma_dword(p.bias + n, &pb[0][wave * 64]);
+            dma_dword(p.mult + n, &pb[1][wave * 64]);
+            dma_dword(p.shift + n, &pb[2][wave * 64]);
+            if (ZP && p.rterm)
+                dma_dword(p.rterm + m, &pb[3][wave * 64]);
+        }
+        if constexpr (F16) {
+            if (p.scale_b)
+                dma_dword(p.scale_b + n, &pb[0][wave * 64]);
+            if (p.scale_a)
+                dma_dword(p.scale_a + m, &pb[3][wave * 64]);
+        }
+    };
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (RQ && !p.bias)
+            prm_buf[b][0][tid] = 0;
+        if (ZP && !p.rterm)
+            prm_buf[b][3][tid] = 0;
+        if (F16 && !p.scale_b)
+            prm_buf[b][0][tid] = __float_as_int(1.0f);
+        if (F16 && !p.scale_a)
+            prm_buf[b][3][tid] = __float_as_int(1.0f);
+    }
+
+    // ---- the walk: tiles v = blockIdx.x + k * gridDim.x.  The ring runs
+    //      across tile boundaries: stages past this tile's last are the next
+    //      tile's first, loaded while this tile's last stages multiply ----
+    int v = blockIdx.x;
+    int m0, n0, m0n, n0n;
+    coords(v, m0, n0);
+    bool has_next = v + (int)gridDim.x < ntiles;
+    if (has_next)
+        coords(v + (int)gridDim.x, m0n, n0n);
+    else
+        m0n = m0, n0n = n0;
+    // byte offsets of stage 0 of this tile in A and B, and of the next
+    // tile's stage 0 minus nkt stages, so that stage s (s >= nkt: the next
+    // tile's stage s - nkt) is one select and one add away.  With no next
+    // tile the stages past the last re-read this tile's first ones into
+    // slots no later stage uses.
+    int64_t a_cur, b_cur, a_nxt, b_nxt;
+    auto set_bases = [&]() __attribute__((always_inline)) {
+        a_cur = (int64_t)m0 * p.lda_b;
+        b_cur = (int64_t)n0 * p.ldb_b;
+        a_nxt = (int64_t)m0n * p.lda_b - (int64_t)nkt * kRowA;
+        b_nxt = (int64_t)n0n * p.ldb_b - (int64_t)nkt * kRowB;
+    };
+    set_bases();
+
+    // load l (0..LA-1: A, LA..LA+3: B) of stage s of this tile into ring
+    // slot `slot`
+    auto issue = [&](int s, int slot, int l) __attribute__((always_inline)) {
+        const bool nxt = s >= nkt;
         const bool isb = l >= LA;
-        uint8_t *dst = lds + (s % kStages) * kStage +
+        uint8_t *dst = lds + slot * kStage +
                        (isb ? kStageA + wave * 4096 + (l - LA) * 1024
                             : wave * (64 * kRowA) + l * 1024);
-        const uint8_t *g = isb ? p.B + (int64_t)kt * kRowB : p.A + (int64_t)kt * kRowA;
+        const uint8_t *g = isb ? p.B + (nxt ? b_nxt : b_cur) + (int64_t)s * kRowB
+                               : p.A + (nxt ? a_nxt : a_cur) + (int64_t)s * kRowA;
         __builtin_amdgcn_global_load_lds((const glb_void_t *)(g + src[l]), (lds_void_t *)dst, 16,
                                          0, 0);
     };
@@ -251,18 +319,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     }
 
     v16i acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        for (int e = 0; e < 16; ++e)
-            acc[i][e] = 0;
 
     // raw fragments of read groups 0 and 1 (int8 A facing int4 B: two A
     // fragments per sub-tile, [i] and [4 + i])
     constexpr int NA = MIX ? 8 : 4;
     v4i fa[2][NA], fb[2][4];
 
-    auto read_group = [&](int kt, int g, v4i (&ra)[NA], v4i (&rb)[4]) {
-        const uint8_t *st = lds + (kt % kStages) * kStage;
+    auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[4]) __attribute__((always_inline)) {
+        const uint8_t *st = lds + slot * kStage;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             ra[i] = *(const v4i *)(st + a_rd[g][0] + i * 32 * kRowA);
@@ -277,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     };
 
     // MFMAs of one read group over sub-tiles (j, i) in [j0, j1) x [0, 4)
-    auto mma_group = [&](const v4i (&ra)[NA], const v4i (&rb)[4], int j0, int j1) {
+    auto mma_group = [&](const v4i(&ra)[NA], const v4i(&rb)[4], int j0, int j1) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < STEPS_PER_READ; ++h) {
             // int8 A facing int4 B: K step h of this group is A fragment
@@ -315,184 +379,193 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         }
     };
 
-    // ---- prologue: stages 0..kStages-2 and the first loads of the next
-    //      issued, stage 0 readable.  Loads issued behind any stage's are
-    //      always kStages-2 whole stages when it is waited for ----
+    // ---- prologue of the first tile: its parameters, stages
+    //      0..kStages-2 and the first loads of the next issued, stage 0
+    //      readable.  Loads issued behind any stage's are always kStages-2
+    //      whole stages when it is waited for ----
+    if constexpr (RQ || F16)
+        load_prm(0, m0, n0);
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
 #pragma unroll
         for (int l = 0; l < kLoadsPerStage; ++l)
-            issue(s, l);
+            issue(s, s, l);
 #pragma unroll
     for (int l = 0; l < kEarlyLoads; ++l)
-        issue(kStages - 1, l);
-    if constexpr (RQ) {
-        prm[0][tid] = pb;
-        prm[1][tid] = pm;
-        prm[2][tid] = ps;
-    }
-    if constexpr (ZP)
-        prm[3][tid] = pr;
-    if constexpr (F16) {
-        prm[0][tid] = pb;
-        prm[3][tid] = pr;
-    }
+        issue(kStages - 1, kStages - 1, l);
     wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage + kEarlyLoads>();
     read_group(0, 0, fa[0], fb[0]);
+    int rs = 0;  // ring slot of the stage being multiplied
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        // group 1 of this stage streams in behind group 0's MFMAs, and the
-        // rest of stage kt+kStages-1 (its slot was freed at the last barrier)
-        read_group(kt, 1, fa[1], fb[1]);
+    for (int k = 0;; ++k) {
 #pragma unroll
-        for (int l = kEarlyLoads; l < kLoadsPerStage; ++l)
-            issue(kt + kStages - 1, l);
-        mma_group(fa[0], fb[0], 0, 4);
-        mma_group(fa[1], fb[1], 0, 2);
+        for (int i = 0; i < 16; ++i)
+            for (int e = 0; e < 16; ++e)
+                acc[i][e] = 0;
+        // the last kStages - 1 stages issue the next tile's first loads (the
+        // ring is never deeper than a tile: nkt >= kStages)
+        for (int kt = 0; kt < nkt; ++kt) {
+            // slots of stages kt + kStages - 1 (the one before rs) and kt + 1
+            const int ps = rs == 0 ? kStages - 1 : rs - 1;
+            const int ns = rs == kStages - 1 ? 0 : rs + 1;
+            // group 1 of this stage streams in behind group 0's MFMAs, and
+            // the rest of stage kt+kStages-1 (its slot was freed at the last
+            // barrier)
+            read_group(rs, 1, fa[1], fb[1]);
 #pragma unroll
-        for (int i = 0; i < DSG; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            for (int l = kEarlyLoads; l < kLoadsPerStage; ++l)
+                issue(kt + kStages - 1, ps, l);
+            mma_group(fa[0], fb[0], 0, 4);
+            mma_group(fa[1], fb[1], 0, 2);
+#pragma unroll
+            for (int i = 0; i < DSG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+#pragma unroll
+            for (int i = 0; i < kLoadsPerStage - kEarlyLoads; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+            }
+            __builtin_amdgcn_sched_group_barrier(
+                0x008, MG + MG / 2 - DSG - 2 * (kLoadsPerStage - kEarlyLoads), 0);
+            // nothing crosses the barrier: the MFMAs before it keep the
+            // matrix pipe busy while the waves meet
+            __builtin_amdgcn_sched_barrier(0);
+            // stage kt+1 landed for this wave; after the barrier, for all.
+            // Every wave has read all of stage kt, so its slot takes stage
+            // kt+kStages.
+            wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage>();
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int l = 0; l < kEarlyLoads; ++l)
+                issue(kt + kStages, rs, l);
+            // after the last stage this reads the next tile's first
+            // fragments, which are read again once the epilogue is done
+            read_group(ns, 0, fa[0], fb[0]);
+            mma_group(fa[1], fb[1], 2, 4);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+            }
+#pragma unroll
+            for (int i = 0; i < DSG / 2 - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MG / 2 - DSG / 2, 0);
+            rs = ns;
         }
-#pragma unroll
-        for (int i = 0; i < kLoadsPerStage - kEarlyLoads; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-        }
-        __builtin_amdgcn_sched_group_barrier(
-            0x008, MG + MG / 2 - DSG - 2 * (kLoadsPerStage - kEarlyLoads), 0);
-        // nothing crosses the barrier: the MFMAs before it keep the matrix
-        // pipe busy while the waves meet
-        __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 landed for this wave; after the barrier, for all.  Every
-        // wave has read all of stage kt, so its slot takes stage kt+kStages.
-        wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage>();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int l = 0; l < kEarlyLoads; ++l)
-            issue(kt + kStages, l);
-        read_group(kt + 1, 0, fa[0], fb[0]);
-        mma_group(fa[1], fb[1], 2, 4);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-        }
-#pragma unroll
-        for (int i = 0; i < DSG / 2 - 2; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MG / 2 - DSG / 2, 0);
-    }
-    // the re-issued loads past the last stage must land before the LDS is
-    // reused for the output tile, and every wave must be done reading it
-    wait_loads_and_barrier<0>();
 
-    // ---- epilogue: lane holds rows ml = wm*128 + i*32 + lane%32 and columns
-    //      nl = wn*128 + j*32 + q*8 + (lane/32)*4 + e of the tile in
-    //      accumulator registers 4q + e of sub-tile (j, i) ----
-    const int khalf = lane >> 5;
-    if constexpr (RQ) {
-        // requantize into an LDS copy of the 256 x 256 int8 tile, with the
-        // cheapest exact form that every shift of the tile allows (chosen
-        // once, so the accumulator indices stay compile-time constants)
-        uint8_t *otile = lds;
-        const v4i sh4 = *(const v4i *)&prm[2][lane * 4];
-        bool s33 = true, s31 = true;
-        for (int e = 0; e < 4; ++e) {
-            s33 = s33 && sh4[e] >= 33;
-            s31 = s31 && sh4[e] >= 31;
-        }
-        auto requant_tile = [&](auto tier_tag) {
-            constexpr int TIER = decltype(tier_tag)::value;
+        // ---- epilogue: lane holds rows ml = wm*128 + i*32 + lane%32 and
+        //      columns nl = wn*128 + j*32 + q*8 + (lane/32)*4 + e of the
+        //      tile in accumulator registers 4q + e of sub-tile (j, i).  Its
+        //      parameters landed before the last stage's barrier; the ring
+        //      already holds the next tile's first stages ----
+        int(*prm)[kBN] = prm_buf[k & 1];
+        const int lane = fresh_lane();
+        const int khalf = lane >> 5;
+        if constexpr (RQ) {
+            // requantize with the cheapest exact form that every shift of
+            // the tile allows (chosen once, so the accumulator indices stay
+            // compile-time constants).  For each 32x32 sub-tile a lane
+            // packs its 16 results of one row into 4 dwords (q = 0..3, 4
+            // columns each); one v_permlane32_swap per dword pair gives the
+            // lower half-wave columns 0..15 and the upper columns 16..31 of
+            // that row, stored as one 16-byte write.
+            const v4i sh4 = *(const v4i *)&prm[2][lane * 4];
+            bool s33 = true, s31 = true;
+            for (int e = 0; e < 4; ++e) {
+                s33 = s33 && sh4[e] >= 33;
+                s31 = s31 && sh4[e] >= 31;
+            }
+            int8_t *C = (int8_t *)p.C;
+            const bool vec_ok = (p.ldc & 15) == 0;
+            auto requant_tile = [&](auto tier_tag) __attribute__((always_inline)) {
+                constexpr int TIER = decltype(tier_tag)::value;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
+                    v4i b4[4], m4[4], s4[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                    const v4i b4 = *(const v4i *)&prm[0][nl];
-                    const v4i m4 = *(const v4i *)&prm[1][nl];
-                    const v4i s4 = *(const v4i *)&prm[2][nl];
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                        b4[q] = *(const v4i *)&prm[0][nl];
+                        m4[q] = *(const v4i *)&prm[1][nl];
+                        s4[q] = *(const v4i *)&prm[2][nl];
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int ml = wm * 128 + i * 32 + (lane & 31);
                         const int rt = ZP ? prm[3][ml] : 0;
                         const int zo = ZP ? p.out_zero : 0;
                         const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
-                        int y[4];
+                        unsigned d[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            int y[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                int a = acc[j * 4 + i][4 * q + e] >> ACC_SHIFT;
+                                if constexpr (ZP)
+                                    a = wrap_sub(a, rt);
+                                if constexpr (TIER == 2)
+                                    y[e] = requant_one_s33(a, b4[q][e], m4[q][e], s4[q][e], zo,
+                                                           lo, hi);
+                                else if constexpr (TIER == 1)
+                                    y[e] = requant_one_s31(a, b4[q][e], m4[q][e], s4[q][e],
+                                                           1ll << ((s4[q][e] - 1) & 63), zo, lo,
+                                                           hi);
+                                else
+                                    y[e] = requant_one(a, b4[q][e], m4[q][e], s4[q][e],
+                                                       1ll << ((s4[q][e] - 1) & 63), zo, lo, hi);
+                            }
+                            d[q] = pack4_i8(y[0], y[1], y[2], y[3]);
+                        }
+                        const auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+                        const auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+                        const v4i out = {(int)r02[0], (int)r02[1], (int)r13[0], (int)r13[1]};
+                        int8_t *dst = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128 + j * 32 +
+                                      khalf * 16;
+                        if (vec_ok) {
+                            *(v4i *)dst = out;
+                        } else {
+                            for (int b = 0; b < 16; ++b)
+                                dst[b] = (int8_t)(out[b >> 2] >> (8 * (b & 3)));
+                        }
+                    }
+                }
+            };
+            if (__builtin_amdgcn_ballot_w64(!s33) == 0)
+                requant_tile(std::integral_constant<int, 2>{});
+            else if (__builtin_amdgcn_ballot_w64(!s31) == 0)
+                requant_tile(std::integral_constant<int, 1>{});
+            else
+                requant_tile(std::integral_constant<int, 0>{});
+        } else if constexpr (F16) {
+            // binary16: 4 adjacent columns of one row per 8-byte store
+            uint16_t *C = (uint16_t *)p.C;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                    const int n = n0 + nl;
+                    const bool vec = (p.ldc & 3) == 0;
+                    const v4i sb4 = *(const v4i *)&prm[0][nl];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ml = wm * 128 + i * 32 + (lane & 31);
+                        const int m = m0 + ml;
+                        const float sa = __int_as_float(prm[3][ml]);
+                        const v16i &a = acc[j * 4 + i];
+                        unsigned short h[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            int a = acc[j * 4 + i][4 * q + e] >> ACC_SHIFT;
-                            if constexpr (ZP)
-                                a = wrap_sub(a, rt);
-                            if constexpr (TIER == 2)
-                                y[e] = requant_one_s33(a, b4[e], m4[e], s4[e], zo, lo, hi);
-                            else if constexpr (TIER == 1)
-                                y[e] = requant_one_s31(a, b4[e], m4[e], s4[e],
-                                                       1ll << ((s4[e] - 1) & 63), zo, lo, hi);
-                            else
-                                y[e] = requant_one(a, b4[e], m4[e], s4[e],
-                                                   1ll << ((s4[e] - 1) & 63), zo, lo, hi);
+                            const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
+                            h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
                         }
-                        *(unsigned *)(otile + ml * kOutStride + nl) =
-                            pack4_i8(y[0], y[1], y[2], y[3]);
-                    }
-                }
-            }
-        };
-        if (__builtin_amdgcn_ballot_w64(!s33) == 0)
-            requant_tile(std::integral_constant<int, 2>{});
-        else if (__builtin_amdgcn_ballot_w64(!s31) == 0)
-            requant_tile(std::integral_constant<int, 1>{});
-        else
-            requant_tile(std::integral_constant<int, 0>{});
-        __syncthreads();
-        // 256 rows x 16 chunks of 16 bytes; consecutive threads walk a row
-        int8_t *C = (int8_t *)p.C;
-        const bool vec_ok = (p.ldc & 15) == 0;
-#pragma unroll 4
-        for (int it = 0; it < kBM * (kBN / 16) / 256; ++it) {
-            const int id = it * 256 + tid;
-            const int rl = id >> 4, cl = (id & 15) * 16;
-            const int m = m0 + rl, n = n0 + cl;
-            const v4i v = *(const v4i *)(otile + rl * kOutStride + cl);
-            if (m < p.M) {
-                int8_t *dst = C + (int64_t)m * p.ldc + n;
-                if (vec_ok && n + 15 < p.N) {
-                    *(v4i *)dst = v;
-                } else {
-                    for (int b = 0; b < 16; ++b)
-                        if (n + b < p.N)
-                            dst[b] = (int8_t)(v[b >> 2] >> (8 * (b & 3)));
-                }
-            }
-        }
-    } else if constexpr (F16) {
-        // binary16: 4 adjacent columns of one row per 8-byte store
-        uint16_t *C = (uint16_t *)p.C;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                const int n = n0 + nl;
-                const bool vec = n + 3 < p.N && (p.ldc & 3) == 0;
-                const v4i sb4 = *(const v4i *)&prm[0][nl];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ml = wm * 128 + i * 32 + (lane & 31);
-                    const int m = m0 + ml;
-                    const float sa = __int_as_float(prm[3][ml]);
-                    const v16i &a = acc[j * 4 + i];
-                    unsigned short h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
-                        h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
-                    }
-                    if (m < p.M) {
                         uint16_t *dst = C + (int64_t)m * p.ldc + n;
                         if (vec) {
                             v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
@@ -500,43 +573,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                             *(v2u *)dst = w;
                         } else {
                             for (int e = 0; e < 4; ++e)
-                                if (n + e < p.N)
-                                    dst[e] = h[e];
+                                dst[e] = h[e];
                         }
                     }
                 }
             }
-        }
-    } else {
-        // raw int32: 4 adjacent columns of one row per 16-byte store
-        int32_t *C = (int32_t *)p.C;
+        } else {
+            // raw int32: 4 adjacent columns of one row per 16-byte store
+            int32_t *C = (int32_t *)p.C;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + j * 32 + q * 8 + khalf * 4;
-                const bool vec = n + 3 < p.N && (p.ldc & 3) == 0;
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + wn * 128 + j * 32 + q * 8 + khalf * 4;
+                    const bool vec = (p.ldc & 3) == 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-                    const v16i &a = acc[j * 4 + i];
-                    v4i y;
-                    for (int e = 0; e < 4; ++e)
-                        y[e] = a[4 * q + e] >> ACC_SHIFT;
-                    if (m < p.M) {
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+                        const v16i &a = acc[j * 4 + i];
+                        v4i y;
+                        for (int e = 0; e < 4; ++e)
+                            y[e] = a[4 * q + e] >> ACC_SHIFT;
                         int32_t *dst = C + (int64_t)m * p.ldc + n;
                         if (vec) {
                             *(v4i *)dst = y;
                         } else {
                             for (int e = 0; e < 4; ++e)
-                                if (n + e < p.N)
-                                    dst[e] = y[e];
+                                dst[e] = y[e];
                         }
                     }
                 }
             }
         }
+
+        if (!has_next)
+            break;
+        // ---- advance: the next tile's stage 0 landed before the last
+        //      barrier; its parameters go to the other buffer, whose last
+        //      reader (the epilogue two tiles back) finished long ago ----
+        v += (int)gridDim.x;
+        m0 = m0n;
+        n0 = n0n;
+        has_next = v + (int)gridDim.x < ntiles;
+        if (has_next)
+            coords(v + (int)gridDim.x, m0n, n0n);
+        set_bases();
+        if constexpr (RQ || F16)
+            load_prm((k + 1) & 1, m0, n0);
+        read_group(rs, 0, fa[0], fb[0]);
     }
+    // the re-reads past the last stage must land before the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int KIND, int EPI>
@@ -563,20 +650,28 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     a.act_max = d.act_max;
     a.scale_a = d.scale_a;
     a.scale_b = d.scale_b;
-    hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, s, a);
+    // one persistent workgroup per CU (the LDS ring allows no second)
+    const int ntiles = a.tiles_m * a.tiles_n;
+    const int grid = ntiles < d.cus ? ntiles : d.cus;
+    hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// The ring kernel takes whole 64-byte K rows and 32-bit source offsets.
+// The ring kernel takes whole 64-byte K rows, at least a ring's worth of
+// them (the ring then only ever holds stages of this tile and the next), at
+// least one whole tile each way (edge tiles move inward), and 32-bit offsets
+// inside a tile.
 bool dma_gemm_fits(const GemmDesc &d, bool int4)
 {
     const int64_t kb = int4 ? d.K / 2 : d.K;
-    if (kb % kRowB != 0)
+    if (kb % kRowB != 0 || kb / kRowB < (int4 ? Geo<OP_S4>::kStages : Geo<OP_S8>::kStages))
+        return false;
+    if (d.M < kBM || d.N < kBN)
         return false;
     const int64_t lim = (int64_t)1 << 32;
-    if ((d.M - 1) * d.lda_b + kb >= lim || (d.N - 1) * d.ldb_b + kb >= lim)
+    if ((kBM - 1) * d.lda_b + kb >= lim || (kBN - 1) * d.ldb_b + kb >= lim)
         return false;
     // enough 256x256 tiles to fill the chip
     return ((d.M + kBM - 1) / kBM) * ((d.N + kBN - 1) / kBN) >= 128;
@@ -602,13 +697,16 @@ hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
     return run<OP_S4, EPI_F16>(d, s);
 }
 
-// int8 A x int4 B: whole 128-value K stages and 32-bit source offsets
+// int8 A x int4 B: whole 128-value K stages, at least a ring's worth, at
+// least one whole tile each way, and 32-bit offsets inside a tile
 bool dma_w4a8_fits(const GemmDesc &d)
 {
-    if (d.K % 128 != 0)
+    if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX>::kStages)
+        return false;
+    if (d.M < kBM || d.N < kBN)
         return false;
     const int64_t lim = (int64_t)1 << 32;
-    if ((d.M - 1) * d.lda_b + d.K >= lim || (d.N - 1) * d.ldb_b + d.K / 2 >= lim)
+    if ((kBM - 1) * d.lda_b + d.K >= lim || (kBN - 1) * d.ldb_b + d.K / 2 >= lim)
         return false;
     return ((d.M + kBM - 1) / kBM) * ((d.N + kBN - 1) / kBN) >= 128;
 }
