@@ -55,7 +55,10 @@ constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
 constexpr int kEarlyLoads = 2;                // issued right after the barrier
-constexpr int kGroupM = 4;
+#ifndef QG_DMA_GROUP_M
+#define QG_DMA_GROUP_M 4
+#endif
+constexpr int kGroupM = QG_DMA_GROUP_M;      // tile rows that share B panels in L2
 constexpr int kOutStride = kBN + 16;          // LDS row stride of the int8 output tile
 
 // OP_MIX: int8 A x packed int4 B (W4A8); OP_MIXM: the same with B packed
@@ -485,25 +488,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             const bool vec_ok = (p.ldc & 15) == 0;
             auto requant_tile = [&](auto tier_tag) __attribute__((always_inline)) {
                 constexpr int TIER = decltype(tier_tag)::value;
+                // one 32-row band at a time, its four sub-tiles back to back,
+                // so that each 128-byte line of a row is written by
+                // consecutive stores (a line left partly written in L2 for
+                // long is written back in pieces)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v4i b4[4], m4[4], s4[4];
+                for (int i = 0; i < 4; ++i) {
+                    const int ml = wm * 128 + i * 32 + (lane & 31);
+                    const int rt = ZP ? prm[3][ml] : 0;
+                    const int zo = ZP ? p.out_zero : 0;
+                    const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
+                    int8_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128 + khalf * 16;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                        b4[q] = *(const v4i *)&prm[0][nl];
-                        m4[q] = *(const v4i *)&prm[1][nl];
-                        s4[q] = *(const v4i *)&prm[2][nl];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ml = wm * 128 + i * 32 + (lane & 31);
-                        const int rt = ZP ? prm[3][ml] : 0;
-                        const int zo = ZP ? p.out_zero : 0;
-                        const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
+                    for (int j = 0; j < 4; ++j) {
                         unsigned d[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
+                            const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                            const v4i b4 = *(const v4i *)&prm[0][nl];
+                            const v4i m4 = *(const v4i *)&prm[1][nl];
+                            const v4i s4 = *(const v4i *)&prm[2][nl];
                             int y[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -511,29 +515,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                                 if constexpr (ZP)
                                     a = wrap_sub(a, rt);
                                 if constexpr (TIER == 2)
-                                    y[e] = requant_one_s33(a, b4[q][e], m4[q][e], s4[q][e], zo,
-                                                           lo, hi);
+                                    y[e] = requant_one_s33(a, b4[e], m4[e], s4[e], zo, lo, hi);
                                 else if constexpr (TIER == 1)
-                                    y[e] = requant_one_s31(a, b4[q][e], m4[q][e], s4[q][e],
-                                                           1ll << ((s4[q][e] - 1) & 63), zo, lo,
-                                                           hi);
+                                    y[e] = requant_one_s31(a, b4[e], m4[e], s4[e],
+                                                           1ll << ((s4[e] - 1) & 63), zo, lo, hi);
                                 else
-                                    y[e] = requant_one(a, b4[q][e], m4[q][e], s4[q][e],
-                                                       1ll << ((s4[q][e] - 1) & 63), zo, lo, hi);
+                                    y[e] = requant_one(a, b4[e], m4[e], s4[e],
+                                                       1ll << ((s4[e] - 1) & 63), zo, lo, hi);
                             }
                             d[q] = pack4_i8(y[0], y[1], y[2], y[3]);
                         }
                         const auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
                         const auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
                         const v4i out = {(int)r02[0], (int)r02[1], (int)r13[0], (int)r13[1]};
-                        int8_t *dst = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128 + j * 32 +
-                                      khalf * 16;
+                        int8_t *dst = row + j * 32;
                         if (vec_ok) {
                             *(v4i *)dst = out;
                         } else {
                             for (int b = 0; b < 16; ++b)
                                 dst[b] = (int8_t)(out[b >> 2] >> (8 * (b & 3)));
                         }
+                        // one sub-tile's parameters in registers at a time:
+                        // hoisting a whole band's would spill
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             };
@@ -544,29 +548,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             else
                 requant_tile(std::integral_constant<int, 0>{});
         } else if constexpr (F16) {
-            // binary16: 4 adjacent columns of one row per 8-byte store
+            // binary16: 4 adjacent columns of one row per 8-byte store, a
+            // 32-row band at a time so that each row's lines fill from
+            // consecutive stores
             uint16_t *C = (uint16_t *)p.C;
+            const bool vec = (p.ldc & 3) == 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int i = 0; i < 4; ++i) {
+                const int ml = wm * 128 + i * 32 + (lane & 31);
+                const float sa = __int_as_float(prm[3][ml]);
+                uint16_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                    const int n = n0 + nl;
-                    const bool vec = (p.ldc & 3) == 0;
-                    const v4i sb4 = *(const v4i *)&prm[0][nl];
+                for (int j = 0; j < 4; ++j) {
+                    const v16i &a = acc[j * 4 + i];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ml = wm * 128 + i * 32 + (lane & 31);
-                        const int m = m0 + ml;
-                        const float sa = __int_as_float(prm[3][ml]);
-                        const v16i &a = acc[j * 4 + i];
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                        const v4i sb4 = *(const v4i *)&prm[0][nl];
                         unsigned short h[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
                             h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
                         }
-                        uint16_t *dst = C + (int64_t)m * p.ldc + n;
+                        uint16_t *dst = row + nl;
                         if (vec) {
                             v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
                                      (unsigned)h[2] | ((unsigned)h[3] << 16)};
@@ -579,22 +584,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 }
             }
         } else {
-            // raw int32: 4 adjacent columns of one row per 16-byte store
+            // raw int32: 4 adjacent columns of one row per 16-byte store, a
+            // 32-row band at a time so that each row's lines fill from
+            // consecutive stores
             int32_t *C = (int32_t *)p.C;
+            const bool vec = (p.ldc & 3) == 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int i = 0; i < 4; ++i) {
+                const int ml = wm * 128 + i * 32 + (lane & 31);
+                int32_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + wn * 128 + j * 32 + q * 8 + khalf * 4;
-                    const bool vec = (p.ldc & 3) == 0;
+                for (int j = 0; j < 4; ++j) {
+                    const v16i &a = acc[j * 4 + i];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = m0 + wm * 128 + i * 32 + (lane & 31);
-                        const v16i &a = acc[j * 4 + i];
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
                         v4i y;
                         for (int e = 0; e < 4; ++e)
                             y[e] = a[4 * q + e] >> ACC_SHIFT;
-                        int32_t *dst = C + (int64_t)m * p.ldc + n;
+                        int32_t *dst = row + nl;
                         if (vec) {
                             *(v4i *)dst = y;
                         } else {
