@@ -19,20 +19,31 @@
 //     the input zero point (0 for symmetric inputs): a tap of an output pixel
 //     is then one fixed LDS offset away from its (0, 0) tap, with no bounds
 //     test, and the padding costs nothing;
-//   * 16 consecutive pixels at an 80-byte stride fall in 16 different LDS
-//     bank groups, so the operand reads are conflict free;
+//   * the LDS is read with 16-byte reads, which gfx950 serves 16 lanes per
+//     cycle over 64 4-byte banks, the 16 lanes of a cycle being those that
+//     share lane bit 5 and the parity of lane bits 2..4 (measured).  Three
+//     choices make every operand read conflict free: an LDS row pitch that
+//     is congruent to Wo pixels modulo 256 bytes (so the bank of a pixel
+//     follows its linear index across row ends), lane row g taking channel
+//     chunk (0, 2, 1, 3)[g] (both operands, so the K pairing is kept), and,
+//     within each 16-pixel MFMA tile, the lane quads that share a cycle
+//     taking the odd and the even pixels respectively;
 //   * the workgroup's 64 weight rows (KH*KW*64 bytes each, OHWI) are copied
 //     with direct-to-LDS loads (global_load_lds_dwordx4, 1 KB of contiguous
 //     bytes per wave instruction), weight granule G of row oc stored at
-//     G ^ ((oc >> 2) & 3) of its 64-byte group for the same reason;
+//     G ^ ((oc >> 3) & 1), which with the chunk order above spreads each read
+//     cycle over all 16 bank groups;
 //   * with 64 input channels one tap is exactly one K step of
 //     v_mfma_i32_16x16x64_i8: weights are the first operand (rows = output
 //     channels), pixels the second; each wave owns 64 pixels x 64 channels
 //     (4 x 4 MFMA tiles), and the operands of tap t+1 are read from LDS
 //     while tap t is multiplied;
 //   * the requantize uses the cheapest exact form that all 64 shifts of the
-//     workgroup allow; the int8 tile goes back to LDS and leaves with
-//     16-byte stores, contiguous when C_out == 64.
+//     workgroup allow.  A lane holds 4 channels of one pixel per MFMA tile;
+//     a 4 x 4 transpose across the four 16-lane rows (v_permlane32_swap,
+//     then v_permlane16_swap) gives it 16 consecutive channels, written with
+//     one 16-byte store (1 KB contiguous per wave instruction when
+//     C_out == 64).
 // Two workgroups fit on a CU, so one stages its rows while the other
 // multiplies.
 #include <algorithm>
@@ -66,7 +77,8 @@ struct HaloArgs {
     int8_t *Y;
     int H, Wd, C_out, ph, pw, Ho, Wo;
     int tiles_per_img;
-    int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+    int in_bytes;  // LDS bytes of the staged input rows
+    int rowL;      // LDS bytes of one staged input row
     int pad4;                  // padding byte (the input zero point) x4
     int a_zero, b_zero, out_zero;  // ZP: the zero points
     int act_min, act_max;          // ZP: output clamp bounds
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
             const int pos = P * 1024 + 16 * lane;
             const int oc = pos / kRowW;
             const int G = (pos - oc * kRowW) >> 4;
-            const int sG = G ^ ((oc >> 2) & 3);
+            const int sG = G ^ ((oc >> 3) & 1);
             __builtin_amdgcn_global_load_lds((const glb_void_t *)(src + oc * kRowW + 16 * sG),
                                              (lds_void_t *)(WT + P * 1024), 16, 0, 0);
         }
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     // ---- input rows: LDS row r holds input row ih0 + r, LDS column c holds
     //      input column c - pw; the padding value outside the image ----
     const int colsL = p.Wd + 2 * p.pw;
-    const int rowL = colsL * kPixL;
+    const int rowL = p.rowL;
     const int nrow_in = oh_last - oh_first + KH;  // LDS rows this tile reads
     // rows ih_lo..ih_hi are one contiguous NHWC span of 16-byte granules;
     // a thread loads up to 8 of them per pass (loads past the end read the
@@ -183,14 +195,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 
     // ---- this lane's pixel in each of the wave's 4 M tiles, as the LDS
     //      offset of its (0, 0) tap; pixels past the tile reuse the last one ----
+    // lane column col stands for pixel pcol of each 16-pixel tile, and lane
+    // row g for channel chunk chk (both bank-conflict choices above)
+    const int pcol = 2 * (col & 7) + ((((col >> 2) ^ (col >> 3)) & 1) ? 0 : 1);
+    const int chk = ((g & 1) << 1) | (g >> 1);
     int abase[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int q = min(64 * wave + 16 * i + col, npix - 1);
+        const int q = min(64 * wave + 16 * i + pcol, npix - 1);
         const int pp = p0 + q;
         const int oh = pp / p.Wo;
         const int ow = pp - oh * p.Wo;
-        abase[i] = (oh - oh_first) * rowL + ow * kPixL + 16 * g;
+        abase[i] = (oh - oh_first) * rowL + ow * kPixL + 16 * chk;
     }
 
     // ZP: per-channel weight sums of the 64 weight rows in LDS, four threads
@@ -229,8 +245,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int oc = 16 * n + col;
-            const int G = 4 * t + g;
-            wt[n] = *(const v4i *)(WT + oc * kRowW + ((G ^ ((oc >> 2) & 3)) << 4));
+            const int G = 4 * t + chk;
+            wt[n] = *(const v4i *)(WT + oc * kRowW + ((G ^ ((oc >> 3) & 1)) << 4));
         }
     };
     read_tap(0, a[0], w[0]);
@@ -266,39 +282,49 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
         }
     }
 
-    // ---- requantize into LDS (the input rows are no longer needed) ----
-    __syncthreads();
-    // lane holds pixel 64*wave + 16*i + col and channels 16*n + 4*g + e; the
-    // requantize form is chosen once for the tile's 64 channels
+    // ---- requantize; lane holds pixel pcol of M tile i and channels
+    //      16*n + 4*g + e; the form is chosen once for the tile's 64
+    //      channels ----
     const int sh_l = prm[2 * kNT + lane];
+    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C_out + n0 + 16 * g;
     auto requant_tile = [&](auto tier_tag) {
         constexpr int TIER = decltype(tier_tag)::value;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int c0 = 16 * n + 4 * g;
-            const v4i b4 = *(const v4i *)&prm[c0];
-            const v4i m4 = *(const v4i *)&prm[kNT + c0];
-            const v4i s4 = *(const v4i *)&prm[2 * kNT + c0];
+        for (int i = 0; i < 4; ++i) {
+            unsigned x[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int n = 0; n < 4; ++n) {
+                const int c0 = 16 * n + 4 * g;
+                const v4i b4 = *(const v4i *)&prm[c0];
+                const v4i m4 = *(const v4i *)&prm[kNT + c0];
+                const v4i s4 = *(const v4i *)&prm[2 * kNT + c0];
                 int y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int x = ZP ? wrap_sub(acc[i][n][e], rt[i]) : acc[i][n][e];
+                    const int xa = ZP ? wrap_sub(acc[i][n][e], rt[i]) : acc[i][n][e];
                     const int zo = ZP ? p.out_zero : 0;
                     const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo, lo, hi);
+                        y[e] = requant_one_s33(xa, b4[e], m4[e], s4[e], zo, lo, hi);
                     else if constexpr (TIER == 1)
-                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
+                        y[e] = requant_one_s31(xa, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
                                                zo, lo, hi);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
+                        y[e] = requant_one(xa, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
                                            lo, hi);
                 }
-                const int q = 64 * wave + 16 * i + col;
-                *(unsigned *)(IN + q * 64 + c0) = pack4_i8(y[0], y[1], y[2], y[3]);
+                x[n] = pack4_i8(y[0], y[1], y[2], y[3]);
             }
+            // 4 x 4 transpose over the lane rows: row g receives dword g of
+            // rows 0..3, i.e. channels 16g .. 16g+15 in order
+            const auto r02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+            const auto r13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+            const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+            const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+            const v4i out = {(int)r01[0], (int)r01[1], (int)r23[0], (int)r23[1]};
+            const int q = 64 * wave + 16 * i + pcol;
+            if (q < npix)
+                *(v4i *)(ybase + (int64_t)q * p.C_out) = out;
         }
     };
     if (__builtin_amdgcn_ballot_w64(sh_l < 33) == 0)
@@ -307,14 +333,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
         requant_tile(std::integral_constant<int, 1>{});
     else
         requant_tile(std::integral_constant<int, 0>{});
-    __syncthreads();
-
-    // ---- 16-byte stores of the tile's npix x 64 output bytes ----
-    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C_out + n0;
-    for (int idx = tid; idx < npix * 4; idx += kWaves * 64) {
-        const int pix = idx >> 2, qq = idx & 3;
-        *(v4i *)(ybase + (int64_t)pix * p.C_out + 16 * qq) = *(const v4i *)(IN + pix * 64 + 16 * qq);
-    }
 }
 
 template <int KH, int KW, bool ZP>
@@ -348,13 +366,20 @@ int halo_rows(const ConvDesc &d)
     return std::min((kTP - 1) / d.Wo + 2, d.Ho) + d.KH - 1;
 }
 
-// LDS bytes of the input-row region (at least the kTP x 64-byte output
-// staging), rounded up to 1 KB so that the weight rows start aligned.
+// LDS bytes of one staged input row: Wd + 2*pw pixels of kPixL bytes, plus
+// the padding that makes the pitch congruent to Wo pixels modulo 256 bytes
+int halo_row_bytes(const ConvDesc &d)
+{
+    const int colsL = d.Wd + 2 * d.pw;
+    const int pad = (((d.Wo - colsL) * kPixL) % 256 + 256) % 256;
+    return colsL * kPixL + pad;
+}
+
+// LDS bytes of the input-row region, rounded up to 1 KB so that the weight
+// rows start aligned.
 int64_t halo_in_bytes(const ConvDesc &d)
 {
-    int64_t in = (int64_t)halo_rows(d) * (d.Wd + 2 * d.pw) * kPixL;
-    if (in < (int64_t)kTP * 64)
-        in = (int64_t)kTP * 64;
+    const int64_t in = (int64_t)halo_rows(d) * halo_row_bytes(d);
     return (in + 1023) & ~(int64_t)1023;
 }
 
@@ -392,6 +417,7 @@ hipError_t launch_conv_halo(const ConvDesc &d, hipStream_t s)
     a.Wo = d.Wo;
     a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
     a.in_bytes = (int)halo_in_bytes(d);
+    a.rowL = halo_row_bytes(d);
     a.pad4 = (int)(0x01010101u * (uint8_t)d.a_zero);
     a.a_zero = d.a_zero;
     a.b_zero = d.b_zero;
