@@ -55,6 +55,10 @@ constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
 constexpr int kEarlyLoads = 2;                // issued right after the barrier
+#ifndef QG_DMA_PRE_J1
+#define QG_DMA_PRE_J1 2
+#endif
+constexpr int kPreJ1 = QG_DMA_PRE_J1;          // read group 1 sub-tile columns before the barrier
 #ifndef QG_DMA_GROUP_M
 #define QG_DMA_GROUP_M 4
 #endif
@@ -164,6 +168,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : (MIX ? 4 : 0);
     constexpr int MG = 16 * STEPS_PER_READ;  // MFMAs per read group
     constexpr int DSG = G::kDsPerGroup;
+    // MFMAs of a stage before its barrier (read group 0, and the first
+    // kPreJ1 sub-tile columns of group 1) and after it (the rest of group 1,
+    // which covers the reads of the next stage's group 0)
+    constexpr int kMfmaPerJ = 4 * STEPS_PER_READ;
+    constexpr int kMfmaPre = MG + kPreJ1 * kMfmaPerJ;
+    constexpr int kMfmaPost = (4 - kPreJ1) * kMfmaPerJ;
+    constexpr int kPreMfmaPerLoad = (kMfmaPre - DSG) / (G::kLoads - kEarlyLoads);
+    static_assert(kPreMfmaPerLoad >= 1 && kMfmaPost >= DSG / 2, "stage schedule");
     constexpr bool RQ = EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP;
     constexpr bool ZP = EPI == EPI_REQUANT_ZP;
     constexpr bool F16 = EPI == EPI_F16;
@@ -419,7 +431,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             for (int l = kEarlyLoads; l < kLoadsPerStage; ++l)
                 issue(kt + kStages - 1, ps, l);
             mma_group(fa[0], fb[0], 0, 4);
-            mma_group(fa[1], fb[1], 0, 2);
+            if constexpr (kPreJ1 > 0)
+                mma_group(fa[1], fb[1], 0, kPreJ1);
 #pragma unroll
             for (int i = 0; i < DSG; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -427,11 +440,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             }
 #pragma unroll
             for (int i = 0; i < kLoadsPerStage - kEarlyLoads; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x008, kPreMfmaPerLoad, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // VMEM read
             }
             __builtin_amdgcn_sched_group_barrier(
-                0x008, MG + MG / 2 - DSG - 2 * (kLoadsPerStage - kEarlyLoads), 0);
+                0x008, kMfmaPre - DSG - kPreMfmaPerLoad * (kLoadsPerStage - kEarlyLoads), 0);
             // nothing crosses the barrier: the MFMAs before it keep the
             // matrix pipe busy while the waves meet
             __builtin_amdgcn_sched_barrier(0);
@@ -446,19 +459,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             // after the last stage this reads the next tile's first
             // fragments, which are read again once the epilogue is done
             read_group(ns, 0, fa[0], fb[0]);
-            mma_group(fa[1], fb[1], 2, 4);
+            mma_group(fa[1], fb[1], kPreJ1, 4);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kEarlyLoads; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
             }
 #pragma unroll
-            for (int i = 0; i < DSG / 2 - 2; ++i) {
+            for (int i = 0; i < DSG / 2 - kEarlyLoads; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, MG / 2 - DSG / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPost - DSG / 2, 0);
             rs = ns;
         }
 
