@@ -30,8 +30,14 @@
 //     so the four waves never queue 32 loads at once;
 //   * int4 operands are widened in registers (dev_common.hpp): a 16-byte
 //     fragment read of packed data covers two MFMA K steps;
-//   * the int8 epilogue requantizes into an LDS copy of the output tile and
-//     writes it back with row-contiguous 16-byte stores.
+//   * the grid is one workgroup per compute unit, walking its tiles; the
+//     ring runs across tile boundaries (a tile's last stages issue the next
+//     tile's first), and per-tile parameters come in by direct-to-LDS loads
+//     into a double buffer, so a tile starts with its operands in LDS;
+//   * the epilogue works from registers: the int8 results of each 32x32
+//     sub-tile row are regrouped across the two half-waves with
+//     v_permlane32_swap into 16-byte stores, a 32-row band at a time so that
+//     each output line fills from consecutive stores.
 #include <type_traits>
 
 #include "dev_common.hpp"
@@ -63,7 +69,6 @@ constexpr int kPreJ1 = QG_DMA_PRE_J1;          // read group 1 sub-tile columns 
 #define QG_DMA_GROUP_M 4
 #endif
 constexpr int kGroupM = QG_DMA_GROUP_M;      // tile rows that share B panels in L2
-constexpr int kOutStride = kBN + 16;          // LDS row stride of the int8 output tile
 
 // OP_MIX: int8 A x packed int4 B (W4A8); OP_MIXM: the same with B packed
 // high nibble first
