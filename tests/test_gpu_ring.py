@@ -9,7 +9,9 @@ binary16, W4A8 with either nibble order):
     take one tile more than others);
   * M and N that are not multiples of 256, so the bottom and right edge
     tiles are moved inward and overlap their neighbours;
-  * K at the ring's minimum (one ring of stages per tile) and just above it.
+  * K at the ring's minimum (one ring of stages per tile) and just above it;
+  * strided operands, no bias, and output row strides with and without the
+    16-byte alignment the vector stores need.
 Every row of the bottom edge tile and of its neighbour is compared, with a
 random sample of the rest, all bit for bit with the oracle.
 """
@@ -129,3 +131,43 @@ def test_w4a8_ring_walk(qg, orc, M, N, K, msb):
     want = orc.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows,
                                  msb_first=msb)
     assert np.array_equal(C[rows], want)
+
+
+# strided operands, no bias, and output row strides that do (ldc % 16 == 0)
+# and do not allow the 16-byte stores
+@pytest.mark.parametrize("ldc_extra", [16, 3])
+def test_s8s8_ring_walk_strided(qg, orc, ldc_extra):
+    M, N, K = 4100, 4400, 320
+    _say("s8s8 ring walk strided", M, N, K, ldc_extra)
+    d = datagen.gemm_s8s8(M, N, K, seed=9 + ldc_extra, shift=(36, 42))
+    Aw = np.zeros((M, K + 64), np.int8)
+    Aw[:, :K] = d["A"]
+    Bw = np.zeros((N, K + 32), np.int8)
+    Bw[:, :K] = d["B"]
+    At, Bt = dev(Aw), dev(Bw)
+    Cw = torch.full((M, N + ldc_extra), 99, dtype=torch.int8, device="cuda")
+    qg.qgemm_s8s8_requant(At[:, :K], Bt[:, :K], None, dev(d["mult"]), dev(d["shift"]),
+                          C=Cw[:, :N])
+    got = host(Cw)
+    rows = _rows(M, ldc_extra)
+    want = orc.gemm_s8s8_requant(d["A"], d["B"], None, d["mult"], d["shift"], rows=rows)
+    assert np.array_equal(got[rows, :N], want)
+    assert np.all(got[:, N:] == 99)  # nothing written past N
+
+
+@pytest.mark.parametrize("ldc_extra", [4, 1])
+def test_s4s4_ring_walk_output_stride(qg, orc, ldc_extra):
+    M, N, K = 2304, 4130, 512
+    _say("s4s4 ring walk output stride", M, N, K, ldc_extra)
+    d = datagen.gemm_s4s4(M, N, K, seed=21 + ldc_extra)
+    Ci = torch.full((M, N + ldc_extra), -7, dtype=torch.int32, device="cuda")
+    qg.qgemm_s4s4_i32(dev(d["A"]), dev(d["B"]), C=Ci[:, :N])
+    Ch = torch.full((M, N + ldc_extra), -1.0, dtype=torch.float16, device="cuda")
+    qg.qgemm_s4s4_f16(dev(d["A"]), dev(d["B"]), None, None, C=Ch[:, :N])
+    gi, gh = host(Ci), host(Ch)
+    rows = _rows(M, ldc_extra + 1)
+    assert np.array_equal(gi[rows, :N], orc.gemm_s4s4_i32(d["A"], d["B"], rows=rows))
+    assert np.all(gi[:, N:] == -7)
+    want_h = orc.gemm_s4s4_f16(d["A"], d["B"], None, None, rows=rows)
+    assert np.array_equal(gh[rows, :N].view(np.uint16), want_h.view(np.uint16))
+    assert np.all(gh[:, N:] == -1.0)
