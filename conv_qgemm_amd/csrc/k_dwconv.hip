@@ -20,7 +20,8 @@
 //     different bank groups;
 //   * the diagonal weight operands live in registers (12 per lane);
 //   * the requantize takes the cheapest exact form all 64 shifts of the
-//     slice allow, and the tile leaves through LDS with 16-byte stores.
+//     slice allow; a 4 x 4 lane transpose (permlane swaps) gives each lane
+//     16 consecutive channels of one pixel for a 16-byte store.
 // Other kernel sizes and strides use a direct kernel: one thread per output
 // pixel and 4 channels.
 #include <algorithm>
@@ -50,7 +51,7 @@ struct DwArgs {
     int8_t *Y;
     int H, Wd, C, KH, KW, sh, sw, ph, pw, Ho, Wo;
     int tiles_per_img;
-    int in_bytes;  // LDS bytes of the staged input rows (also the output staging)
+    int in_bytes;  // LDS bytes of the staged input rows
     // asymmetric form: the padding byte x4 and the zero points; the 3x3 path
     // takes zb = 0 with `bias` holding bias - za * sum_t w[t][c]
     int pad4, a_zero, b_zero, out_zero;
@@ -212,38 +213,49 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
                                                                  0, 0, 0);
     }
 
-    // ---- requantize into LDS; lane holds pixel 64*wave + 16*i + col and
-    //      channels 16*n + 4*g + e of the slice ----
-    __syncthreads();
+    // ---- requantize; lane holds pixel 64*wave + 16*i + col and channels
+    //      16*n + 4*g + e of the slice.  A 4 x 4 transpose across the four
+    //      16-lane rows (v_permlane32_swap, then v_permlane16_swap) gives
+    //      lane row g channels 16g .. 16g+15, written with one 16-byte store
+    //      when the slice has them ----
     const int sh_l = prm[2 * kCS + lane];
+    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C + c0 + 16 * g;
     auto requant_tile = [&](auto tier_tag) {
         constexpr int TIER = decltype(tier_tag)::value;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int cc = 16 * n + 4 * g;
-            const v4i b4 = *(const v4i *)&prm[cc];
-            const v4i m4 = *(const v4i *)&prm[kCS + cc];
-            const v4i s4 = *(const v4i *)&prm[2 * kCS + cc];
+        for (int i = 0; i < 4; ++i) {
+            unsigned x[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int n = 0; n < 4; ++n) {
+                const int cc = 16 * n + 4 * g;
+                const v4i b4 = *(const v4i *)&prm[cc];
+                const v4i m4 = *(const v4i *)&prm[kCS + cc];
+                const v4i s4 = *(const v4i *)&prm[2 * kCS + cc];
                 int y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int x = acc[i][n][e];
+                    const int xa = acc[i][n][e];
                     const int zo = ZP ? p.out_zero : 0;
                     const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
                     if constexpr (TIER == 2)
-                        y[e] = requant_one_s33(x, b4[e], m4[e], s4[e], zo, lo, hi);
+                        y[e] = requant_one_s33(xa, b4[e], m4[e], s4[e], zo, lo, hi);
                     else if constexpr (TIER == 1)
-                        y[e] = requant_one_s31(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
+                        y[e] = requant_one_s31(xa, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63),
                                                zo, lo, hi);
                     else
-                        y[e] = requant_one(x, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
+                        y[e] = requant_one(xa, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63), zo,
                                            lo, hi);
                 }
-                const int q = 64 * wave + 16 * i + col;
-                *(unsigned *)(IN + q * 64 + cc) = pack4_i8(y[0], y[1], y[2], y[3]);
+                x[n] = pack4_i8(y[0], y[1], y[2], y[3]);
             }
+            const auto r02 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+            const auto r13 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+            const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+            const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+            const v4i out = {(int)r01[0], (int)r01[1], (int)r23[0], (int)r23[1]};
+            const int q = 64 * wave + 16 * i + col;
+            if (q < npix && g < ngrp)
+                *(v4i *)(ybase + (int64_t)q * p.C) = out;
         }
     };
     // parameters of channels past the slice read as shift 31 (a valid value)
@@ -253,14 +265,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
         requant_tile(std::integral_constant<int, 1>{});
     else
         requant_tile(std::integral_constant<int, 0>{});
-    __syncthreads();
-
-    // ---- 16-byte stores of the tile's npix x cs output bytes ----
-    int8_t *ybase = p.Y + ((int64_t)b * HW + p0) * p.C + c0;
-    for (int idx = tid; idx < npix * ngrp; idx += kWaves * 64) {
-        const int pix = idx / ngrp, qq = idx - pix * ngrp;
-        *(v4i *)(ybase + (int64_t)pix * p.C + 16 * qq) = *(const v4i *)(IN + pix * 64 + 16 * qq);
-    }
 }
 
 // ---- any kernel size and stride: one thread per output pixel x 4 channels;
@@ -307,15 +311,12 @@ __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
 
 // LDS bytes of the staged input rows for a 3x3 conv with stride S: the
 // output rows a tile of kTP consecutive pixels touches (never more than the
-// image has), times S, plus the halo; at least the kTP x 64-byte output
-// staging; rounded to 1 KB.
+// image has), times S, plus the halo; rounded to 1 KB.
 int64_t dw_in_bytes(const ConvDesc &d)
 {
     const int64_t span = std::min<int64_t>((kTP - 1) / d.Wo + 1, d.Ho - 1);
     const int64_t rows = span * d.sh + d.KH;
     int64_t in = rows * (d.Wd + 2 * d.pw) * kPixL;
-    if (in < (int64_t)kTP * 64)
-        in = (int64_t)kTP * 64;
     return (in + 1023) & ~(int64_t)1023;
 }
 
