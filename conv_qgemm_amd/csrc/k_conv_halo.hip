@@ -10,8 +10,9 @@
 // tap reads the same input rows, so a workgroup stages those rows in LDS
 // once and reads all taps from there.
 //
-// Per workgroup (4 waves): 256 consecutive output pixels of one image times
-// 64 output channels.
+// Per workgroup (8 waves, one workgroup per CU): 392 consecutive output
+// pixels of one image (7 rows of a 56-wide image: 32 images x 8 bands make
+// one workgroup per CU of an MI355X) times 64 output channels.
 //   * the input rows those pixels touch (with the KH-1 halo rows) are read
 //     once with 16-byte loads and written to LDS with every pixel in 80
 //     bytes (64 channels + 16 unused), row by row with padding columns on
@@ -35,17 +36,21 @@
 //     cycle over all 16 bank groups;
 //   * with 64 input channels one tap is exactly one K step of
 //     v_mfma_i32_16x16x64_i8: weights are the first operand (rows = output
-//     channels), pixels the second; each wave owns 64 pixels x 64 channels
-//     (4 x 4 MFMA tiles), and the operands of tap t+1 are read from LDS
-//     while tap t is multiplied;
+//     channels), pixels the second; the band's 25 16-pixel tiles go to the
+//     waves in turn (wave w takes tiles w, w + 8, w + 16, and wave 0 also
+//     tile 24), so a SIMD multiplies 6 or 7 tiles x 64 channels, and the
+//     operands of tap t+1 are read from LDS while tap t is multiplied;
 //   * the requantize uses the cheapest exact form that all 64 shifts of the
 //     workgroup allow.  A lane holds 4 channels of one pixel per MFMA tile;
 //     a 4 x 4 transpose across the four 16-lane rows (v_permlane32_swap,
 //     then v_permlane16_swap) gives it 16 consecutive channels, written with
 //     one 16-byte store (1 KB contiguous per wave instruction when
 //     C_out == 64).
-// Two workgroups fit on a CU, so one stages its rows while the other
-// multiplies.
+// Measured on conv3x3 32x56x56x64->64 against 256-pixel, 4-wave
+// workgroups two to a CU (416 workgroups: 160 CUs ran two, the rest one):
+// 8.2 vs 8.8 us, and 10.0 vs 11.3 us with zero points.  With one wave per
+// SIMD instead (7 tiles each) the band is slower than either (9.1 us): the
+// second wave hides the LDS latency.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -60,12 +65,14 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-constexpr int kTP = 256;     // output pixels per workgroup
+constexpr int kTP = 392;     // output pixels per workgroup (7 rows of a 56-wide image)
+constexpr int kTiles = (kTP + 15) / 16;  // 16-pixel MFMA tiles per workgroup (25)
 constexpr int kNT = 64;      // output channels per workgroup
 constexpr int kCin = 64;     // input channels = bytes per input pixel
 constexpr int kPixL = 80;    // LDS bytes per staged input pixel
-constexpr int kWaves = 4;
-constexpr int kMaxLds = 80 * 1024;  // two workgroups per CU
+constexpr int kWaves = 8;    // two waves per SIMD
+constexpr int kTPW = (kTiles + kWaves - 1) / kWaves;  // MFMA tiles per wave: w, w + 8, ... < kTiles
+constexpr int kMaxLds = 160 * 1024;  // one workgroup per CU
 constexpr int kMaxDevices = 64;
 
 struct HaloArgs {
@@ -95,7 +102,7 @@ __device__ __forceinline__ void drain_and_barrier()
 // weight rows in LDS; x = acc - zb * rowsum + (bias - za * wsum + K za zb),
 // modulo 2^32.  The output zero point joins before the saturation.
 template <int KH, int KW, bool ZP>
-__global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
+__global__ __launch_bounds__(kWaves * 64, 1) void k_conv_halo(HaloArgs p)
 {
     constexpr int KK = KH * KW;
     constexpr int kRowW = KK * kCin;  // bytes of one weight row (one output channel)
@@ -107,6 +114,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the wave's last MFMA tile exists for the first kTiles % kWaves waves
+    const bool has_last = wave + kWaves * (kTPW - 1) < kTiles;
     const int col = lane & 15;
     const int g = lane >> 4;
 
@@ -199,10 +208,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     // row g for channel chunk chk (both bank-conflict choices above)
     const int pcol = 2 * (col & 7) + ((((col >> 2) ^ (col >> 3)) & 1) ? 0 : 1);
     const int chk = ((g & 1) << 1) | (g >> 1);
-    int abase[4];
+    int abase[kTPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = min(64 * wave + 16 * i + pcol, npix - 1);
+    for (int i = 0; i < kTPW; ++i) {
+        const int q = min(16 * (wave + kWaves * i) + pcol, npix - 1);
         const int pp = p0 + q;
         const int oh = pp / p.Wo;
         const int ow = pp - oh * p.Wo;
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
 
     // ZP: per-channel weight sums of the 64 weight rows in LDS, four threads
     // per row; the bias slot of prm becomes bias - za * wsum + K * za * zb
-    if constexpr (ZP) {
+    if (ZP && tid < 4 * kNT) {
         const int oc = tid >> 2, part = tid & 3;
         unsigned ws = 0;
         for (int G = part; G < KK * 4; G += 4) {
@@ -226,22 +235,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
             prm[oc] = (int)((unsigned)prm[oc] - (unsigned)p.a_zero * ws +
                             (unsigned)(KK * kCin) * (unsigned)(p.a_zero * p.b_zero));
     }
+    // every wave's requantize reads all 64 adjusted biases
+    if constexpr (ZP)
+        __syncthreads();
 
-    v4i acc[4][4];
+    v4i acc[kTPW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTPW; ++i)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             acc[i][n] = (v4i){0, 0, 0, 0};
-    unsigned rs[4] = {0, 0, 0, 0};  // ZP: this lane's 16 channels of each pixel's im2col row
+    unsigned rs[kTPW] = {};  // ZP: this lane's 16 channels of each pixel's im2col row
 
-    v4i a[2][4], w[2][4];
-    auto read_tap = [&](int t, v4i(&at)[4], v4i(&wt)[4]) {
+    v4i a[2][kTPW], w[2][4];
+    auto read_tap = [&](int t, v4i(&at)[kTPW], v4i(&wt)[4]) {
         const int kh = t / KW, kw = t - (t / KW) * KW;
         const int toff = kh * rowL + kw * kPixL;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            at[i] = *(const v4i *)(IN + abase[i] + toff);
+        for (int i = 0; i < kTPW; ++i)
+            if (i < kTPW - 1 || has_last)
+                at[i] = *(const v4i *)(IN + abase[i] + toff);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int oc = 16 * n + col;
@@ -255,14 +268,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
         if (t + 1 < KK)
             read_tap(t + 1, a[(t + 1) & 1], w[(t + 1) & 1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTPW; ++i) {
+            if (i == kTPW - 1 && !has_last)
+                continue;
 #pragma unroll
             for (int n = 0; n < 4; ++n)
                 acc[i][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[t & 1][n], a[t & 1][i],
                                                                  acc[i][n], 0, 0, 0);
+        }
         if constexpr (ZP) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kTPW; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     rs[i] = (unsigned)__builtin_amdgcn_sdot4(a[t & 1][i][e], 0x01010101,
@@ -271,10 +287,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     }
     // ZP: the four K groups of a pixel sit in lanes col, col + 16, col + 32,
     // col + 48; after the sum every one of them holds zb * (its im2col row sum)
-    int rt[4] = {0, 0, 0, 0};
+    int rt[kTPW] = {};
     if constexpr (ZP) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kTPW; ++i) {
             unsigned v = rs[i];
             v += (unsigned)__shfl_xor((int)v, 16);
             v += (unsigned)__shfl_xor((int)v, 32);
@@ -290,7 +306,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
     auto requant_tile = [&](auto tier_tag) {
         constexpr int TIER = decltype(tier_tag)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kTPW; ++i) {
+            if (i == kTPW - 1 && !has_last)
+                continue;
             unsigned x[4];
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
@@ -322,7 +340,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_conv_halo(HaloArgs p)
             const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
             const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
             const v4i out = {(int)r01[0], (int)r01[1], (int)r23[0], (int)r23[1]};
-            const int q = 64 * wave + 16 * i + pcol;
+            const int q = 16 * (wave + kWaves * i) + pcol;
             if (q < npix)
                 *(v4i *)(ybase + (int64_t)q * p.C_out) = out;
         }
