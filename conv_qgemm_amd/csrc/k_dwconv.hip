@@ -11,8 +11,11 @@
 // operand holds the weights on a diagonal (weight w[t][c] at K position
 // (t, c) of column c, zero elsewhere).  Three MFMAs then give 16 pixels x 16
 // channels of a 3x3 conv (taps 9..11 have zero weights).  Per workgroup
-// (4 waves): 256 consecutive output pixels of one image x a 64-channel
-// slice.
+// (8 waves, one workgroup per CU): 392 consecutive output pixels of one
+// image (7 rows of a 56-wide output, so 32 images make one workgroup per CU
+// of an MI355X) x a 64-channel slice; the 25 16-pixel MFMA tiles go to the
+// waves in turn (wave w takes tiles w, w + 8, w + 16, and wave 0 also
+// tile 24).
 //   * the input rows those pixels touch are staged once in LDS, every pixel
 //     in 80 bytes (the slice's 64 channels + 16 unused) with columns and
 //     rows of the padding value (the input zero point, 0 when symmetric), so
@@ -35,11 +38,13 @@ namespace qg {
 
 namespace {
 
-constexpr int kTP = 256;     // output pixels per workgroup
+constexpr int kTP = 392;     // output pixels per workgroup (7 rows of a 56-wide output)
+constexpr int kTiles = (kTP + 15) / 16;  // 16-pixel MFMA tiles per workgroup (25)
 constexpr int kCS = 64;      // channels per workgroup slice
 constexpr int kPixL = 80;    // LDS bytes per staged input pixel
-constexpr int kWaves = 4;
-constexpr int kMaxLds = 80 * 1024;
+constexpr int kWaves = 8;    // two waves per SIMD
+constexpr int kTPW = (kTiles + kWaves - 1) / kWaves;  // MFMA tiles per wave: w, w + 8, ... < kTiles
+constexpr int kMaxLds = 160 * 1024;  // one workgroup per CU
 constexpr int kMaxDevices = 64;
 
 struct DwArgs {
@@ -67,7 +72,7 @@ __device__ __forceinline__ void drain_and_barrier()
 // S: stride (both directions); ZP: the asymmetric form (padding a_zero, the
 // output zero point before the saturation)
 template <int S, bool ZP>
-__global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
+__global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
 {
     constexpr int KH = 3, KW = 3, KK = 9, kSlices = 3;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -77,6 +82,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the wave's last MFMA tile exists for the first kTiles % kWaves waves
+    const bool has_last = wave + kWaves * (kTPW - 1) < kTiles;
     const int col = lane & 15;
     const int g = lane >> 4;
 
@@ -173,12 +180,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
     }
     __syncthreads();
 
-    // ---- this lane's pixel in each of the wave's 4 M tiles (LDS offset of
+    // ---- this lane's pixel in each of the wave's M tiles (LDS offset of
     //      its (0, 0) tap) and its tap in each slice ----
-    int abase[4];
+    int abase[kTPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = min(64 * wave + 16 * i + col, npix - 1);
+    for (int i = 0; i < kTPW; ++i) {
+        const int q = min(16 * (wave + kWaves * i) + col, npix - 1);
         const int pp = p0 + q;
         const int oh = pp / p.Wo;
         const int ow = pp - oh * p.Wo;
@@ -191,29 +198,33 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
         toff[s] = (t / KW) * rowL + (t % KW) * kPixL;
     }
 
-    v4i acc[4][4];
+    v4i acc[kTPW][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTPW; ++i)
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             acc[i][n] = (v4i){0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < kSlices; ++s) {
-        v4i a[4][4];
+        v4i a[kTPW][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTPW; ++i)
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-                a[i][n] = *(const v4i *)(IN + abase[i] + toff[s] + 16 * n);
+                if (i < kTPW - 1 || has_last)
+                    a[i][n] = *(const v4i *)(IN + abase[i] + toff[s] + 16 * n);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kTPW; ++i) {
+            if (i == kTPW - 1 && !has_last)
+                continue;
 #pragma unroll
             for (int n = 0; n < 4; ++n)
                 acc[i][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wd[s][n], a[i][n], acc[i][n],
                                                                  0, 0, 0);
+        }
     }
 
-    // ---- requantize; lane holds pixel 64*wave + 16*i + col and channels
+    // ---- requantize; lane holds pixel 16*(wave + 8*i) + col and channels
     //      16*n + 4*g + e of the slice.  A 4 x 4 transpose across the four
     //      16-lane rows (v_permlane32_swap, then v_permlane16_swap) gives
     //      lane row g channels 16g .. 16g+15, written with one 16-byte store
@@ -223,7 +234,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
     auto requant_tile = [&](auto tier_tag) {
         constexpr int TIER = decltype(tier_tag)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kTPW; ++i) {
+            if (i == kTPW - 1 && !has_last)
+                continue;
             unsigned x[4];
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void k_dwconv3x3(DwArgs p)
             const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
             const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
             const v4i out = {(int)r01[0], (int)r01[1], (int)r23[0], (int)r23[1]};
-            const int q = 64 * wave + 16 * i + col;
+            const int q = 16 * (wave + kWaves * i) + col;
             if (q < npix && g < ngrp)
                 *(v4i *)(ybase + (int64_t)q * p.C) = out;
         }
