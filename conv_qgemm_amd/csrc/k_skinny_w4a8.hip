@@ -28,7 +28,10 @@
 //     activations as the second operand;
 //   * activations live in registers, loaded once when K <= 8192 and double-
 //     buffered per unit otherwise; values past the end of K are zeroed, so
-//     whatever sits in LDS there (clamped or stale bytes) adds nothing;
+//     whatever sits in LDS there (clamped or stale bytes) adds nothing.
+//     When K <= 8192, six of the eight waves bring theirs through LDS regions
+//     that are idle until the first barrier, with loads in which
+//     neighbouring lanes read contiguous bytes;
 //   * one barrier per unit: after it, this unit's bytes have landed for every
 //     wave and the other slot is free, so the next unit's loads go out at
 //     once; the 8 partial 16x16 sums of a finished group are added by one
@@ -57,8 +60,8 @@ constexpr int kMaxGroups = 32;                 // column groups per workgroup (L
 constexpr int kRedOff = 2 * kSlot;                          // v4i red[2][kWaves][64]
 constexpr int kPrmOff = kRedOff + 2 * kWaves * 64 * 16;     // int prm[3][kMaxGroups*16]
 constexpr int kOutOff = kPrmOff + 3 * kMaxGroups * 16 * 4;  // unsigned outb[kMaxGroups][64]
-constexpr int kLdsBytes = kOutOff + kMaxGroups * 64 * 4;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+constexpr int kLdsBytes = 160 * 1024;
+static_assert(kOutOff + kMaxGroups * 64 * 4 <= kLdsBytes, "LDS budget");
 
 struct SkinnyArgs {
     const int8_t *A;
@@ -76,9 +79,13 @@ struct SkinnyArgs {
 
 // Wait until this wave's vector memory operations (the direct-to-LDS loads
 // included) and LDS operations are done, then meet the other waves.
+// The wait is the builtin, not inline asm, so that the compiler knows every
+// load (direct-to-LDS ones included) has landed behind the barrier and adds
+// no waits of its own for them.
 __device__ __forceinline__ void drain_and_barrier()
 {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // ONE: K fits one chunk, so the activations are loaded once.
@@ -131,9 +138,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     };
 
     // ---- direct-to-LDS loads of unit u into slot `slot` ----
-    // wave w loads rows 2w and 2w+1, kPieces KB each; a piece lying wholly
-    // past the end of the row is skipped (its LDS bytes meet zero
-    // activations), a piece crossing it reads clamped in-bounds addresses
+    // wave w loads rows 2w and 2w+1, kPieces KB each; a piece crossing or
+    // lying past the end of the row reads clamped in-bounds addresses (those
+    // LDS bytes meet zero activations).  Every wave issues exactly kLoads,
+    // which the wait for the staged activations below counts on.
     auto issue = [&](int u, int slot) {
         const int i = u / nchunks, c = u - i * nchunks;
         const int grp = group_of(i);
@@ -141,8 +149,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         for (int l = 0; l < kLoads; ++l) {
             const int r = 2 * wave + l / kPieces, piece = l % kPieces;
             const int kb0 = c * kRowBytes + piece * 1024;  // packed byte offset in the row
-            if (kb0 >= KbB)
-                continue;
             const int n = min(grp * 16 + r, p.N - 1);  // clamped rows are never stored
             const int kb = min(kb0 + ((lane ^ r) << 4), KbB - 16);
             uint8_t *dst = lds + slot * kSlot + (r * kPieces + piece) * 1024;
@@ -193,6 +199,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         outb[i][lane] = pack4_i8(y[0], y[1], y[2], y[3]);
     };
 
+    // ---- per-column parameters of this workgroup's columns (at most
+    // kMaxGroups * 16, one per thread), copied by 4-byte direct-to-LDS loads
+    // at the end of the first unit (until its barrier their region holds
+    // staged activations); the first reduce reads them a barrier later.  Loads into
+    // registers here would make the compiler wait for every load in flight,
+    // the next unit's included, before the first LDS read that follows. ----
+    static_assert(kMaxGroups * 16 <= kWaves * 64, "one column per thread");
+    auto load_prm = [&]() {
+        if (tid < ng * 16) {
+            const int n = min(group_of(tid >> 4) * 16 + (tid & 15), p.N - 1);
+            if (p.bias)
+                __builtin_amdgcn_global_load_lds((const glb_void_t *)(p.bias + n),
+                                                 (lds_void_t *)&prm[0][wave * 64], 4, 0, 0);
+            else
+                prm[0][tid] = 0;
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(p.mult + n),
+                                             (lds_void_t *)&prm[1][wave * 64], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)(p.shift + n),
+                                             (lds_void_t *)&prm[2][wave * 64], 4, 0, 0);
+        }
+    };
     // unit u: its bytes are in slot u&1 and its activations in `af`; the
     // next unit's loads (and activations, when K has several chunks) go out
     // right after the barrier
@@ -214,17 +241,50 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         consume(slot, af);
         if (c == nchunks - 1)
             red[i & 1][wave][lane] = acc;
+        // behind this unit's LDS reads: the compiler cannot tell the copy's
+        // LDS range from the slot's and would wait for it before them
+        if (u == 0)
+            load_prm();
     };
 
-    // ---- per-column parameters of this workgroup's columns into LDS ----
-    for (int c = tid; c < ng * 16; c += kWaves * 64) {
-        const int n = min(group_of(c >> 4) * 16 + (c & 15), p.N - 1);
-        prm[0][c] = p.bias ? p.bias[n] : 0;
-        prm[1][c] = p.mult[n];
-        prm[2][c] = p.shift[n];
+    // ---- first activations.  A load in the MFMA layout touches 16 token
+    // rows and 64 bytes of each, with neighbouring lanes on different rows;
+    // loads in which neighbouring lanes read contiguous bytes pull the
+    // 128 KB a CU needs 1 us faster per launch (measured).  Until the first
+    // barrier, slot 1, the reduction buffer and the parameter and output
+    // blocks (with the rest of the LDS) are unused: waves 0..5 copy
+    // their 16 x 1 KB slices there with direct-to-LDS loads (token t's KB in
+    // one instruction, lane L fetching granule L ^ t) and read them back in
+    // the MFMA layout, granule G of token t at position G ^ t, which puts the
+    // 16 lanes of every LDS read cycle on 16 different bank groups.  Waves
+    // 6 and 7 load theirs directly.  K > kChunk keeps the direct loads. ----
+    constexpr int kStagedWaves = 6;
+    static_assert(4 * 16 * 1024 == kSlot && kPrmOff - kRedOff == 16 * 1024 &&
+                      kLdsBytes - kPrmOff == 16 * 1024,
+                  "staging regions: slot 1 for waves 0-3, the reduction buffer for wave 4, "
+                  "the parameter and output blocks for wave 5");
+    const bool staged = ONE && wave < kStagedWaves;
+    const int stage_off = wave < 4 ? kSlot + wave * 16 * 1024 : wave == 4 ? kRedOff : kPrmOff;
+    if (staged) {
+        const int kbase = wave * (kSteps * 64);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int8_t *src = p.A + (int64_t)min((int)blockIdx.y * 16 + t, p.M - 1) * p.lda +
+                                min(kbase + 16 * (lane ^ t), p.K - 16);
+            __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
+                                             (lds_void_t *)(lds + stage_off + t * 1024), 16, 0, 0);
+        }
+    } else {
+        load_acts(0, af0);
     }
-    load_acts(0, af0);
     issue(0, 0);
+    if (staged) {
+        // the copies above are done once at most kLoads later loads are out
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+            af0[s] = *(const v4i *)(lds + stage_off + col * 1024 + (((kofs(s) >> 4) ^ col) << 4));
+    }
     if (ONE)
         fix_acts(0, af0);
     for (int u = 0; u < nunits; u += 2) {
