@@ -262,8 +262,10 @@ CONV_GEOMS = [
     (1, 12, 13, 64, 128, 3, 3, (1, 1), (1, 1)),   # two output-channel tiles
     (2, 10, 9, 64, 64, 3, 3, (1, 1), (0, 0)),     # no padding
     (1, 9, 30, 64, 192, 3, 3, (1, 1), (2, 0)),    # unequal padding, three channel tiles
-    (2, 40, 3, 64, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: a tile spans 86 rows
-    (1, 4, 100, 64, 64, 3, 3, (1, 1), (1, 1)),    # wide rows, near the LDS limit
+    (2, 40, 3, 64, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: one tile spans the image
+    (1, 4, 100, 64, 64, 3, 3, (1, 1), (1, 1)),    # wide rows: a 392-pixel band and an 8-pixel one
+    (2, 30, 30, 64, 64, 3, 3, (1, 1), (1, 1)),    # bands of 392 pixels starting mid-row
+    (1, 200, 3, 64, 64, 3, 3, (1, 1), (1, 1)),    # a band spanning 131 rows
     (1, 5, 6, 64, 64, 1, 1, (1, 1), (1, 1)),      # 1x1 with padding: border pixels see zeros
     (3, 17, 19, 64, 64, 3, 3, (1, 1), (1, 1)),    # several images, partial last tile
 ]
@@ -300,7 +302,10 @@ DW_GEOMS = [
     (2, 9, 8, 32, 3, 3, (2, 2), (1, 1)),
     (1, 10, 7, 96, 3, 3, (1, 1), (0, 0)),     # a full and a 32-channel slice
     (1, 20, 16, 16, 3, 3, (1, 1), (1, 1)),    # the MCU front-end's 20x16x16 map
-    (2, 40, 3, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: a tile spans 86 rows
+    (2, 40, 3, 64, 3, 3, (1, 1), (1, 1)),     # 3 pixels wide: one tile spans the image
+    (2, 30, 30, 64, 3, 3, (1, 1), (1, 1)),    # bands of 392 pixels starting mid-row
+    (1, 200, 3, 64, 3, 3, (1, 1), (1, 1)),    # a band spanning 131 rows
+    (1, 61, 60, 64, 3, 3, (2, 2), (1, 1)),    # stride 2, bands starting mid-row
     (1, 13, 30, 128, 3, 3, (2, 2), (1, 1)),   # stride 2, two slices
     (3, 17, 19, 64, 3, 3, (1, 1), (2, 0)),    # unequal padding, several images
     (1, 8, 8, 16, 5, 5, (1, 1), (2, 2)),      # direct kernel: 5x5
