@@ -226,14 +226,16 @@ def test_w4a8_small(qg, M, N, K):
     assert np.array_equal(host(C), want)
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 1000, 8192), (17, 4100, 8128), (64, 96, 8192)])
+@pytest.mark.parametrize("M,N,K", [(40, 1000, 8192), (17, 4100, 8128), (64, 96, 8192),
+                                   (16, 1, 8192), (64, 8, 32), (63, 17, 4096)])
 @pytest.mark.parametrize("msb", [False, True])
 def test_w4a8_skinny_staged_activations(qg, M, N, K, msb):
     """K <= 8192 on the weight-streaming kernel: six of its eight waves bring
     their activation slices through LDS (token-swizzled direct-to-LDS copies
     read back in the MFMA layout), two load them directly.  Several 16-token
     row blocks (M > 16), a ragged last block, a K tail short of the 8192-value
-    chunk and a ragged N, in both nibble orders."""
+    chunk and a ragged N, in both nibble orders; one column (a single group,
+    whose parameters arrive at the end of its only unit) and K = 32."""
     _say("w4a8 staged", M, N, K, msb)
     d = datagen.gemm_w4a8(M, N, K, seed=M + N + K, shift=(37, 43))
     C = qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
