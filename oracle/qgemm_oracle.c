@@ -31,8 +31,8 @@
  *   - packed INT4: element 2i is the LOW nibble of byte i, element 2i+1 the
  *     high nibble; codes are 4-bit two's complement (0x8 = -8).
  *   - bias is added to the int32 accumulator before the Q31 multiply.
- *   - ">>" on a negative int64 is an arithmetic (flooring) shift.  GCC
- *     documents this for signed right shifts; the oracle is built with gcc.
+ *   - the page's ">>" of a negative product is an arithmetic (flooring)
+ *     shift, so the requantize rounds exact halves up (toward +infinity).
  *   - requant domain: acc + bias fits int32, mult in [0, 2^31-1],
  *     shift in [1, 63]; outside it the oracle reports ORC_E_DOMAIN/RANGE
  *     instead of producing a value.
@@ -69,22 +69,45 @@ int orc_int4_at(const uint8_t *row, int64_t i)
     return code < 8 ? code : code - 16;
 }
 
-/* ---- O3: Q31 requantize ([MCU-CONV] §2.3, bias per §3.3) ---- */
+/* ---- O3: Q31 requantize ([MCU-CONV] §2.3, bias per §3.3) ----
+ * The output code is the product x * M of x = acc + bias and the Q31
+ * multiplier, scaled down by 2^shift and rounded to the nearest integer; the
+ * page rounds by adding half an LSB before an arithmetic (flooring) shift,
+ * so a value exactly halfway between two integers goes up, toward +infinity.
+ * The code is then saturated to the int8 range.  Below, the rounding is
+ * stated through the quotient and remainder of a floor division, in 128-bit
+ * integers, so that no intermediate can overflow for any shift in [1, 63]. */
+
+/* Nearest integer to t / 2^s, exact halves rounded up. */
+static __int128 round_half_up_pow2(__int128 t, int s)
+{
+    const __int128 unit = (__int128)1 << s;
+    __int128 q = t / unit, r = t % unit;   /* C division truncates toward 0 */
+    if (r < 0) {                           /* make q the floor, 0 <= r < unit */
+        q -= 1;
+        r += unit;
+    }
+    return 2 * r >= unit ? q + 1 : q;      /* a remainder of half or more rounds up */
+}
+
+/* v limited to [lo, hi]. */
+static int8_t saturate(__int128 v, int32_t lo, int32_t hi)
+{
+    if (v < lo)
+        return (int8_t)lo;
+    if (v > hi)
+        return (int8_t)hi;
+    return (int8_t)v;
+}
+
 int orc_requant(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int8_t *out)
 {
-    int64_t x = acc + (int64_t)bias;
+    const int64_t x = acc + bias;
     if (x < INT32_MIN || x > INT32_MAX)
         return ORC_E_RANGE;
     if (shift < 1 || shift > 63 || mult < 0)
         return ORC_E_DOMAIN;
-    int64_t t = x * (int64_t)mult;          /* |t| < 2^62 */
-    t = t + ((int64_t)1 << (shift - 1));    /* half an LSB */
-    t = t >> shift;                         /* arithmetic shift (gcc) */
-    if (t > 127)
-        t = 127;
-    if (t < -128)
-        t = -128;
-    *out = (int8_t)t;
+    *out = saturate(round_half_up_pow2((__int128)x * mult, shift), -128, 127);
     return ORC_OK;
 }
 
@@ -408,8 +431,8 @@ int orc_dwconv2d_nhwc_s8_requant(const int8_t *X, const int8_t *Wt,
  * sum_k (A[m][k] - za) * (B[n][k] - zb), written out below term by term. ---- */
 
 /* Q31 requantize with an output zero point and a fused activation: the
- * shifted value plus out_zero, clamped to [act_min, act_max] inside the int8
- * range.  [VOYAGER] §3.1 fuses the activation into the GEMM and requantize
+ * rounded value (as in orc_requant) plus out_zero, clamped to
+ * [act_min, act_max] inside the int8 range.  [VOYAGER] §3.1 fuses the activation into the GEMM and requantize
  * (Conv -> DQ -> ReLU -> Q becomes one operator); on codes with zero point
  * out_zero, ReLU is the clamp at act_min = out_zero, and (-128, 127) is the
  * plain int8 saturation. */
@@ -423,11 +446,8 @@ int orc_requant_zp(int64_t acc, int32_t bias, int32_t mult, int32_t shift, int32
         return ORC_E_DOMAIN;
     if (act_min < -128 || act_max > 127 || act_min > act_max)
         return ORC_E_DOMAIN;
-    int64_t t = (int64_t)mult * x;          /* |t| < 2^62 */
-    t += (int64_t)1 << (shift - 1);         /* half an LSB */
-    t >>= shift;                            /* arithmetic shift (gcc) */
-    t += out_zero;                          /* output zero point */
-    *out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));
+    const __int128 y = round_half_up_pow2((__int128)x * mult, shift);
+    *out = saturate(y + out_zero, act_min, act_max);  /* zero point, then the clamp */
     return ORC_OK;
 }
 

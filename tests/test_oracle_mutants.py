@@ -20,12 +20,19 @@ MUTANTS = {
     "nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
                      "(i % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
     "no_sign_extension": ("return code < 8 ? code : code - 16;", "return code;"),
-    "no_rounding_term": ("t = t + ((int64_t)1 << (shift - 1));", "t = t;"),
-    "rounding_off_by_one": ("((int64_t)1 << (shift - 1))", "((int64_t)1 << shift)"),
-    "saturation_low": ("if (t < -128)\n        t = -128;", "if (t < -127)\n        t = -127;"),
-    "bias_dropped": ("int64_t x = acc + (int64_t)bias;", "int64_t x = acc;"),
-    "bias_after_multiply": ("int64_t t = x * (int64_t)mult; ",
-                            "int64_t t = acc * (int64_t)mult + bias; "),
+    "no_rounding_term": ("return 2 * r >= unit ? q + 1 : q;", "return q;"),
+    "ties_rounded_down": ("return 2 * r >= unit ? q + 1 : q;", "return 2 * r > unit ? q + 1 : q;"),
+    "truncating_division": ("if (r < 0) {", "if (0) {"),
+    "rounding_unit_doubled": ("const __int128 unit = (__int128)1 << s;",
+                              "const __int128 unit = (__int128)1 << (s + 1);"),
+    "saturation_low": ("round_half_up_pow2((__int128)x * mult, shift), -128, 127)",
+                       "round_half_up_pow2((__int128)x * mult, shift), -127, 127)"),
+    "bias_dropped": ("const int64_t x = acc + bias;\n    if (x < INT32_MIN || x > INT32_MAX)\n"
+                     "        return ORC_E_RANGE;\n    if (shift < 1 || shift > 63 || mult < 0)\n",
+                     "const int64_t x = acc;\n    if (x < INT32_MIN || x > INT32_MAX)\n"
+                     "        return ORC_E_RANGE;\n    if (shift < 1 || shift > 63 || mult < 0)\n"),
+    "bias_after_multiply": ("*out = saturate(round_half_up_pow2((__int128)x * mult, shift)",
+                            "*out = saturate(round_half_up_pow2((__int128)acc * mult + bias, shift)"),
     "k_reversed": ("acc += (int64_t)a[k] * (int64_t)b[k];",
                    "acc += (int64_t)a[k] * (int64_t)b[K - 1 - k];"),
     "k_dropped_term": ("for (int64_t k = 0; k < K; ++k)\n        acc += (int64_t)a[k] * (int64_t)b[k];",
@@ -48,13 +55,12 @@ MUTANTS = {
                          "float a = v;\n            if (a > amax)"),
     "quant_nibble_swap": ("if (k % 2 == 0)\n                    *byte",
                           "if (k % 2 == 1)\n                    *byte"),
-    "zp_out_zero_dropped": ("t += out_zero;", "t += 0;"),
-    "zp_out_zero_after_clamp": ("t += out_zero;                          /* output zero point */\n"
-                                "    *out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));",
-                                "*out = (int8_t)((t > act_max ? act_max : (t < act_min ? act_min : t))"
-                                " + out_zero);"),
-    "act_clamp_ignored": ("*out = (int8_t)(t > act_max ? act_max : (t < act_min ? act_min : t));",
-                          "*out = (int8_t)(t > 127 ? 127 : (t < -128 ? -128 : t));"),
+    "zp_out_zero_dropped": ("saturate(y + out_zero, act_min, act_max)",
+                            "saturate(y, act_min, act_max)"),
+    "zp_out_zero_after_clamp": ("*out = saturate(y + out_zero, act_min, act_max);",
+                                "*out = (int8_t)(saturate(y, act_min, act_max) + out_zero);"),
+    "act_clamp_ignored": ("saturate(y + out_zero, act_min, act_max)",
+                          "saturate(y + out_zero, -128, 127)"),
     "zp_a_zero_dropped": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",
                           "acc += ((int64_t)a[k]) * ((int64_t)b[k] - zb);"),
     "zp_b_zero_sign": ("acc += ((int64_t)a[k] - za) * ((int64_t)b[k] - zb);",
