@@ -503,7 +503,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 s31 = s31 && sh4[e] >= 31;
             }
             int8_t *C = (int8_t *)p.C;
-            const bool vec_ok = (p.ldc & 15) == 0;
+            // 16-byte stores need every row start and the tile's first
+            // column on 16 bytes: an edge tile moved inward starts at
+            // n0 = N - 256, which need not be
+            const bool vec_ok = ((p.ldc | n0) & 15) == 0;
             auto requant_tile = [&](auto tier_tag) __attribute__((always_inline)) {
                 constexpr int TIER = decltype(tier_tag)::value;
                 // one 32-row band at a time, its four sub-tiles back to back,
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             // 32-row band at a time so that each row's lines fill from
             // consecutive stores
             uint16_t *C = (uint16_t *)p.C;
-            const bool vec = (p.ldc & 3) == 0;
+            const bool vec = ((p.ldc | n0) & 3) == 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ml = wm * 128 + i * 32 + (lane & 31);
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             // 32-row band at a time so that each row's lines fill from
             // consecutive stores
             int32_t *C = (int32_t *)p.C;
-            const bool vec = (p.ldc & 3) == 0;
+            const bool vec = ((p.ldc | n0) & 3) == 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ml = wm * 128 + i * 32 + (lane & 31);

@@ -171,3 +171,40 @@ def test_s4s4_ring_walk_output_stride(qg, orc, ldc_extra):
     want_h = orc.gemm_s4s4_f16(d["A"], d["B"], None, None, rows=rows)
     assert np.array_equal(gh[rows, :N].view(np.uint16), want_h.view(np.uint16))
     assert np.all(gh[:, N:] == -1.0)
+
+
+def test_s8s8_ring_walk_edge_tile_unaligned_column(qg, orc):
+    """A 16-byte-multiple output stride (4112) with N = 4100: the right edge
+    tile starts at column N - 256 = 3844, which is not on 16 bytes, so that
+    tile must take the narrow stores while the others keep the 16-byte ones."""
+    M, N, K, ldc = 2304, 4100, 256, 4112
+    _say("s8s8 ring walk unaligned edge column", M, N, K, ldc)
+    d = datagen.gemm_s8s8(M, N, K, seed=41, shift=(36, 42))
+    Cw = torch.full((M, ldc), 99, dtype=torch.int8, device="cuda")
+    qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                          dev(d["shift"]), C=Cw[:, :N])
+    got = host(Cw)
+    rows = _rows(M, 41)
+    want = orc.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"], rows=rows)
+    assert np.array_equal(got[rows, :N], want)
+    assert np.all(got[:, N:] == 99)
+
+
+def test_s4s4_ring_walk_edge_tile_unaligned_column(qg, orc):
+    """int32 and binary16 outputs with a 4-element-multiple stride (4132) and
+    N = 4130: the right edge tile starts at column 3874, off the 16-byte
+    (int32) and 8-byte (binary16) alignment of its 4-column stores."""
+    M, N, K, ldc = 2304, 4130, 512, 4132
+    _say("s4s4 ring walk unaligned edge column", M, N, K, ldc)
+    d = datagen.gemm_s4s4(M, N, K, seed=43)
+    Ci = torch.full((M, ldc), -7, dtype=torch.int32, device="cuda")
+    qg.qgemm_s4s4_i32(dev(d["A"]), dev(d["B"]), C=Ci[:, :N])
+    Ch = torch.full((M, ldc), -1.0, dtype=torch.float16, device="cuda")
+    qg.qgemm_s4s4_f16(dev(d["A"]), dev(d["B"]), None, None, C=Ch[:, :N])
+    gi, gh = host(Ci), host(Ch)
+    rows = _rows(M, 43)
+    assert np.array_equal(gi[rows, :N], orc.gemm_s4s4_i32(d["A"], d["B"], rows=rows))
+    assert np.all(gi[:, N:] == -7)
+    want_h = orc.gemm_s4s4_f16(d["A"], d["B"], None, None, rows=rows)
+    assert np.array_equal(gh[rows, :N].view(np.uint16), want_h.view(np.uint16))
+    assert np.all(gh[:, N:] == -1.0)
