@@ -372,6 +372,36 @@ qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, i
     return launched(qg::run_s8s8_requant_zp(d, a_zero, b_zero, workspace, (hipStream_t)stream));
 }
 
+qg_status qgemm_s8s8_requant_zp_noalloc(const int8_t *A, int64_t lda, const int8_t *B,
+                                        int64_t ldb, const int32_t *bias, const int32_t *mult,
+                                        const int32_t *shift, int32_t a_zero, int32_t b_zero,
+                                        int32_t out_zero, int32_t act_min, int32_t act_max,
+                                        int8_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                        void *stream)
+{
+    if (!A || !B || !C || !mult || !shift)
+        return QG_ERR_NULLPTR;
+    qg_status st = check_gemm(A, lda, false, B, ldb, false, C, ldc, 1, M, N, K, kMaxDim);
+    if (st == QG_OK)
+        st = check_params(bias, mult, shift);
+    if (st != QG_OK)
+        return st;
+    if (!zero_point_ok(a_zero) || !zero_point_ok(b_zero) || !zero_point_ok(out_zero) ||
+        !act_ok(act_min, act_max))
+        return QG_ERR_INVALID;
+    if (qg::zp_gemm_workspace_bytes(M, N) > qg::kNoAllocScratchBytes)
+        return QG_ERR_INVALID;
+    int cus = 0;
+    if ((st = check_device(&cus)) != QG_OK)
+        return st;
+    void *ws = nullptr;
+    if (qg::noalloc_scratch(&ws) != hipSuccess)
+        return QG_ERR_LAUNCH;
+    qg::GemmDesc d{A, lda, B, ldb, bias, mult, shift, C, ldc, M, N, K, cus, nullptr, out_zero,
+                   false, act_min, act_max};
+    return launched(qg::run_s8s8_requant_zp(d, a_zero, b_zero, ws, (hipStream_t)stream));
+}
+
 size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32_t Wd,
                                                  int32_t C_out, int32_t KH, int32_t KW,
                                                  int32_t stride_h, int32_t stride_w,

@@ -25,6 +25,8 @@
 // Row sums use v_dot4_i32_i8 against 0x01010101 (four bytes per
 // instruction), one wave per row, 16-byte loads with eight in flight per
 // lane; they are memory-bound passes over A and B.
+#include <atomic>
+
 #include "dev_common.hpp"
 #include "launch.hpp"
 
@@ -250,6 +252,47 @@ hipError_t run_dwconv_zp(ConvDesc d, void *ws, hipStream_t s)
         d.bias = cterm;
     }
     return launch_dwconv_nhwc(d, s);
+}
+
+// ---- the allocation-free asymmetric GEMM: its compensation sums go to a
+//      file-scope device array instead of a caller workspace.  Every GPU the
+//      library runs on holds its own copy for the life of the process, and
+//      every call on that GPU shares it: calls that overlap on one GPU (two
+//      streams, or two host threads) race on it.  Each call writes every
+//      entry it reads (cterm[n] for n < N, rterm[m] for m < M) before the
+//      GEMM kernel reads it, so nothing needs clearing between calls. ----
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// device address of `scratch` on each device, taken once per device with
+// that device current; in host code the array's name is only a stand-in
+std::atomic<void *> g_scratch[kScratchDevices];
+
+}  // namespace
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kScratchDevices)
+        return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace qg

@@ -97,6 +97,11 @@ int64_t zp_gemm_workspace_bytes(int64_t M, int64_t N);
 int64_t zp_conv_workspace_bytes(int64_t C_out, int64_t pixels);
 int64_t zp_dw_workspace_bytes(int64_t C);
 hipError_t run_s8s8_requant_zp(GemmDesc d, int za, int zb, void *ws, hipStream_t s);
+// The allocation-free asymmetric GEMM keeps its compensation sums in a
+// file-scope device array of kNoAllocScratchBytes (k_zp.hip); noalloc_scratch
+// gives that array's address on the current device.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)1 << 20;
+hipError_t noalloc_scratch(void **ptr);
 hipError_t run_conv_zp(ConvDesc d, void *ws, hipStream_t s);
 hipError_t run_dwconv_zp(ConvDesc d, void *ws, hipStream_t s);
 

@@ -69,6 +69,9 @@ def _load():
     lib.qgemm_s8s8_requant_zp.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, P,
                                           I64, I64, I64, I64, P, Z, P]
     lib.qgemm_s8s8_requant_zp.restype = S
+    lib.qgemm_s8s8_requant_zp_noalloc.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32,
+                                                  I32, P, I64, I64, I64, I64, P]
+    lib.qgemm_s8s8_requant_zp_noalloc.restype = S
     lib.qconv2d_nhwc_s8_requant_zp_workspace_size.argtypes = [I32] * 10
     lib.qconv2d_nhwc_s8_requant_zp_workspace_size.restype = Z
     lib.qconv2d_nhwc_s8_requant_zp.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P] + \
@@ -91,6 +94,7 @@ EXPORTS = ("qgemm_s8s8_requant", "qgemm_s4s4_i32", "qgemm_s4s4_f16", "qgemm_w4a8
            "qgemm_w4a8_requant_msb",
            "qconv2d_nhwc_s8_requant", "qdwconv2d_nhwc_s8_requant", "qquant_per_token",
            "qgemm_s8s8_requant_zp_workspace_size", "qgemm_s8s8_requant_zp",
+           "qgemm_s8s8_requant_zp_noalloc",
            "qconv2d_nhwc_s8_requant_zp_workspace_size", "qconv2d_nhwc_s8_requant_zp",
            "qdwconv2d_nhwc_s8_requant_zp_workspace_size", "qdwconv2d_nhwc_s8_requant_zp",
            "qg_status_string", "qg_version")
@@ -385,6 +389,31 @@ def qgemm_s8s8_requant_zp(A, B, bias, mult, shift, a_zero, b_zero, out_zero, C=N
                                    int(out_zero), int(act[0]), int(act[1]), _ptr(C), C.stride(0),
                                    M, N, K, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "qgemm_s8s8_requant_zp")
+    return C
+
+
+def qgemm_s8s8_requant_zp_noalloc(A, B, bias, mult, shift, a_zero, b_zero, out_zero, C=None,
+                                  stream=None, act=(-128, 127)):
+    """qgemm_s8s8_requant_zp through the library's allocation-free entry
+    point: no workspace, the compensation sums stay in the library's own
+    per-GPU array (M + N up to about 262,000; calls that overlap on one GPU
+    race on it).  With C given, nothing is allocated on this path."""
+    _mat(A, torch.int8, "A")
+    _mat(B, torch.int8, "B")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.int8, device=A.device)
+    _mat(C, torch.int8, "C")
+    st = lib.qgemm_s8s8_requant_zp_noalloc(_ptr(A), A.stride(0), _ptr(B), B.stride(0),
+                                           _ptr(_vec(bias, N, "bias")),
+                                           _ptr(_vec(mult, N, "mult")),
+                                           _ptr(_vec(shift, N, "shift")), int(a_zero),
+                                           int(b_zero), int(out_zero), int(act[0]), int(act[1]),
+                                           _ptr(C), C.stride(0), M, N, K, _stream(stream))
+    _check(st, "qgemm_s8s8_requant_zp_noalloc")
     return C
 
 

@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer is DEVICE memory owned by the caller.  The library never
- *     allocates, frees or synchronizes, and keeps no mutable state.
+ *     allocates, frees or synchronizes.  It keeps no mutable state, except
+ *     the per-GPU scratch array of qgemm_s8s8_requant_zp_noalloc.
  *   - stream: a hipStream_t (NULL = default stream).  A call validates its
  *     arguments on the host, enqueues its kernels on `stream` and returns;
  *     the result is ready when the stream reaches that point.  A fault in a
@@ -257,6 +258,27 @@ qg_status qgemm_s8s8_requant_zp(const int8_t *A, int64_t lda, const int8_t *B, i
                                 int32_t act_min, int32_t act_max, int8_t *C, int64_t ldc,
                                 int64_t M, int64_t N, int64_t K, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/*
+ * qgemm_s8s8_requant_zp_noalloc -- qgemm_s8s8_requant_zp without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (less workspace / workspace_bytes), result
+ * and errors as qgemm_s8s8_requant_zp.  The compensation sums live in a
+ * 1 MiB array inside the library, one per GPU, held until the process ends:
+ * the call allocates nothing, and returns QG_ERR_INVALID when
+ * 4 * (ceil(M / 64) + ceil(N / 64)) * 64 > 1048576 (about M + N <= 262,000).
+ * Every call on one GPU shares that array: calls that may overlap on the
+ * same GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  QG_ERR_LAUNCH also covers a failure to find the array's
+ * address on the current device.
+ */
+qg_status qgemm_s8s8_requant_zp_noalloc(const int8_t *A, int64_t lda, const int8_t *B,
+                                        int64_t ldb, const int32_t *bias, const int32_t *mult,
+                                        const int32_t *shift, int32_t a_zero, int32_t b_zero,
+                                        int32_t out_zero, int32_t act_min, int32_t act_max,
+                                        int8_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                        void *stream);
 
 size_t qconv2d_nhwc_s8_requant_zp_workspace_size(int32_t batch, int32_t H, int32_t Wd,
                                                  int32_t C_out, int32_t KH, int32_t KW,

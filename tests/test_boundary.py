@@ -109,6 +109,12 @@ def s8z(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5
                                         ldc, M, N, K, ws, wsb, None)
 
 
+def s8n(qg, A=P, lda=64, B=P, ldb=64, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, lo=-128,
+        hi=127, C=P, ldc=64, M=32, N=64, K=64):
+    return qg.lib.qgemm_s8s8_requant_zp_noalloc(A, lda, B, ldb, bias, mult, shift, za, zb, zo, lo,
+                                                hi, C, ldc, M, N, K, None)
+
+
 def cvz(qg, X=P, W=P, bias=P, mult=P, shift=P, za=3, zb=-4, zo=5, lo=-128, hi=127, Y=P, batch=1,
         H=8, Wd=8, C_in=16, C_out=16, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, ws=WS, wsb=1 << 20):
     return qg.lib.qconv2d_nhwc_s8_requant_zp(X, W, bias, mult, shift, za, zb, zo, lo, hi, Y,
@@ -266,6 +272,31 @@ def test_invalid_zero_point_forms(qg):
     assert qg.lib.qgemm_s8s8_requant_zp_workspace_size(0, 5) == 0
     assert qg.lib.qconv2d_nhwc_s8_requant_zp_workspace_size(1, 2, 8, 16, 5, 3, 1, 1, 1, 1) == 0
     assert qg.lib.qdwconv2d_nhwc_s8_requant_zp_workspace_size(0) == 0
+
+
+def test_invalid_noalloc_form(qg):
+    """The allocation-free asymmetric GEMM checks what qgemm_s8s8_requant_zp
+    checks, and rejects shapes whose compensation sums exceed its 1 MiB
+    per-GPU array: 4 * (ceil(M/64) + ceil(N/64)) * 64 bytes."""
+    for kw in ("A", "B", "C", "mult", "shift"):
+        assert s8n(qg, **{kw: NULL}) == qg.QG_ERR_NULLPTR, kw
+    E = qg.QG_ERR_INVALID
+    for kw in ("za", "zb", "zo"):
+        assert s8n(qg, **{kw: 128}) == E, kw
+        assert s8n(qg, **{kw: -129}) == E, kw
+    assert s8n(qg, lo=10, hi=9) == E
+    assert s8n(qg, K=40) == E
+    assert s8n(qg, M=0) == E
+    assert s8n(qg, A=P + 8) == E
+    assert s8n(qg, M=131072, N=131073, ldc=131088) == E
+    assert s8n(qg, M=262081, N=64) == E
+    import torch
+    if torch.cuda.is_available():
+        return
+    # exactly at the limit the call passes validation and stops at the device
+    assert s8n(qg, M=131072, N=131072, ldc=131072) == qg.QG_ERR_NO_DEVICE
+    assert s8n(qg, M=262080, N=64) == qg.QG_ERR_NO_DEVICE
+    assert s8n(qg, bias=NULL) == qg.QG_ERR_NO_DEVICE
 
 
 def test_valid_call_without_gpu_reports_no_device(qg):
