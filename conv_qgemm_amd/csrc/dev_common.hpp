@@ -133,6 +133,21 @@ __device__ __forceinline__ unsigned short f32_to_f16_bits(float u)
     return __builtin_bit_cast(unsigned short, (_Float16)u);
 }
 
+// One 16-byte direct-to-LDS load per lane through a raw buffer resource:
+// lane L reads base + voff + soff (voff per lane, soff uniform) and writes
+// LDS at lds + 16 L.  Reads at or past `nbytes` return zeros.  The resource
+// is a scalar value the compiler builds once; a per-lane 32-bit offset costs
+// one VGPR and no address arithmetic, where a flat 64-bit address costs a
+// VGPR pair and a 64-bit add per load.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t nbytes,
+                                                  uint32_t voff, uint32_t soff, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+                                          0x00020000),
+        (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ unsigned pack4_i8(int a, int b, int c, int d)
 {
     return (unsigned)(a & 0xFF) | ((unsigned)(b & 0xFF) << 8) | ((unsigned)(c & 0xFF) << 16) |

@@ -1,6 +1,6 @@
 // k_gemm_dma.hip -- the large-GEMM kernel: 256x256 output tiles on the
 // gfx950 int8 MFMA, operands streamed global->LDS by the direct-to-LDS
-// loads (global_load_lds_dwordx4) through a 4-stage ring, with the
+// buffer loads (buffer_load_dwordx4 ... lds) through a 4-stage ring, with the
 // per-channel Q31 requantize (or a raw int32 store) fused into the
 // accumulator writeback.
 //
@@ -18,7 +18,11 @@
 //     writes 64 lanes x 16 bytes contiguously, so the swizzle is chosen on
 //     the source side: LDS slot (row, p) receives logical chunk
 //     p ^ ((row >> 2) & 3) of that row, which spreads the 16 rows read in
-//     one LDS cycle of an MFMA operand fetch over all banks;
+//     one LDS cycle of an MFMA operand fetch over all banks.  The loads go
+//     through buffer resources: a lane's offset inside a tile is one VGPR,
+//     fixed for the whole walk, and the tile and stage enter as the scalar
+//     offset, so the loop forms no per-lane addresses (a flat 64-bit address
+//     per load cost about 2.5% of the s8s8 8192^3 time);
 //   * three stages are in flight while one is multiplied.  Each stage is
 //     read as two groups of 16-byte fragments; the second group's reads
 //     overlap the first group's MFMAs, and the next stage's first group is
@@ -110,6 +114,7 @@ struct DmaArgs {
     void *C;
     int64_t ldc;
     int M, N, K;
+    uint32_t a_bytes, b_bytes;  // bytes of A and B the buffer loads may read
     int tiles_m, tiles_n;
     const int32_t *rterm;  // EPI_REQUANT_ZP: per-row term, or null
     int out_zero;          // EPI_REQUANT_ZP: output zero point
@@ -311,10 +316,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         uint8_t *dst = lds + slot * kStage +
                        (isb ? kStageA + wave * 4096 + (l - LA) * 1024
                             : wave * (64 * kRowA) + l * 1024);
-        const uint8_t *g = isb ? p.B + (nxt ? b_nxt : b_cur) + (int64_t)s * kRowB
-                               : p.A + (nxt ? a_nxt : a_cur) + (int64_t)s * kRowA;
-        __builtin_amdgcn_global_load_lds((const glb_void_t *)(g + src[l]), (lds_void_t *)dst, 16,
-                                         0, 0);
+        const int64_t off = isb ? (nxt ? b_nxt : b_cur) + (int64_t)s * kRowB
+                                : (nxt ? a_nxt : a_cur) + (int64_t)s * kRowA;
+        buffer_load_lds16(isb ? (const void *)p.B : (const void *)p.A,
+                          isb ? p.b_bytes : p.a_bytes, src[l], (uint32_t)off, dst);
     };
 
     // ---- fragment addresses inside a stage: read group g covers chunk
@@ -678,6 +683,8 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     a.M = (int)d.M;
     a.N = (int)d.N;
     a.K = (int)d.K;
+    a.a_bytes = (uint32_t)(d.M * d.lda_b);
+    a.b_bytes = (uint32_t)(d.N * d.ldb_b);
     a.tiles_m = (int)((d.M + kBM - 1) / kBM);
     a.tiles_n = (int)((d.N + kBN - 1) / kBN);
     a.rterm = d.rterm;
@@ -697,8 +704,8 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
 
 // The ring kernel takes whole 64-byte K rows, at least a ring's worth of
 // them (the ring then only ever holds stages of this tile and the next), at
-// least one whole tile each way (edge tiles move inward), and 32-bit offsets
-// inside a tile.
+// least one whole tile each way (edge tiles move inward), and operands of
+// under 4 GiB (32-bit buffer offsets).
 bool dma_gemm_fits(const GemmDesc &d, bool int4)
 {
     const int64_t kb = int4 ? d.K / 2 : d.K;
@@ -706,8 +713,9 @@ bool dma_gemm_fits(const GemmDesc &d, bool int4)
         return false;
     if (d.M < kBM || d.N < kBN)
         return false;
+    // each operand inside one 32-bit buffer range
     const int64_t lim = (int64_t)1 << 32;
-    if ((kBM - 1) * d.lda_b + kb >= lim || (kBN - 1) * d.ldb_b + kb >= lim)
+    if (d.M * d.lda_b >= lim || d.N * d.ldb_b >= lim)
         return false;
     // enough 256x256 tiles to fill the chip
     return ((d.M + kBM - 1) / kBM) * ((d.N + kBN - 1) / kBN) >= 128;
@@ -734,7 +742,7 @@ hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
 }
 
 // int8 A x int4 B: whole 128-value K stages, at least a ring's worth, at
-// least one whole tile each way, and 32-bit offsets inside a tile
+// least one whole tile each way, and operands of under 4 GiB
 bool dma_w4a8_fits(const GemmDesc &d)
 {
     if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX>::kStages)
@@ -742,7 +750,7 @@ bool dma_w4a8_fits(const GemmDesc &d)
     if (d.M < kBM || d.N < kBN)
         return false;
     const int64_t lim = (int64_t)1 << 32;
-    if ((kBM - 1) * d.lda_b + d.K >= lim || (kBN - 1) * d.ldb_b + d.K / 2 >= lim)
+    if (d.M * d.lda_b >= lim || d.N * d.ldb_b >= lim)
         return false;
     return ((d.M + kBM - 1) / kBM) * ((d.N + kBN - 1) / kBN) >= 128;
 }

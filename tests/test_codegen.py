@@ -2,7 +2,8 @@
 here to AMD assembly; no GPU needed).  Two silent regressions these catch:
 the accumulator array demoted to scratch memory (private segment), and the
 compiler waiting for every direct-to-LDS load (vmcnt(0)) inside the main
-loop, which serialises the 4-stage ring."""
+loop, which serialises the 4-stage ring.  The loop is also checked to issue
+its loads as buffer loads with no per-lane address arithmetic."""
 import os
 import re
 import subprocess
@@ -66,7 +67,11 @@ def test_main_loop_shape(asm):
         # operand kind: 8 int8 x int8, 4 int4 x int4, 3 / 5 int8 x int4
         kind = int(re.search(r"k_gemm_dmaILi(\d)E", name).group(1))
         loads = 12 if kind in (3, 5) else 8
-        assert sum("global_load_lds_dwordx4" in ln for ln in loop) == loads, name
+        assert sum(re.search(r"buffer_load_dwordx4 .* offen lds", ln) is not None
+                   for ln in loop) == loads, name
+        # no per-lane address arithmetic for the loads: the loop's only
+        # 64-bit VALU ops would be address adds
+        assert not any(ln.startswith(("v_lshl_add_u64", "v_add_co_u32")) for ln in loop), name
         assert sum("v_mfma_i32_32x32x32_i8" in ln for ln in loop) == (32 if kind == 8 else 64), name
 
 
