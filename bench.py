@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized GEMM / conv hot path on one MI355X.
 
-One step is one call of every entry point on its workload:
+One step is one call of each of the five workloads of the problem
+statement, which together run every step of the path:
   pointwise  qgemm_s8s8_requant  M=320 N=64 K=64 (1x1 conv, 20x16 pixels)
   s4s4       qgemm_s4s4_i32      M=N=K=4096, raw int32 out
   conv3x3    qconv2d_nhwc_s8_requant  batch 32, 56x56, 64->64, 3x3 s1 p1
   w4a8       qgemm_w4a8_requant  M=16 tokens, K=8192, N=28672 (skinny)
-  w4a8_prefill  qgemm_w4a8_requant  M=2048 tokens, same weights (tiled)
+  s8s8       qgemm_s8s8_requant  M=N=K=8192
+The other entry points run on their own workloads as extra legs, reported
+beside the step but not part of its value:
   dw3x3      qdwconv2d_nhwc_s8_requant  batch 32, 56x56, 64 channels, 3x3 s1 p1
   quant_a8   qquant_per_token    8192 tokens x 8192 channels, bfloat16 -> int8
              codes + float32 scales (the s8s8 A operand; no integer ops)
-  s8s8       qgemm_s8s8_requant  M=N=K=8192
+  w4a8_prefill  qgemm_w4a8_requant  M=2048 tokens, same weights (ring kernel)
   conv3x3_zp, s8s8_zp  the asymmetric calls (qconv2d_nhwc_s8_requant_zp,
              qgemm_s8s8_requant_zp) on the same arrays with zero points on
              the input, the weights and the output; their time includes the
@@ -20,11 +23,16 @@ Each workload rotates through enough copies of its buffers that every call
 reads HBM rather than the 256 MB Infinity Cache (the pointwise case is
 L2-sized and reported hot).
 
-Prints ONE JSON line: whole-step int TOPS as `value`, per-workload times,
-TOPS, GB/s and fractions of the INT8 MFMA and HBM peaks, the roofline of the
-dominant kernel (HIP events on the launch stream around a graph replay of
-the timed calls), and the CPU oracle timed on a bounded sample of the same
-step.
+Two calibration legs measure the board's practical ceilings in the same run
+(libqgcalib.so): a read-only HBM stream and an int8 matrix-core stream on
+random operands, with the engine clock it ran at.  The GFX clock the driver
+reports is sampled during every workload's timed replays.
+
+Prints ONE JSON line: the step's int TOPS as `value` (median per-call
+times), per-workload times, TOPS, GB/s and fractions of the published INT8
+MFMA and HBM peaks and of the calibrated ceilings, the roofline of the
+dominant kernel (HIP events on the launch stream around graph replays of
+the timed calls), and the CPU oracle timed on a bounded sample of the step.
 """
 from __future__ import annotations
 
@@ -43,6 +51,10 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published (8 TB/s)
 METRIC = "int TOPS + % of INT8 MFMA peak (or HBM GB/s % peak) per qgemm config"
 ORDER = ["pointwise", "dw3x3", "quant_a8", "w4a8", "conv3x3", "conv3x3_zp", "s4s4",
          "w4a8_prefill", "s8s8", "s8s8_zp"]
+# the problem statement's five workloads: one call of each is a step
+STEP = ("pointwise", "s4s4", "conv3x3", "w4a8", "s8s8")
+MFMA_BOUND = ("s8s8", "s8s8_zp", "s4s4", "conv3x3", "conv3x3_zp", "pointwise", "w4a8_prefill")
+HBM_BOUND = ("w4a8", "quant_a8", "dw3x3")
 # buffer sets per workload so that the rotation exceeds the Infinity Cache
 ROTATE = {"pointwise": 1, "s4s4": 7, "conv3x3": 40, "conv3x3_zp": 40, "dw3x3": 40,
           "quant_a8": 3, "w4a8": 5, "w4a8_prefill": 3, "s8s8": 3, "s8s8_zp": 3}
@@ -301,54 +313,180 @@ def hbm_copy_gbs(torch, nbytes=1 << 30, iters=10):
     return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def _csv_rows(path):
-    import csv
-    import glob
-    files = [path] if os.path.isfile(path) else sorted(
-        glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
-    for f in files:
-        with open(f) as fh:
-            yield from csv.DictReader(fh)
+def _calib_lib():
+    import ctypes
+    path = os.path.join(ROOT, "conv_qgemm_amd", "libqgcalib.so")
+    lib = ctypes.CDLL(path)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.qgc_stream_read.argtypes = [P, I64, P, I32, I32, P]
+    lib.qgc_stream_read.restype = I32
+    lib.qgc_mfma_stream.argtypes = [P, I32, P, P, I32, P]
+    lib.qgc_mfma_stream.restype = I32
+    lib.qgc_wall_clock_khz.argtypes = []
+    lib.qgc_wall_clock_khz.restype = I32
+    return lib
 
 
-def summarize_trace(stats_csv, title, cmd):
-    """Markdown table of a rocprofv3 --kernel-trace --stats kernel summary."""
-    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
-             "```", cmd, "```", "",
-             "| kernel | calls | avg us | min us | max us | % of GPU time |",
-             "|---|---|---|---|---|---|"]
-    for r in _csv_rows(stats_csv):
-        if "AverageNs" not in r:
-            continue
-        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.2f} |")
-    return "\n".join(lines)
-
-
-def summarize_pmc(name, fetch_dir, write_dir, copy_bytes=1 << 30):
-    """One traffic line for `name` from two rocprofv3 --pmc runs of
-    `bench.py --config name` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
-    Every dispatch that is not a copy kernel belongs to the workload; the
-    1 GiB device copy of hbm_copy_gbs() in the same run calibrates the
-    counter (factor = known bytes / what the counter reads for that copy)."""
+def read_calibration(torch, reps=5):
+    """Best read-only streaming rates (GB/s) over a few launch shapes, with
+    16-byte loads, grid-stride, `unroll` loads in flight per thread:
+      read_gb_s          a 1 GiB buffer (4x the Infinity Cache) per launch;
+      read_gb_s_117mb    a 117,440,512-byte buffer per launch (the skinny
+                         W4A8 weight matrix), five copies in rotation so
+                         that each launch reads HBM: the like-for-like
+                         ceiling of a bandwidth-bound kernel of that size,
+                         launch and ramp included."""
+    lib = _calib_lib()
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
     out = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        work, copies = [], []
-        for r in _csv_rows(d):
-            if r.get("Counter_Name") != counter:
-                continue
-            v = float(r["Counter_Value"]) * 1024.0
-            (copies if "copy" in r["Kernel_Name"].lower() else work).append(v)
-        if not work or not copies:
-            raise SystemExit(f"no {counter} rows for the workload or the copy kernel in {d}")
-        calib = copy_bytes / max(copies)
-        out[counter] = (sum(work) / len(work), calib)
-    (f, cf), (w, cw) = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    total = f * cf + w * cw
-    return (f"traffic workload={name} src_sha={src_sha(KERNEL_SOURCES[name])} "
-            f"bytes_per_launch={int(total)} fetch_bytes_raw={int(f)} write_bytes_raw={int(w)} "
-            f"calib_fetch={cf:.4f} calib_write={cw:.4f}")
+    for key, nbytes, ncopy, nrep in (("read_gb_s", 1 << 30, 1, reps),
+                                     ("read_gb_s_117mb", 117440512, 5, 20)):
+        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+                for _ in range(ncopy)]
+        best = (0.0, None)
+        for grid in (2048, 4096, 8192, 16384):
+            for unroll in (4, 8):
+                def go(i):
+                    rc = lib.qgc_stream_read(bufs[i % ncopy].data_ptr(), nbytes, sink.data_ptr(),
+                                             grid, unroll, ctypes_stream(st))
+                    if rc != 0:
+                        raise RuntimeError(f"qgc_stream_read: hip error {rc}")
+                for i in range(ncopy):
+                    go(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for i in range(nrep):
+                    go(i)
+                e1.record(st)
+                torch.cuda.synchronize()
+                gbs = nbytes * nrep / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if gbs > best[0]:
+                    best = (gbs, f"grid {grid} x 256 threads, {unroll} x 16-byte loads in flight")
+        out[key] = round(best[0], 1)
+        out[key.replace("gb_s", "shape")] = best[1]
+        del bufs
+    return out
+
+
+def mfma_calibration(torch, cus, iters=20000, reps=5, seed=99):
+    """int8 matrix-core ceiling on random operands: v_mfma_i32_32x32x32_i8
+    back to back, 16 accumulators per wave, 4 waves per CU, one workgroup
+    per CU; the median of `reps` launches of ~5 ms.  The clock it ran at is
+    the shader-clock counter over the constant-rate counter around the loop
+    (s_memtime / s_memrealtime), times the latter's rate."""
+    import numpy as np
+    lib = _calib_lib()
+    g = np.random.default_rng(seed)
+    ops = torch.from_numpy(g.integers(-128, 127, size=cus * 4 * 8 * 64 * 16, endpoint=True,
+                                      dtype=np.int8)).cuda()
+    clk = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(cus * 256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    wall_khz = lib.qgc_wall_clock_khz()
+    res = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        rc = lib.qgc_mfma_stream(ops.data_ptr(), iters, clk.data_ptr(), sink.data_ptr(), cus,
+                                 ctypes_stream(st))
+        e1.record(st)
+        if rc != 0:
+            raise RuntimeError(f"qgc_mfma_stream: hip error {rc}")
+        torch.cuda.synchronize()
+        if r == 0:
+            continue  # warm-up launch
+        t = e0.elapsed_time(e1) * 1e-3
+        c = clk.cpu().numpy().reshape(cus, 4).astype(np.float64)
+        ratio = (c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1)
+        res.append((cus * 4 * iters * 16 * 65536 / t / 1e12, float(np.median(ratio))))
+    res.sort()
+    tops, ratio = res[len(res) // 2]
+    return {"mfma_random_tops": round(tops, 1),
+            "mfma_random_frac_of_peak": round(tops / PEAK_INT8_TOPS, 4),
+            "mfma_clock_mhz": round(ratio * wall_khz / 1e3, 1) if wall_khz else None,
+            "wall_clock_khz": wall_khz,
+            "shape": f"{cus} workgroups x 4 waves x {iters} x 16 MFMA 32x32x32 i8, "
+                     f"random int8 operands, median of {reps} launches"}
+
+
+def ctypes_stream(st):
+    """The raw hipStream_t of a torch stream, for a ctypes call."""
+    return st.cuda_stream
+
+
+class ClockSampler:
+    """The GFX clock and socket power the driver reports (amdsmi GPU
+    metrics: the mean of the per-XCD current_gfxclks, current_socket_power),
+    sampled every few ms on a host thread; means over a time window.  Absent
+    (None) where amdsmi cannot be opened."""
+
+    def __init__(self, period=0.004):
+        import threading
+        self.samples = []
+        self.ok = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            if self._read() is None:
+                return
+            self.ok = True
+        except Exception:
+            return
+        self._stop = False
+        self._period = period
+        self._t = threading.Thread(target=self._run, daemon=True)
+        self._t.start()
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = m.get("current_gfxclks")
+        clks = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 10000] \
+            if isinstance(clks, (list, tuple)) else []
+        if not clks:
+            return None
+        pw = m.get("current_socket_power")
+        pw = float(pw) if isinstance(pw, (int, float)) and 0 < pw < 100000 else float("nan")
+        return sum(clks) / len(clks), pw
+
+    def _run(self):
+        while not self._stop:
+            try:
+                r = self._read()
+                if r is not None:
+                    self.samples.append((time.perf_counter(), r[0], r[1]))
+            except Exception:
+                pass
+            time.sleep(self._period)
+
+    def mean(self, t0, t1):
+        """(mean MHz, mean W, samples) over [t0, t1]."""
+        v = [(c, w) for t, c, w in self.samples if t0 <= t <= t1]
+        if not v:
+            return None, None, 0
+        w = [x[1] for x in v if x[1] == x[1]]
+        return (round(sum(x[0] for x in v) / len(v), 1),
+                round(sum(w) / len(w), 1) if w else None, len(v))
+
+    def close(self):
+        if self.ok:
+            self._stop = True
+            self._t.join(timeout=1)
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+
+LABELS = {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
+          "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
+          "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
+          "quant_a8": "per-token quant bf16 8192x8192 -> int8",
+          "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3",
+          "w4a8_prefill": "w4a8 prefill 2048x28672x8192",
+          "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}
 
 
 def main():
@@ -364,6 +502,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="all", help="all, or a comma list of " + ",".join(ORDER))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-calib", action="store_true", help="skip the calibration legs")
     ap.add_argument("--cpu-frac", type=int, default=2)
     args = ap.parse_args()
 
@@ -383,20 +522,23 @@ def main():
 
     names = ORDER if args.config == "all" else args.config.split(",")
     torch.cuda.set_device(0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     cases = [Case(n, torch, qgemm, datagen) for n in names]
     torch.cuda.synchronize()
+    clock = ClockSampler()
 
     # Timed region: each workload runs as its own phase, lightest first, so
     # that a workload is not measured in the power state a heavier one leaves
     # behind.  A phase is W warm-up calls, then K back-to-back eager calls
     # between two HIP events on the launch stream, then the same K calls
     # captured in a HIP graph, replayed once untimed and then 20 times with
-    # an event between replays.  The first timed replay (exactly K calls) is
-    # the per-launch GPU time without the Python binding's per-call host cost,
-    # which decides the launch-bound pointwise case and is hidden behind the
-    # GPU for the others; all 20 give the median and p99 over batches.
+    # an event between replays.  The median replay, divided by K, is the
+    # per-launch GPU time without the Python binding's per-call host cost
+    # (which decides the launch-bound pointwise case and is hidden behind
+    # the GPU for the others); the first replay and the p99 are reported
+    # beside it.
     stream = torch.cuda.current_stream()
-    eager, graphed, spread = {}, {}, {}
+    eager, graphed, spread, windows = {}, {}, {}, {}
     nb = 20  # timed replays of the K-call graph
 
     def timed(fn):
@@ -420,11 +562,15 @@ def main():
             for i in range(args.steps):
                 c(i)
         g.replay()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
         bmarks = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
         bmarks[0].record(stream)
         for r in range(nb):
             g.replay()
             bmarks[r + 1].record(stream)
+        torch.cuda.synchronize()
+        windows[c.name] = (w0, time.perf_counter())
         graphed[c.name] = bmarks
         # 20 more eager calls with an event after each give the spread of
         # single launches (median, max); they enter no average
@@ -437,48 +583,70 @@ def main():
         torch.cuda.synchronize()
         del g
     wall = time.perf_counter() - t0
-    gpu_step = sum(m[0].elapsed_time(m[1]) for m in graphed.values()) * 1e-3 / args.steps
+
+    calib = {}
+    if not args.no_calib:
+        try:
+            calib.update(read_calibration(torch))
+            w0 = time.perf_counter()
+            calib.update(mfma_calibration(torch, cus))
+            mhz, watts, _ = clock.mean(w0, time.perf_counter())
+            calib["mfma_smi_gfxclk_mhz"] = mhz
+            calib["mfma_smi_socket_w"] = watts
+        except (OSError, RuntimeError) as e:
+            calib["error"] = str(e)
+    try:
+        copy_gbs = round(hbm_copy_gbs(torch), 1)
+    except RuntimeError:
+        copy_gbs = None
+    clock.close()
 
     per = {}
-    total_ops = 0
     for c in cases:
         bm = graphed[c.name]
-        avg = bm[0].elapsed_time(bm[1]) * 1e-3 / args.steps
-        bt = sorted(bm[r].elapsed_time(bm[r + 1]) * 1e-3 / args.steps for r in range(nb))
-        b_med = bt[len(bt) // 2]
-        b_p99 = bt[min(len(bt) - 1, int(0.99 * len(bt)))]
+        bt = [bm[r].elapsed_time(bm[r + 1]) * 1e-3 / args.steps for r in range(nb)]
+        first = bt[0]
+        bts = sorted(bt)
+        b_med = bts[len(bts) // 2]
+        b_p99 = bts[min(len(bts) - 1, int(0.99 * len(bts)))]
         a, b = eager[c.name]
         avg_eager = a.elapsed_time(b) * 1e-3 / args.steps
         m = spread[c.name]
         times = sorted(m[i].elapsed_time(m[i + 1]) * 1e-3 for i in range(len(m) - 1))
-        med = times[len(times) // 2]
-        p99 = times[-1]
-        tops = c.ops / avg / 1e12
-        gbs = c.bytes / avg / 1e9
-        per[c.name] = {"us_avg": round(avg * 1e6, 2),
-                       "us_batch_median": round(b_med * 1e6, 2),
-                       "us_batch_p99": round(b_p99 * 1e6, 2),
-                       "us_avg_eager": round(avg_eager * 1e6, 2),
-                       "us_single_median": round(med * 1e6, 2),
-                       "us_single_max": round(p99 * 1e6, 2), "tops": round(tops, 2),
-                       "gb_s": round(gbs, 1),
-                       "pct_int8_mfma_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
-                       "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-                       "ops": c.ops, "alg_bytes": c.bytes,
-                       "buffer_sets": ROTATE[c.name], "input_sha256": c.input_sha}
-        total_ops += c.ops
-    # one step = one timed call of every workload; warm-up calls are outside
-    ms_per_step = gpu_step * 1e3
-    value = total_ops / gpu_step / 1e12
+        tops = c.ops / b_med / 1e12
+        gbs = c.bytes / b_med / 1e9
+        mhz, watts, nsamp = clock.mean(*windows[c.name])
+        e = {"us_median": round(b_med * 1e6, 2),
+             "us_first_replay": round(first * 1e6, 2),
+             "us_batch_p99": round(b_p99 * 1e6, 2),
+             "us_avg_eager": round(avg_eager * 1e6, 2),
+             "us_single_median": round(times[len(times) // 2] * 1e6, 2),
+             "us_single_max": round(times[-1] * 1e6, 2), "tops": round(tops, 2),
+             "gb_s": round(gbs, 1),
+             "pct_int8_mfma_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
+             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+             "ops": c.ops, "alg_bytes": c.bytes,
+             "smi_gfxclk_mhz": mhz, "smi_socket_w": watts, "smi_samples": nsamp,
+             "buffer_sets": ROTATE[c.name], "input_sha256": c.input_sha}
+        if c.name in HBM_BOUND and calib.get("read_gb_s"):
+            e["pct_of_read_rate"] = round(100 * gbs / calib["read_gb_s"], 1)
+        if c.name == "w4a8" and calib.get("read_gb_s_117mb"):
+            e["pct_of_read_rate_117mb"] = round(100 * gbs / calib["read_gb_s_117mb"], 1)
+        if c.name in MFMA_BOUND and calib.get("mfma_random_tops") and c.name != "pointwise":
+            e["pct_of_mfma_calib"] = round(100 * tops / calib["mfma_random_tops"], 1)
+        per[c.name] = e
 
-    # the roofline describes the dominant single kernel: the longest of the
-    # workloads that are one kernel launch (the asymmetric calls add a
-    # compensation-sum pass in front of theirs)
-    single = [n for n in per if not n.endswith("_zp")] or list(per)
-    dom = max(single, key=lambda n: per[n]["us_avg"])
-    mfma_bound = dom in ("s8s8", "s8s8_zp", "s4s4", "conv3x3", "conv3x3_zp", "pointwise",
-                         "w4a8_prefill")
-    if mfma_bound:
+    # one step = one call of each of the five workloads (median per-call
+    # times); warm-up calls are outside
+    step = [n for n in STEP if n in per] or list(per)
+    step_s = sum(per[n]["us_median"] for n in step) * 1e-6
+    step_ops = sum(cases[names.index(n)].ops for n in step)
+    value = step_ops / step_s / 1e12
+
+    # the roofline describes the dominant single kernel of the step: the
+    # longest of its workloads
+    dom = max(step, key=lambda n: per[n]["us_median"])
+    if dom in MFMA_BOUND:
         achieved = per[dom]["tops"]
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                 "frac": round(achieved / PEAK_INT8_TOPS, 4)}
@@ -488,6 +656,7 @@ def main():
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["kernel"] = dom
     roof["traffic"] = load_traffic(dom)
+    roof["time"] = "median of 20 graph replays of the timed calls, per call"
 
     out = {
         "metric": METRIC,
@@ -496,45 +665,31 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "qgemm step: " + " + ".join(
-            {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
-             "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
-             "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
-             "quant_a8": "per-token quant bf16 8192x8192 -> int8",
-             "w4a8": "w4a8 skinny 16x28672x8192", "s8s8": "s8s8 8192^3",
-             "w4a8_prefill": "w4a8 prefill 2048x28672x8192",
-             "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}[n]
-            for n in names),
-                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..7",
+        "config": {"workload": "qgemm step: " + " + ".join(LABELS[n] for n in step),
+                   "extra_legs": [LABELS[n] for n in names if n not in step],
+                   "parallelism": "single GPU", "seeds": "numpy PCG64 1..8",
                    "timing": f"per workload: {args.warmup} warm-up calls; "
                              f"{args.steps} back-to-back calls issued eagerly from Python "
                              f"(us_avg_eager); the same {args.steps} calls captured in a "
                              f"HIP graph, replayed once untimed and {nb} times between "
-                             f"HIP events (us_avg: the first timed replay, which value "
-                             f"and roofline use; us_batch_median / us_batch_p99: per "
-                             f"call over the {nb} replays); single-launch spread from "
-                             f"20 more eager calls; wall {wall:.3f} s for all phases"},
-        "per_config": per,
+                             f"HIP events (us_median, which value and roofline use; "
+                             f"us_first_replay; us_batch_p99: per call over the {nb} "
+                             f"replays); single-launch spread from 20 more eager calls; "
+                             f"wall {wall:.3f} s for all phases"},
+        "per_config": {n: per[n] for n in step},
+        "extra": {n: per[n] for n in names if n not in step},
         "roofline": roof,
+        "calibration": calib,
+        "hbm_copy_gb_s": copy_gbs,
     }
-    try:
-        out["hbm_copy_gb_s"] = round(hbm_copy_gbs(torch), 1)
-    except RuntimeError:
-        out["hbm_copy_gb_s"] = None
-    # the HBM-bound workloads against the rate a plain device copy reaches in
-    # the same run (torch's reductions, the only plain streaming reads at
-    # hand, read slower than these kernels, so the copy is the calibration)
-    for n in ("w4a8", "quant_a8"):
-        if n in per and out["hbm_copy_gb_s"]:
-            per[n]["pct_of_copy_rate"] = round(100 * per[n]["gb_s"] / out["hbm_copy_gb_s"], 1)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(names, args.cpu_frac)
+        out["cpu_baseline"] = cpu_baseline(step, args.cpu_frac)
     print(json.dumps(out))
 
 

@@ -1,7 +1,9 @@
 """Build libqgemm.so in-tree with hipcc for gfx950 (CDNA4 / MI355X).
 
-Every HIP source under ``csrc/`` is compiled to an object in parallel and
-linked into ``conv_qgemm_amd/libqgemm.so``.  Objects go to ``_build/`` at the
+The library's HIP sources under ``csrc/`` are compiled to objects in
+parallel and linked into ``conv_qgemm_amd/libqgemm.so``; the benchmark's
+calibration kernels (``csrc/calib.hip``) go to their own
+``conv_qgemm_amd/libqgcalib.so``.  Objects go to ``_build/`` at the
 repository root.
 """
 from __future__ import annotations
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "qgemm")
 LIB = os.path.join(PKG, "libqgemm.so")
+CALIB_LIB = os.path.join(PKG, "libqgcalib.so")
+CALIB_SOURCES = ["calib.hip"]
 SOURCES = ["api.cpp", "k_tile_gemm.hip", "k_gemm_dma.hip", "k_skinny_w4a8.hip", "k_conv_halo.hip", "k_dwconv.hip",
            "k_quant.hip", "k_zp.hip"]
 
@@ -39,17 +43,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
            "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {lib}", file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], CALIB_LIB, verbose)
     return LIB
 
 

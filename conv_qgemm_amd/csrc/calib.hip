@@ -1,0 +1,152 @@
+// calib.hip -- calibration kernels of the benchmark (libqgcalib.so, not part
+// of the quantized GEMM library's ABI).  They measure the two ceilings that
+// the GEMM and conv kernels are judged against on the board at hand:
+//
+//   * a read-only HBM stream: every byte of a buffer read once with 16-byte
+//     loads, each wave load instruction covering 1 KB of contiguous memory,
+//     U loads in flight per thread.  The bandwidth-bound kernels (the skinny
+//     W4A8 weight stream, the activation quantizer) read far more than they
+//     write, so this, not a device copy, is their practical ceiling;
+//   * a matrix-core stream: v_mfma_i32_32x32x32_i8 back to back on random
+//     int8 operands held in registers, 16 independent accumulators per wave,
+//     4 waves per CU, one workgroup per CU.  The board's power limit pulls
+//     the engine clock down when the multiplier arrays toggle, so this is the
+//     practical int8 ceiling; the shader-clock and constant-rate counters
+//     read around the loop give the clock it ran at.
+//
+// The bandwidth and the MAC count are the figures of merit the INT4 GEMM
+// article (www.cf-1.com/news/6060138) and the MCU conv front-end article
+// (news.rkmt.cn/news/16638, §2.1) measure by; the latter's §4.1 checks the
+// measuring setup itself before trusting a number.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+template <int U>
+__global__ __launch_bounds__(256) void k_stream_read(const v4i *__restrict__ src, int64_t nvec,
+                                                     unsigned *sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    v4i acc = {0, 0, 0, 0};
+    for (; i + (U - 1) * stride < nvec; i += U * stride) {
+        v4i v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u];
+    }
+    for (; i < nvec; i += stride)
+        acc ^= src[i];
+    const unsigned r = (unsigned)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+    // the loads must not be dropped: their XOR reaches a store that the
+    // compiler cannot rule out (sink holds one word per workgroup)
+    if (r == 0x9E3779B9u)
+        sink[blockIdx.x] = r;
+}
+
+// ops: [grid * 4 waves][8 fragments][64 lanes] x 16 bytes of int8 operands.
+// clk[4 * block] = {shader clock at start, at end, constant-rate clock at
+// start, at end}, read by the first lane of wave 0 after the operands landed.
+__global__ __launch_bounds__(256, 1) void k_mfma_stream(const v4i *__restrict__ ops, int iters,
+                                                        long long *clk, int *sink)
+{
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    v4i a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = ops[(gw * 8 + i) * 64 + lane];
+        b[i] = ops[(gw * 8 + 4 + i) * 64 + lane];
+    }
+    v16i acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        for (int e = 0; e < 16; ++e)
+            acc[i][e] = 0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const long long t0 = __builtin_amdgcn_s_memtime();
+    const long long r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[j * 4 + i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j * 4 + i],
+                                                                       0, 0, 0);
+    }
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        for (int e = 0; e < 16; ++e)
+            r ^= acc[i][e];
+    __syncthreads();
+    const long long t1 = __builtin_amdgcn_s_memtime();
+    const long long r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        clk[4 * blockIdx.x + 0] = t0;
+        clk[4 * blockIdx.x + 1] = t1;
+        clk[4 * blockIdx.x + 2] = r0;
+        clk[4 * blockIdx.x + 3] = r1;
+    }
+    sink[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Read `bytes` (a multiple of 16, 16-byte aligned) from device memory src
+// with `grid` workgroups of 256 threads and `unroll` (1, 2, 4 or 8) loads in
+// flight per thread.  sink: device memory of >= grid words (rarely written).
+// Returns a hipError_t value (0 = enqueued).
+int qgc_stream_read(const void *src, int64_t bytes, unsigned *sink, int grid, int unroll,
+                    void *stream)
+{
+    if (!src || !sink || bytes <= 0 || bytes % 16 || grid < 1)
+        return (int)hipErrorInvalidValue;
+    const int64_t nvec = bytes / 16;
+    hipStream_t s = (hipStream_t)stream;
+    const v4i *p = (const v4i *)src;
+    switch (unroll) {
+    case 1: hipLaunchKernelGGL(k_stream_read<1>, dim3(grid), dim3(256), 0, s, p, nvec, sink); break;
+    case 2: hipLaunchKernelGGL(k_stream_read<2>, dim3(grid), dim3(256), 0, s, p, nvec, sink); break;
+    case 4: hipLaunchKernelGGL(k_stream_read<4>, dim3(grid), dim3(256), 0, s, p, nvec, sink); break;
+    case 8: hipLaunchKernelGGL(k_stream_read<8>, dim3(grid), dim3(256), 0, s, p, nvec, sink); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+// Run `iters` rounds of 16 int8 MFMAs (32x32x32 each) per wave on `grid`
+// workgroups of 4 waves.  ops: device memory of grid * 4 * 8 * 64 * 16
+// bytes; clk: device memory of 4 * grid int64; sink: grid * 256 int32.
+int qgc_mfma_stream(const void *ops, int iters, long long *clk, int *sink, int grid,
+                    void *stream)
+{
+    if (!ops || !clk || !sink || iters < 1 || grid < 1)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_mfma_stream, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const v4i *)ops, iters, clk, sink);
+    return (int)hipGetLastError();
+}
+
+// Rate of the constant-rate counter (s_memrealtime) in kHz, or 0.
+int qgc_wall_clock_khz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return 0;
+    return khz;
+}
+
+}  // extern "C"
