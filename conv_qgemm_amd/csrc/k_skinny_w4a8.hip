@@ -17,6 +17,9 @@
 //   * one workgroup of 8 waves per CU walks a strided list of 16-row column
 //     groups; a unit is one group times one K chunk of 8192 values
 //     (16 rows x 4 KB), and units alternate between two 64 KB LDS slots;
+//   * up to 64 tokens run as 16-token blocks side by side on the CUs, the
+//     blocks of one column set on one XCD at the same time, so each weight
+//     byte is read from HBM once (the other blocks read it from L2);
 //   * the direct-to-LDS load (global_load_lds_dwordx4) writes lane L's 16
 //     bytes at LDS offset 16*L of a 1 KB piece, so every load reads one
 //     contiguous KB of one weight row; lane L fetches granule L ^ row of that
@@ -336,13 +339,20 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
     a.N = (int)d.N;
     a.K = (int)d.K;
     a.ngroups = (int)((d.N + 15) / 16);
-    // one workgroup per CU, but never more than kMaxGroups groups each
-    int grid_x = d.cus;
+    // One workgroup per CU, but never more than kMaxGroups groups each.
+    // Several 16-token blocks (grid_y > 1) share the CUs: each block gets a
+    // multiple of 8 workgroups, so that workgroups (x, y) and (x, y') --
+    // the same weight columns for different tokens, dispatched round-robin
+    // over the 8 XCDs -- run at the same time on the same XCD, and the
+    // weights come from HBM once and from that XCD's L2 for the other blocks.
+    const int grid_y = (int)((d.M + 15) / 16);
+    int grid_x = grid_y > 1 ? (d.cus / grid_y) & ~7 : d.cus;
+    if (grid_x < 8)
+        grid_x = 8;
     if (grid_x * kMaxGroups < a.ngroups)
         grid_x = (a.ngroups + kMaxGroups - 1) / kMaxGroups;
     if (grid_x > a.ngroups)
         grid_x = a.ngroups;
-    const int grid_y = (int)((d.M + 15) / 16);
     const dim3 grid(grid_x, grid_y), block(kWaves * 64);
     if (d.msb_first) {
         if (d.K <= kChunk)

@@ -399,6 +399,19 @@ def test_workload_w4a8_full(qg, unsat):
     assert np.array_equal(C, want)
 
 
+@pytest.mark.parametrize("M", [17, 33, 64])
+def test_skinny_token_blocks_full(qg, M):
+    """17, 33 and 64 tokens against the full 28672 x 8192 int4 weights: two to
+    four 16-token blocks share the weight-streaming kernel's pass over the
+    weights (the last block ragged at 17 and 33); every output compared."""
+    _say("w4a8 skinny token blocks", M)
+    d = datagen.gemm_w4a8(M, 28672, 8192, seed=200 + M, shift=(37, 43))
+    C = host(qg.qgemm_w4a8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    want = oracle.gemm_w4a8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(C, want)
+
+
 W4A8_RING = [(2048, 4096, 256), (2048, 4096, 1152), (2000, 4100, 640), (1025, 8200, 384)]
 
 
