@@ -483,6 +483,56 @@ class ClockSampler:
                 pass
 
 
+def _csv_rows(path):
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*.csv"), recursive=True))
+    for f in files:
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def summarize_trace(stats_csv, title, cmd):
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel summary."""
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in _csv_rows(stats_csv):
+        if "AverageNs" not in r:
+            continue
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_pmc(name, fetch_dir, write_dir, copy_bytes=1 << 30):
+    """One traffic line for `name` from two rocprofv3 --pmc runs of
+    `bench.py --config name` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Every dispatch that is not a copy kernel belongs to the workload; the
+    1 GiB device copy of hbm_copy_gbs() in the same run calibrates the
+    counter (factor = known bytes / what the counter reads for that copy)."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        work, copies = [], []
+        for r in _csv_rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            (copies if "copy" in r["Kernel_Name"].lower() else work).append(v)
+        if not work or not copies:
+            raise SystemExit(f"no {counter} rows for the workload or the copy kernel in {d}")
+        calib = copy_bytes / max(copies)
+        out[counter] = (sum(work) / len(work), calib)
+    (f, cf), (w, cw) = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    total = f * cf + w * cw
+    return (f"traffic workload={name} src_sha={src_sha(KERNEL_SOURCES[name])} "
+            f"bytes_per_launch={int(total)} fetch_bytes_raw={int(f)} write_bytes_raw={int(w)} "
+            f"calib_fetch={cf:.4f} calib_write={cw:.4f}")
+
+
 LABELS = {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
           "conv3x3": "conv3x3 NHWC 32x56x56x64->64",
           "dw3x3": "depthwise 3x3 NHWC 32x56x56x64",
@@ -493,7 +543,68 @@ LABELS = {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
           "conv3x3_zp": "conv3x3 with zero points", "s8s8_zp": "s8s8 8192^3 with zero points"}
 
 
+# kernel of each workload, as it appears in a rocprofv3 kernel name
+KERNEL_NAMES = {"s8s8": "k_gemm_dma<8, 0>", "s8s8_zp": "k_gemm_dma<8, 2>",
+                "w4a8_prefill": "k_gemm_dma<3, 0>", "s4s4": "k_gemm_dma<4, 1>",
+                "conv3x3": "k_conv_halo<3, 3, false>", "conv3x3_zp": "k_conv_halo<3, 3, true>",
+                "w4a8": "k_skinny_w4a8", "w4a8_m64": "k_skinny_w4a8",
+                "dw3x3": "k_dwconv3x3<1, false>", "quant_a8": "k_quant", "pointwise": "k_tile"}
+
+
+def summarize_counters(name, *dirs, n_xcd=8, n_simd=1024):
+    """One line per workload from rocprofv3 --pmc runs of `bench.py --config
+    name`: each counter averaged over the workload kernel's dispatches, plus
+    derived figures where their counters are present:
+      clock_mhz   = GRBM_GUI_ACTIVE / n_xcd / dispatch duration (the engine
+                    clock while the kernel ran; GRBM counts per XCD), for
+                    dispatches of 200 us or more
+      mfma_busy   = SQ_VALU_MFMA_BUSY_CYCLES / n_simd / (GRBM_GUI_ACTIVE /
+                    n_xcd): share of the kernel's cycles the matrix pipe
+                    issues in
+      lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      tcp_* stall shares = the TCP counter / 256 CUs / (GRBM_GUI_ACTIVE / n_xcd)"""
+    import collections
+    kn = KERNEL_NAMES[name]
+    vals = collections.defaultdict(list)
+    durs = []
+    for d in dirs:
+        for r in _csv_rows(d):
+            if "Counter_Name" not in r or kn not in r["Kernel_Name"]:
+                continue
+            vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                durs.append((float(r["Counter_Value"]),
+                             float(r["End_Timestamp"]) - float(r["Start_Timestamp"])))
+    if not vals:
+        raise SystemExit(f"no dispatches of {kn} in {dirs}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    out = [f"counters workload={name} kernel=\"{kn}\""]
+    if durs:
+        g = sum(x for x, _ in durs) / len(durs) / n_xcd
+        t_us = sum(t for _, t in durs) / len(durs) / 1e3
+        # GRBM_GUI_ACTIVE also counts a few thousand cycles around the
+        # dispatch, so the clock is only given for long dispatches
+        if t_us >= 200:
+            out.append(f"clock_mhz={sum(x / n_xcd / t for x, t in durs) / len(durs) * 1e3:.0f}")
+        out.append(f"dispatch_us={t_us:.1f}")
+        out.append(f"grbm_active_per_xcd={g:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            out.append(f"mfma_busy_pct={100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / n_simd / g:.1f}")
+        for k in ("TCP_PENDING_STALL_CYCLES", "TCP_TCR_TCP_STALL_CYCLES",
+                  "TCP_UTCL1_STALL_INFLIGHT_MAX", "TCP_UTCL1_SERIALIZATION_STALL",
+                  "TA_ADDR_STALLED_BY_TC_CYCLES"):
+            if k in avg:
+                out.append(f"{k.lower()}_pct={100 * avg[k] / 256 / g:.1f}")
+    if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+        out.append(f"lds_conflict_pct={100 * avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.1f}")
+    out += [f"{k.lower()}={v:.0f}" for k, v in sorted(avg.items()) if k != "GRBM_GUI_ACTIVE"]
+    return " ".join(out)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        print(summarize_counters(sys.argv[2], *sys.argv[3:]))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         print(summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4]))
         return
