@@ -495,7 +495,13 @@ qg_status qdwconv2d_nhwc_s8_requant_zp(const int8_t *X, const int8_t *W, const i
 
 const char *qg_status_string(qg_status s)
 {
-    switch (s) {
+    // A C caller may pass any int here.  In C++ an enumeration object that
+    // holds a value outside the enumerators' range must not be read as the
+    // enumeration (undefined behaviour), so switch on its bytes as an int.
+    int v;
+    static_assert(sizeof v == sizeof s, "qg_status is int-sized");
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
     case QG_OK:
         return "QG_OK";
     case QG_ERR_NULLPTR:

@@ -17,7 +17,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
+# QG_LIB may point the loader at another build of the same library (the
+# tests load one built with host-side sanitizers this way)
+_LIB_PATH = os.environ.get("QG_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libqgemm.so")
 
 QG_OK = 0
 QG_ERR_NULLPTR = 1
