@@ -17,9 +17,11 @@
 //   * one workgroup of 8 waves per CU walks a strided list of 16-row column
 //     groups; a unit is one group times one K chunk of 8192 values
 //     (16 rows x 4 KB), and units alternate between two 64 KB LDS slots;
-//   * up to 64 tokens run as 16-token blocks side by side on the CUs, the
-//     blocks of one column set on one XCD at the same time, so each weight
-//     byte is read from HBM once (the other blocks read it from L2);
+//   * more than 16 tokens (up to 64) run as blocks side by side on the CUs,
+//     32 tokens to a workgroup when K fits one chunk (each weight fragment
+//     read and widened once feeds two MFMA chains), the blocks of one column
+//     set on one XCD at the same time, so each weight byte is read from HBM
+//     once (the other blocks read it from L2);
 //   * the direct-to-LDS load (global_load_lds_dwordx4) writes lane L's 16
 //     bytes at LDS offset 16*L of a 1 KB piece, so every load reads one
 //     contiguous KB of one weight row; lane L fetches granule L ^ row of that
@@ -91,10 +93,22 @@ __device__ __forceinline__ void drain_and_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Plain LDS barrier: this wave's LDS reads are done, then meet the other
+// waves; loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ONE: K fits one chunk, so the activations are loaded once.
-template <bool ONE, bool MSB>
+// TB: 16-token blocks per workgroup (1, or 2 when K fits one chunk).  With
+// two, every weight fragment read from LDS and widened feeds two MFMA
+// chains, the reduction buffer's two halves hold the two blocks (one group
+// at a time, behind an extra barrier), and results are stored directly.
+template <bool ONE, bool MSB, int TB>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
 {
+    static_assert(TB == 1 || (TB == 2 && ONE), "two token blocks need K within one chunk");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     v4i(*red)[kWaves][64] = (v4i(*)[kWaves][64])(lds + kRedOff);
     int(*prm)[kMaxGroups * 16] = (int(*)[kMaxGroups * 16])(lds + kPrmOff);
@@ -105,7 +119,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;  // weight row within the group / token index
     const int g = lane >> 4;    // 16-value group within a 64-value K step
-    const int tok = blockIdx.y * 16 + col;
+    const int tok = blockIdx.y * 16 * TB + col;  // token of block 0; block b adds 16 b
     const int nchunks = ONE ? 1 : (p.K + kChunk - 1) / kChunk;
     const int KbB = p.K / 2;
 
@@ -120,8 +134,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // value offset of (step s, lane group g) inside a wave's 1024 values: a
     // 16-byte weight read covers two steps, lane group g taking 32 values
     auto kofs = [&](int s) { return (s >> 1) * 128 + g * 32 + (s & 1) * 16; };
-    const int8_t *arow = p.A + (int64_t)min(tok, p.M - 1) * p.lda;
-    auto load_acts = [&](int chunk, v4i(&af)[kSteps]) {
+    auto load_acts = [&](int chunk, v4i(&af)[kSteps], int b = 0) {
+        const int8_t *arow = p.A + (int64_t)min(tok + 16 * b, p.M - 1) * p.lda;
         const int kbase = chunk * kChunk + wave * (kSteps * 64);
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
@@ -168,28 +182,70 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     for (int l = 0; l < kSteps / 2; ++l)
         rd[l] = (col * kPieces + (wave >> 1)) * 1024 + ((((wave & 1) * 32 + 4 * l + g) ^ col) << 4);
 
-    v4i acc = {0, 0, 0, 0};
+    v4i acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};  // acc2: the second token block
+    v4i af2[TB == 2 ? kSteps : 1];
     auto consume = [&](int slot, const v4i(&af)[kSteps]) {
 #pragma unroll
         for (int l = 0; l < kSteps / 2; ++l) {
             const v4i wl = *(const v4i *)(lds + slot * kSlot + rd[l]);
             const v2u lo = {(unsigned)wl[0], (unsigned)wl[1]};
             const v2u hi = {(unsigned)wl[2], (unsigned)wl[3]};
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(lo), af[2 * l], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(widen_int4_x16(hi), af[2 * l + 1], acc, 0,
-                                                        0, 0);
+            const v4i wlo = widen_int4_x16(lo), whi = widen_int4_x16(hi);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, af[2 * l], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, af[2 * l + 1], acc, 0, 0, 0);
+            if constexpr (TB == 2) {
+                acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, af2[2 * l], acc2, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, af2[2 * l + 1], acc2, 0, 0, 0);
+            }
         }
     };
 
     // one wave adds the 8 partial sums of group i and requantizes; the lane
     // holds token lane%16 and columns 4*(lane/16) + e of the group
+    // two blocks: all 512 threads take one output value each (block b =
+    // tid / 256; the partial sums of source lane L, value e at
+    // red[b][v][L][e]: 16 lanes x 16 bytes contiguous per 64 threads, no
+    // bank conflicts), then lanes e = 1..3 hand their byte to lane e = 0,
+    // which stores the dword
+    auto reduce2 = [&](int i) {
+        const int b = tid >> 8, r = tid & 255, ls = r >> 2, e = r & 3;
+        const int *rp = (const int *)&red[b][0][ls] + e;
+        int sum = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v)
+            sum += rp[v * 64 * 4];
+        const int c = i * 16 + 4 * (ls >> 4) + e;
+        const int y = requant_one(sum >> 4, prm[0][c], prm[1][c], prm[2][c],
+                                  1ll << ((prm[2][c] - 1) & 63));
+        // lanes 4k .. 4k+3 hold e = 0..3: after two exchanges each holds all four bytes
+        unsigned v = (unsigned)(y & 0xFF) << (8 * e);
+        v |= (unsigned)__shfl_xor((int)v, 1);
+        v |= (unsigned)__shfl_xor((int)v, 2);
+        const int t = tok - col + 16 * b + (ls & 15), n = group_of(i) * 16 + 4 * (ls >> 4);
+        if (e == 0 && t < p.M && n < p.N) {
+            int8_t *dst = p.C + (int64_t)t * p.ldc + n;
+            if (n + 3 < p.N && (p.ldc & 3) == 0) {
+                *(unsigned *)dst = v;
+            } else {
+                for (int q = 0; q < 4; ++q)
+                    if (n + q < p.N)
+                        dst[q] = (int8_t)(v >> (8 * q));
+            }
+        }
+    };
     auto reduce = [&](int i) {
+        if constexpr (TB == 2) {
+            reduce2(i);
+            return;
+        }
+        const int b = 0;
         if (wave != i % kWaves)
             return;
-        v4i sum = red[i & 1][0][lane];
+        const int rb = i & 1;
+        v4i sum = red[rb][0][lane];
 #pragma unroll
         for (int v = 1; v < kWaves; ++v) {
-            const v4i x = red[i & 1][v][lane];
+            const v4i x = red[rb][v][lane];
             for (int e = 0; e < 4; ++e)
                 sum[e] += x[e];
         }
@@ -199,6 +255,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         int y[4];
         for (int e = 0; e < 4; ++e)
             y[e] = requant_one(sum[e] >> 4, b4[e], m4[e], s4[e], 1ll << ((s4[e] - 1) & 63));
+        (void)b;
         outb[i][lane] = pack4_i8(y[0], y[1], y[2], y[3]);
     };
 
@@ -237,13 +294,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         const int i = u / nchunks, c = u - i * nchunks;
         if (!ONE)
             fix_acts(c, af);
-        if (c == 0 && i > 0)
+        if (c == 0 && i > 0) {
             reduce(i - 1);
+            // two blocks share one buffer per block: its readers finish
+            // before this group's partial sums overwrite it
+            if constexpr (TB == 2)
+                lds_barrier();
+        }
         if (c == 0)
-            acc = (v4i){0, 0, 0, 0};
+            acc = acc2 = (v4i){0, 0, 0, 0};
         consume(slot, af);
-        if (c == nchunks - 1)
-            red[i & 1][wave][lane] = acc;
+        if (c == nchunks - 1) {
+            red[TB == 1 ? i & 1 : 0][wave][lane] = acc;
+            if constexpr (TB == 2)
+                red[1][wave][lane] = acc2;
+        }
         // behind this unit's LDS reads: the compiler cannot tell the copy's
         // LDS range from the slot's and would wait for it before them
         if (u == 0)
@@ -266,7 +331,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
                       kLdsBytes - kPrmOff == 16 * 1024,
                   "staging regions: slot 1 for waves 0-3, the reduction buffer for wave 4, "
                   "the parameter and output blocks for wave 5");
-    const bool staged = ONE && wave < kStagedWaves;
+    const bool staged = ONE && TB == 1 && wave < kStagedWaves;
     const int stage_off = wave < 4 ? kSlot + wave * 16 * 1024 : wave == 4 ? kRedOff : kPrmOff;
     if (staged) {
         const int kbase = wave * (kSteps * 64);
@@ -280,6 +345,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     } else {
         load_acts(0, af0);
     }
+    if constexpr (TB == 2)
+        load_acts(0, af2, 1);
     issue(0, 0);
     if (staged) {
         // the copies above are done once at most kLoads later loads are out
@@ -290,6 +357,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     }
     if (ONE)
         fix_acts(0, af0);
+    if constexpr (TB == 2)
+        fix_acts(0, af2);
     for (int u = 0; u < nunits; u += 2) {
         step(u, 0, af0, af1);
         if (u + 1 < nunits) {
@@ -301,6 +370,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     }
     drain_and_barrier();
     reduce(ng - 1);
+    if constexpr (TB == 2)
+        return;  // stored by the reducing waves
 
     // ---- results: 16 tokens x 16 columns per group, one dword per lane ----
     drain_and_barrier();
@@ -340,12 +411,16 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
     a.K = (int)d.K;
     a.ngroups = (int)((d.N + 15) / 16);
     // One workgroup per CU, but never more than kMaxGroups groups each.
-    // Several 16-token blocks (grid_y > 1) share the CUs: each block gets a
-    // multiple of 8 workgroups, so that workgroups (x, y) and (x, y') --
-    // the same weight columns for different tokens, dispatched round-robin
-    // over the 8 XCDs -- run at the same time on the same XCD, and the
-    // weights come from HBM once and from that XCD's L2 for the other blocks.
-    const int grid_y = (int)((d.M + 15) / 16);
+    // Beyond 16 tokens with K within one chunk a workgroup takes two 16-token
+    // blocks (32 tokens); the blocks of a grid row (grid_y > 1) share the CUs:
+    // each gets a multiple of 8 workgroups, so that workgroups (x, y) and
+    // (x, y') -- the same weight columns for different tokens, dispatched
+    // round-robin over the 8 XCDs -- run at the same time on the same XCD,
+    // and the weights come from HBM once and from that XCD's L2 for the
+    // other blocks.
+    const bool one = d.K <= kChunk;
+    const int tb = one && d.M > 16 ? 2 : 1;
+    const int grid_y = (int)((d.M + 16 * tb - 1) / (16 * tb));
     int grid_x = grid_y > 1 ? (d.cus / grid_y) & ~7 : d.cus;
     if (grid_x < 8)
         grid_x = 8;
@@ -354,16 +429,21 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
     if (grid_x > a.ngroups)
         grid_x = a.ngroups;
     const dim3 grid(grid_x, grid_y), block(kWaves * 64);
-    if (d.msb_first) {
-        if (d.K <= kChunk)
-            hipLaunchKernelGGL((k_skinny_w4a8<true, true>), grid, block, 0, s, a);
+    if (tb == 2) {
+        if (d.msb_first)
+            hipLaunchKernelGGL((k_skinny_w4a8<true, true, 2>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((k_skinny_w4a8<false, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_skinny_w4a8<true, false, 2>), grid, block, 0, s, a);
+    } else if (d.msb_first) {
+        if (one)
+            hipLaunchKernelGGL((k_skinny_w4a8<true, true, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_skinny_w4a8<false, true, 1>), grid, block, 0, s, a);
     } else {
-        if (d.K <= kChunk)
-            hipLaunchKernelGGL((k_skinny_w4a8<true, false>), grid, block, 0, s, a);
+        if (one)
+            hipLaunchKernelGGL((k_skinny_w4a8<true, false, 1>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((k_skinny_w4a8<false, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_skinny_w4a8<false, false, 1>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
