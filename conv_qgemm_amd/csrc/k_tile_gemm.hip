@@ -93,6 +93,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
     constexpr int ACC_SHIFT = (KA == OP_S4 ? 4 : 0) + (KB == OP_S4 ? 4 : 0);
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    // the tile's per-column requantize parameters (bias, multiplier, shift),
+    // loaded with the first K tile so that the epilogue needs no second trip
+    // to memory; columns past N hold column N-1's (never stored)
+    constexpr bool RQ = EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP;
+    static_assert(BN <= kThreads, "one column per thread");
+    __shared__ __attribute__((aligned(16))) int prm[3][RQ ? BN : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -228,8 +234,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
     };
 
     // ---- main K loop: prefetch tile kt+1 to registers while multiplying kt ----
+    int pb = 0, pm = 0, ps = 0;
+    if (RQ && tid < BN) {
+        const int nn = min(n0 + tid, p.N - 1);
+        pb = p.bias ? p.bias[nn] : 0;
+        pm = p.mult[nn];
+        ps = p.shift[nn];
+    }
     load_tile(0);
     store_tile(0);
+    if (RQ && tid < BN) {
+        prm[0][tid] = pb;
+        prm[1][tid] = pm;
+        prm[2][tid] = ps;
+    }
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
         const int buf = kt & 1;
@@ -257,21 +275,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_tile(TileArgs p)
                 constexpr bool ZP = EPI == EPI_REQUANT_ZP;
                 int bia[4], mul[4], shf[4];
                 long long rnd[4];
-                if (full) {
-                    v4i b4 = p.bias ? *(const v4i *)(p.bias + n) : zero4;
-                    v4i m4 = *(const v4i *)(p.mult + n);
-                    v4i s4 = *(const v4i *)(p.shift + n);
+                {
+                    const int nl = n - n0;  // 4 consecutive local columns, 16-byte aligned
+                    const v4i b4 = *(const v4i *)&prm[0][nl];
+                    const v4i m4 = *(const v4i *)&prm[1][nl];
+                    const v4i s4 = *(const v4i *)&prm[2][nl];
                     for (int e = 0; e < 4; ++e) {
                         bia[e] = b4[e];
                         mul[e] = m4[e];
                         shf[e] = s4[e];
-                    }
-                } else {
-                    for (int e = 0; e < 4; ++e) {
-                        const int nn = min(n + e, p.N - 1);
-                        bia[e] = p.bias ? p.bias[nn] : 0;
-                        mul[e] = p.mult[nn];
-                        shf[e] = p.shift[nn];
                     }
                 }
                 for (int e = 0; e < 4; ++e)
