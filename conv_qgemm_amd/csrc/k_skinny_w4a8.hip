@@ -60,6 +60,7 @@ constexpr int kSlot = 16 * kRowBytes;          // 64 KB
 constexpr int kPieces = kRowBytes / 1024;      // 1 KB pieces per row per unit
 constexpr int kLoads = 16 * kPieces / kWaves;  // direct-to-LDS loads per wave per unit (8)
 constexpr int kMaxGroups = 32;                 // column groups per workgroup (LDS staging)
+constexpr int kMaxGroups2 = 16;                // the same with two token blocks (32 tokens)
 
 // LDS map, one object so that the compiler sees one buffer
 constexpr int kRedOff = 2 * kSlot;                          // v4i red[2][kWaves][64]
@@ -104,7 +105,8 @@ __device__ __forceinline__ void lds_barrier()
 // TB: 16-token blocks per workgroup (1, or 2 when K fits one chunk).  With
 // two, every weight fragment read from LDS and widened feeds two MFMA
 // chains, the reduction buffer's two halves hold the two blocks (one group
-// at a time, behind an extra barrier), and results are stored directly.
+// at a time, behind an extra barrier), and the results wait in the output
+// block (16 groups at most) until the end, as with one block.
 template <bool ONE, bool MSB, int TB>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
 {
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // tid / 256; the partial sums of source lane L, value e at
     // red[b][v][L][e]: 16 lanes x 16 bytes contiguous per 64 threads, no
     // bank conflicts), then lanes e = 1..3 hand their byte to lane e = 0,
-    // which stores the dword
+    // which puts the dword in the output block
     auto reduce2 = [&](int i) {
         const int b = tid >> 8, r = tid & 255, ls = r >> 2, e = r & 3;
         const int *rp = (const int *)&red[b][0][ls] + e;
@@ -221,17 +223,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         unsigned v = (unsigned)(y & 0xFF) << (8 * e);
         v |= (unsigned)__shfl_xor((int)v, 1);
         v |= (unsigned)__shfl_xor((int)v, 2);
-        const int t = tok - col + 16 * b + (ls & 15), n = group_of(i) * 16 + 4 * (ls >> 4);
-        if (e == 0 && t < p.M && n < p.N) {
-            int8_t *dst = p.C + (int64_t)t * p.ldc + n;
-            if (n + 3 < p.N && (p.ldc & 3) == 0) {
-                *(unsigned *)dst = v;
-            } else {
-                for (int q = 0; q < 4; ++q)
-                    if (n + q < p.N)
-                        dst[q] = (int8_t)(v >> (8 * q));
-            }
-        }
+        // kept in LDS until the end (token 16 b + ls % 16, column quad ls / 16):
+        // stores here would sit in the count that the next unit's wait drains
+        if (e == 0)
+            outb[i * 2 + b][4 * (ls & 15) + (ls >> 4)] = v;
     };
     auto reduce = [&](int i) {
         if constexpr (TB == 2) {
@@ -325,19 +320,29 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // one instruction, lane L fetching granule L ^ t) and read them back in
     // the MFMA layout, granule G of token t at position G ^ t, which puts the
     // 16 lanes of every LDS read cycle on 16 different bank groups.  Waves
-    // 6 and 7 load theirs directly.  K > kChunk keeps the direct loads. ----
+    // 6 and 7 load theirs directly, and so does every wave for a second
+    // token block (the regions hold one).  K > kChunk keeps the direct
+    // loads. ----
     constexpr int kStagedWaves = 6;
     static_assert(4 * 16 * 1024 == kSlot && kPrmOff - kRedOff == 16 * 1024 &&
                       kLdsBytes - kPrmOff == 16 * 1024,
                   "staging regions: slot 1 for waves 0-3, the reduction buffer for wave 4, "
                   "the parameter and output blocks for wave 5");
-    const bool staged = ONE && TB == 1 && wave < kStagedWaves;
+    const bool staged = ONE && wave < kStagedWaves;
     const int stage_off = wave < 4 ? kSlot + wave * 16 * 1024 : wave == 4 ? kRedOff : kPrmOff;
+    // two blocks: the second block's activations load directly, before the
+    // staged copies, so that the wait below (for all but the weight loads
+    // issued after the copies) also covers them whatever order the compiler
+    // gives these loads among themselves
+    if constexpr (TB == 2) {
+        load_acts(0, af2, 1);
+        asm volatile("" ::: "memory");
+    }
     if (staged) {
         const int kbase = wave * (kSteps * 64);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const int8_t *src = p.A + (int64_t)min((int)blockIdx.y * 16 + t, p.M - 1) * p.lda +
+            const int8_t *src = p.A + (int64_t)min(tok - col + t, p.M - 1) * p.lda +
                                 min(kbase + 16 * (lane ^ t), p.K - 16);
             __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
                                              (lds_void_t *)(lds + stage_off + t * 1024), 16, 0, 0);
@@ -345,8 +350,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     } else {
         load_acts(0, af0);
     }
-    if constexpr (TB == 2)
-        load_acts(0, af2, 1);
     issue(0, 0);
     if (staged) {
         // the copies above are done once at most kLoads later loads are out
@@ -370,11 +373,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     }
     drain_and_barrier();
     reduce(ng - 1);
-    if constexpr (TB == 2)
-        return;  // stored by the reducing waves
 
-    // ---- results: 16 tokens x 16 columns per group, one dword per lane ----
+    // ---- results: 16 tokens x 16 columns per group and token block, one
+    // dword per lane (two blocks: outb rows 2i and 2i + 1, token-major) ----
     drain_and_barrier();
+    if constexpr (TB == 2) {
+        for (int j = tid >> 6; j < 2 * ng; j += kWaves) {
+            const int i = j >> 1, t = tok - col + 16 * (j & 1) + (lane >> 2);
+            const int n = group_of(i) * 16 + 4 * (lane & 3);
+            if (t >= p.M || n >= p.N)
+                continue;
+            const unsigned v = outb[j][lane];
+            int8_t *dst = p.C + (int64_t)t * p.ldc + n;
+            if (n + 3 < p.N && (p.ldc & 3) == 0) {
+                *(unsigned *)dst = v;
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < p.N)
+                        dst[e] = (int8_t)(v >> (8 * e));
+            }
+        }
+        return;
+    }
     const bool tok_ok = tok < p.M;
     for (int i = wave; i < ng; i += kWaves) {
         const int n = group_of(i) * 16 + 4 * g;
@@ -424,8 +444,9 @@ hipError_t launch_w4a8_skinny(const GemmDesc &d, hipStream_t s)
     int grid_x = grid_y > 1 ? (d.cus / grid_y) & ~7 : d.cus;
     if (grid_x < 8)
         grid_x = 8;
-    if (grid_x * kMaxGroups < a.ngroups)
-        grid_x = (a.ngroups + kMaxGroups - 1) / kMaxGroups;
+    const int max_groups = tb == 2 ? kMaxGroups2 : kMaxGroups;
+    if (grid_x * max_groups < a.ngroups)
+        grid_x = (a.ngroups + max_groups - 1) / max_groups;
     if (grid_x > a.ngroups)
         grid_x = a.ngroups;
     const dim3 grid(grid_x, grid_y), block(kWaves * 64);
