@@ -330,14 +330,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
                   "the parameter and output blocks for wave 5");
     const bool staged = ONE && wave < kStagedWaves;
     const int stage_off = wave < 4 ? kSlot + wave * 16 * 1024 : wave == 4 ? kRedOff : kPrmOff;
-    // two blocks: the second block's activations load directly, before the
-    // staged copies, so that the wait below (for all but the weight loads
-    // issued after the copies) also covers them whatever order the compiler
-    // gives these loads among themselves
-    if constexpr (TB == 2) {
-        load_acts(0, af2, 1);
-        asm volatile("" ::: "memory");
-    }
+    // One branch holds everything from the copies to the read-back: with two
+    // tests of `staged`, the compiler assumed the other branch's direct
+    // loads (into the same registers) pending and waited for every load,
+    // the first unit's weights included, before the read-back.  A second
+    // token block loads directly, after the weights in the staged branch,
+    // where the wait for the copies counts those loads too (compiler
+    // barriers keep the order).
     if (staged) {
         const int kbase = wave * (kSteps * 64);
 #pragma unroll
@@ -347,16 +346,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
             __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
                                              (lds_void_t *)(lds + stage_off + t * 1024), 16, 0, 0);
         }
-    } else {
-        load_acts(0, af0);
-    }
-    issue(0, 0);
-    if (staged) {
-        // the copies above are done once at most kLoads later loads are out
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+        issue(0, 0);
+        if constexpr (TB == 2) {
+            asm volatile("" ::: "memory");
+            load_acts(0, af2, 1);
+            asm volatile("" ::: "memory");
+        }
+        // the copies above are done once at most this many later loads are out
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads + (TB == 2 ? kSteps : 0)) : "memory");
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
             af0[s] = *(const v4i *)(lds + stage_off + col * 1024 + (((kofs(s) >> 4) ^ col) << 4));
+    } else {
+        if constexpr (TB == 2)
+            load_acts(0, af2, 1);
+        load_acts(0, af0);
+        issue(0, 0);
     }
     if (ONE)
         fix_acts(0, af0);
