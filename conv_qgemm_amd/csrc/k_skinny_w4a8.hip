@@ -320,9 +320,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // one instruction, lane L fetching granule L ^ t) and read them back in
     // the MFMA layout, granule G of token t at position G ^ t, which puts the
     // 16 lanes of every LDS read cycle on 16 different bank groups.  Waves
-    // 6 and 7 load theirs directly, and so does every wave for a second
-    // token block (the regions hold one).  K > kChunk keeps the direct
-    // loads. ----
+    // 6 and 7 load theirs directly.  A second token block goes through the
+    // same regions in a second round.  K > kChunk keeps the direct loads. ----
     constexpr int kStagedWaves = 6;
     static_assert(4 * 16 * 1024 == kSlot && kPrmOff - kRedOff == 16 * 1024 &&
                       kLdsBytes - kPrmOff == 16 * 1024,
@@ -334,9 +333,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // tests of `staged`, the compiler assumed the other branch's direct
     // loads (into the same registers) pending and waited for every load,
     // the first unit's weights included, before the read-back.  A second
-    // token block loads directly, after the weights in the staged branch,
-    // where the wait for the copies counts those loads too (compiler
-    // barriers keep the order).
+    // token block takes a second round through the same region once the
+    // first round's reads are back (its wait also covers the weights, which
+    // the first barrier needs anyway).
     if (staged) {
         const int kbase = wave * (kSteps * 64);
 #pragma unroll
@@ -347,16 +346,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
                                              (lds_void_t *)(lds + stage_off + t * 1024), 16, 0, 0);
         }
         issue(0, 0);
-        if constexpr (TB == 2) {
-            asm volatile("" ::: "memory");
-            load_acts(0, af2, 1);
-            asm volatile("" ::: "memory");
-        }
-        // the copies above are done once at most this many later loads are out
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads + (TB == 2 ? kSteps : 0)) : "memory");
+        // the copies above are done once at most kLoads later loads are out
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
             af0[s] = *(const v4i *)(lds + stage_off + col * 1024 + (((kofs(s) >> 4) ^ col) << 4));
+        if constexpr (TB == 2) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int8_t *src = p.A + (int64_t)min(tok - col + 16 + t, p.M - 1) * p.lda +
+                                    min(kbase + 16 * (lane ^ t), p.K - 16);
+                __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
+                                                 (lds_void_t *)(lds + stage_off + t * 1024), 16, 0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s)
+                af2[s] = *(const v4i *)(lds + stage_off + col * 1024 + (((kofs(s) >> 4) ^ col) << 4));
+        }
     } else {
         if constexpr (TB == 2)
             load_acts(0, af2, 1);
