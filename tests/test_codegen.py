@@ -96,3 +96,34 @@ def test_binary16_output_rounds_twice(tmp_path, src):
     text = out.read_text()
     assert "v_cvt_f16_f32" in text
     assert not re.search(r"v_(fma|mad)_mix", text)
+
+
+def test_skinny_staged_readback_waits_for_the_copies_only(tmp_path):
+    """The skinny W4A8 kernel stages its first token block's activations
+    through LDS and reads them back before its first barrier.  That read-back
+    must wait only for the staging copies (vmcnt(8): the first unit's eight
+    weight loads per wave stay in flight), not for every load (vmcnt(0)),
+    which would put the weights' HBM latency in front of it.  Checked on the
+    one-chunk kernels, one and two token blocks, both nibble orders."""
+    from conv_qgemm_amd import build
+    out = tmp_path / "k_skinny_w4a8.s"
+    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S",
+           os.path.join(ROOT, "conv_qgemm_amd", "csrc", "k_skinny_w4a8.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = out.read_text()
+    names = re.findall(r"^(_Z\S*k_skinny_w4a8ILb1E\S*):", text, re.M)
+    assert len(names) == 4, names  # one chunk: (one or two blocks) x 2 nibble orders
+    for name in names:
+        start = text.index("\n" + name + ":")
+        body = text[start:text.index(".Lfunc_end", start)]
+        ops = [ln.strip() for ln in body.splitlines()
+               if ln.startswith("\t") and not ln.strip().startswith((".", ";"))]
+        first_bar = next(i for i, ln in enumerate(ops) if ln.startswith("s_barrier"))
+        pro = ops[:first_bar]
+        first_read = next(i for i, ln in enumerate(pro) if ln.startswith("ds_read_b128"))
+        dma = [i for i, ln in enumerate(pro[:first_read]) if ln.startswith("global_load_lds_dwordx4")]
+        # the staged branch: 16 copies, then the unit's 8 weight loads
+        assert len(dma) >= 24, (name, len(dma))
+        waits = [ln for ln in pro[dma[-1]:first_read] if ln.startswith("s_waitcnt")]
+        assert waits and all("vmcnt(0)" not in w for w in waits), (name, waits)
+        assert any("vmcnt(8)" in w for w in waits), (name, waits)
