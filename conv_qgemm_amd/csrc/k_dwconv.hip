@@ -101,84 +101,115 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     const int colsL = p.Wd + 2 * p.pw;
     const int rowL = colsL * kPixL;
 
-    // ---- per-channel parameters ----
-    int pb = 0, pm = 0, ps = 31;
-    if (tid < cs) {
-        pb = p.bias ? p.bias[c0 + tid] : 0;
-        pm = p.mult[c0 + tid];
-        ps = p.shift[c0 + tid];
-    }
-
-    // ---- diagonal weight operands: slice s (taps 4s..4s+3), group n; the
-    //      lane (column col = output channel 16n + col, K group g = tap
-    //      4s + g) holds w[4s + g][c0 + 16n + col] at byte col of 16 ----
-    v4i wd[kSlices][4];
+    // ---- per-channel parameters and this lane's weight bytes, loaded
+    //      behind the input rows (issued first, the compiler waited for
+    //      them before the input loads could go); the diagonal operands are
+    //      built from the bytes after the barrier ----
+    // Unconditional loads at clamped indices, the raw values kept untouched
+    // until after the barrier (a load under a branch, or a value used at
+    // once, makes the compiler wait for the input loads issued before it).
+    int bv, mv, sv;
+    int wb[kSlices][4];
+    auto load_params = [&]() {
+        const int cc = c0 + min(tid, cs - 1);
+        bv = (p.bias ? p.bias : p.mult)[cc];
+        mv = p.mult[cc];
+        sv = p.shift[cc];
 #pragma unroll
-    for (int s = 0; s < kSlices; ++s) {
-        const int t = 4 * s + g;
+        for (int s = 0; s < kSlices; ++s)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int c = c0 + 16 * n + col;
-            int w = 0;
-            if (t < KK && 16 * n < cs)
-                w = (int)p.W[(int64_t)t * p.C + c] & 0xFF;
-            v4i v = {0, 0, 0, 0};
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                v[d] = (col >> 2) == d ? (w << (8 * (col & 3))) : 0;
-            wd[s][n] = v;
-        }
-    }
+            for (int n = 0; n < 4; ++n)
+                wb[s][n] = (uint8_t)p.W[(int64_t)min(4 * s + g, KK - 1) * p.C + c0 +
+                                        min(16 * n, cs - 16) + col];
+    };
 
     // ---- input rows (the slice's channels) -> LDS, the padding value
     //      outside the image ----
     const int gpp = cs >> 4;  // 16-byte granules per pixel
     const int total = ih_lo <= ih_hi ? (ih_hi - ih_lo + 1) * p.Wd * gpp : 0;
-    for (int base = 0; base == 0 || base < total; base += 8 * kWaves * 64) {
+    constexpr int kPass = 8 * kWaves * 64;  // granules of one pass (8 loads per thread)
+    auto src_of = [&](int j) {
+        const int pix = j / gpp, q = j - pix * gpp;  // pix over rows ih_lo.. x Wd
+        const int64_t src = ((int64_t)b * p.H + ih_lo) * p.Wd + pix;
+        return p.X + src * p.C + c0 + 16 * q;
+    };
+    auto put = [&](int j, const v4i &v) {
+        const int pix = j / gpp, q = j - pix * gpp;
+        const int rr = pix / p.Wd, iw = pix - rr * p.Wd;
+        const int r = ih_lo - ih0 + rr;
+        *(v4i *)(IN + r * rowL + (iw + p.pw) * kPixL + 16 * q) = v;
+    };
+    auto pad_rows = [&]() {
+        for (int e = tid; e < nrow_in * colsL; e += kWaves * 64) {
+            const int r = e / colsL, c = e - r * colsL;
+            const int ih = ih0 + r;
+            if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
+                v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
+                z[0] = z[1] = z[2] = z[3] = (v4i){p.pad4, p.pad4, p.pad4, p.pad4};
+            } else if (cs < kCS) {
+                // channels past the slice meet zero weights; keep them finite
+                for (int q = gpp; q < 4; ++q)
+                    *(v4i *)(IN + r * rowL + c * kPixL + 16 * q) = (v4i){0, 0, 0, 0};
+            }
+        }
+    };
+    if (total > 0 && total <= kPass) {
+        // one pass, straight-line, every load and LDS write unconditional (a
+        // granule past the end is the last one again, rewritten in place)
         v4i v[8];
-        if (total > 0) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int j = min(base + k * kWaves * 64 + tid, total - 1);
-                const int pix = j / gpp, q = j - pix * gpp;  // pix over rows ih_lo.. x Wd
-                const int64_t src = ((int64_t)b * p.H + ih_lo) * p.Wd + pix;
-                v[k] = *(const v4i *)(p.X + src * p.C + c0 + 16 * q);
-            }
-        }
-        if (base == 0) {
-            for (int e = tid; e < nrow_in * colsL; e += kWaves * 64) {
-                const int r = e / colsL, c = e - r * colsL;
-                const int ih = ih0 + r;
-                if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
-                    v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
-                    z[0] = z[1] = z[2] = z[3] = (v4i){p.pad4, p.pad4, p.pad4, p.pad4};
-                } else if (cs < kCS) {
-                    // channels past the slice meet zero weights; keep them finite
-                    for (int q = gpp; q < 4; ++q)
-                        *(v4i *)(IN + r * rowL + c * kPixL + 16 * q) = (v4i){0, 0, 0, 0};
-                }
-            }
-        }
-        if (total > 0) {
+        for (int k = 0; k < 8; ++k)
+            v[k] = *(const v4i *)src_of(min(k * kWaves * 64 + tid, total - 1));
+        load_params();
+        pad_rows();
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int j = base + k * kWaves * 64 + tid;
-                if (j < total) {
-                    const int pix = j / gpp, q = j - pix * gpp;
-                    const int rr = pix / p.Wd, iw = pix - rr * p.Wd;
-                    const int r = ih_lo - ih0 + rr;
-                    *(v4i *)(IN + r * rowL + (iw + p.pw) * kPixL + 16 * q) = v[k];
+        for (int k = 0; k < 8; ++k)
+            put(min(k * kWaves * 64 + tid, total - 1), v[k]);
+    } else {
+        load_params();
+        for (int base = 0; base == 0 || base < total; base += kPass) {
+            v4i v[8];
+            if (total > 0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = *(const v4i *)src_of(min(base + k * kWaves * 64 + tid, total - 1));
+            }
+            if (base == 0)
+                pad_rows();
+            if (total > 0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int j = base + k * kWaves * 64 + tid;
+                    if (j < total)
+                        put(j, v[k]);
                 }
             }
         }
     }
     drain_and_barrier();
     if (tid < kCS) {
-        prm[tid] = pb;
-        prm[kCS + tid] = pm;
-        prm[2 * kCS + tid] = ps;
+        const bool in = tid < cs;  // channels past the slice: 0, 0, 31
+        prm[tid] = in && p.bias ? bv : 0;
+        prm[kCS + tid] = in ? mv : 0;
+        prm[2 * kCS + tid] = in ? sv : 31;
     }
     __syncthreads();
+
+    // ---- diagonal weight operands: slice s (taps 4s..4s+3), group n; the
+    //      lane (column col = output channel 16n + col, K group g = tap
+    //      4s + g) holds w[4s + g][c0 + 16n + col] at byte col of 16 ----
+    v4i wd[kSlices][4];
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            v4i v = {0, 0, 0, 0};
+            const int w = 4 * s + g < KK && 16 * n < cs ? wb[s][n] : 0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                v[d] = (col >> 2) == d ? (w << (8 * (col & 3))) : 0;
+            wd[s][n] = v;
+        }
 
     // ---- this lane's pixel in each of the wave's M tiles (LDS offset of
     //      its (0, 0) tap) and its tap in each slice ----
