@@ -338,8 +338,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
     // the first barrier needs anyway).
     if (staged) {
         const int kbase = wave * (kSteps * 64);
+        // every workgroup copies the same activation bytes: each starts at
+        // its own token, so that the workgroups of an XCD do not all read
+        // the same L2 lines at once
+        const int rot = (int)(blockIdx.x >> 3) & 15;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t0 = 0; t0 < 16; ++t0) {
+            const int t = (t0 + rot) & 15;
             const int8_t *src = p.A + (int64_t)min(tok - col + t, p.M - 1) * p.lda +
                                 min(kbase + 16 * (lane ^ t), p.K - 16);
             __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
@@ -354,7 +359,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_skinny_w4a8(SkinnyArgs p)
         if constexpr (TB == 2) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t0 = 0; t0 < 16; ++t0) {
+                const int t = (t0 + rot) & 15;
                 const int8_t *src = p.A + (int64_t)min(tok - col + 16 + t, p.M - 1) * p.lda +
                                     min(kbase + 16 * (lane ^ t), p.K - 16);
                 __builtin_amdgcn_global_load_lds((const glb_void_t *)src,
