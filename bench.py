@@ -623,7 +623,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; runs on more than one GPU are not "
-              "part of it (the path shards by output channel, see the design notes)",
+              "part of it (across GPUs the path would shard the output channels, each GPU "
+              "streaming only its own weight columns)",
               file=sys.stderr)
         sys.exit(2)
 
