@@ -714,6 +714,8 @@ int orc_gemm_w4a8_requant_msb(const int8_t *A, int64_t lda, const uint8_t *B, in
             int64_t acc = 0;
             for (int64_t k = 0; k < K; ++k)
                 acc += (int64_t)a[k] * (int64_t)orc_int4_at_msb(b, k);
+            if (acc < INT32_MIN || acc > INT32_MAX)
+                status |= ORC_E_RANGE;
             int8_t y = 0;
             status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[n], &y);
             C[r * ldc + n] = y;

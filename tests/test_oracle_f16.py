@@ -41,6 +41,13 @@ def test_conversion_matches_ieee_rne(orc):
     got = np.array([orc.f32_to_f16(v) for v in x], np.uint16)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+    # a NaN stays a NaN of the same sign (the quiet NaN as numpy gives it)
+    qnan = np.float32(np.nan)
+    assert orc.f32_to_f16(qnan) == int(_np_f16_bits(qnan))
+    assert orc.f32_to_f16(-qnan) == int(_np_f16_bits(-qnan))
+    for bits in (0x7F800001, 0x7FBFFFFF, 0xFFC00000, 0xFF800010):
+        h = orc.f32_to_f16(np.array([bits], np.uint32).view(np.float32)[0])
+        assert (h & 0x7C00) == 0x7C00 and (h & 0x3FF) != 0 and (h >> 15) == (bits >> 31)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 2), (7, 9, 64), (33, 20, 256), (5, 3, 4096)])
@@ -64,6 +71,10 @@ def test_gemm_f16_scales(orc):
     # either scale alone, and power-of-two scales that only move the exponent
     assert np.array_equal(orc.gemm_s4s4_f16(d["A"], d["B"], sa, None).view(np.uint16),
                           _np_f16_bits(acc * sa[:, None]))
+    # a subset of rows takes each selected row's own scale
+    rows = np.array([39, 0, 17, 17], np.int64)
+    sub = orc.gemm_s4s4_f16(d["A"], d["B"], sa, sb, rows=rows)
+    assert np.array_equal(sub.view(np.uint16), got.view(np.uint16)[rows])
     p2a = np.full(40, 2.0 ** -4, np.float32)
     p2b = np.full(24, 2.0 ** -3, np.float32)
     assert np.array_equal(orc.gemm_s4s4_f16(d["A"], d["B"], p2a, p2b).view(np.uint16),

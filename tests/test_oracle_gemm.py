@@ -135,6 +135,32 @@ def test_w4a8_requant_composition(orc):
                                                 d["shift"]), want)
 
 
+def test_requant_reports_an_accumulator_past_int32(orc):
+    """The accumulator is an int32: one past its range is an error even when
+    the bias would bring the sum back inside (all -128 x -128 rows give
+    16384 K; all -128 x -8 give 1024 K)."""
+    mult = np.array([1 << 30], np.int32)
+    shift = np.array([31], np.int32)
+    bias = np.array([-(1 << 30)], np.int32)
+    for K, bad in ((130000, False), (140000, True)):      # 2.13e9 fits, 2.29e9 does not
+        a = np.full((1, K), -128, np.int8)
+        if bad:
+            with pytest.raises(orc.OracleDomainError):
+                orc.gemm_s8s8_requant(a, a, bias, mult, shift)
+        else:
+            y = orc.gemm_s8s8_requant(a, a, bias, mult, shift)
+            assert y[0, 0] == 127          # (2129920000 - 2^30) / 2 saturates
+    for K, bad in ((2096000, False), (2098000, True)):     # 2^31 / 1024 = 2097152
+        a = np.full((1, K), -128, np.int8)
+        b = np.full((1, K // 2), 0x88, np.uint8)            # -8 in either nibble order
+        for msb in (False, True):
+            if bad:
+                with pytest.raises(orc.OracleDomainError):
+                    orc.gemm_w4a8_requant(a, b, bias, mult, shift, msb_first=msb)
+            else:
+                assert orc.gemm_w4a8_requant(a, b, bias, mult, shift, msb_first=msb)[0, 0] == 127
+
+
 def test_s4s4_range_error(orc):
     # an int32 overflow of the raw output is reported, not wrapped
     K = 2 ** 26  # 64 * 2^26 = 2^32 > int32

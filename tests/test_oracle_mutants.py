@@ -78,6 +78,44 @@ MUTANTS = {
     "f16_scale_b_dropped": ("            if (scale_b)\n                t = t * scale_b[n];",
                             "            if (scale_b)\n                t = t;"),
     "f16_overflow_check_dropped": ("if (a >= 0x477FF000u)", "if (0)"),
+    "s4s4_operand_repeated": ("orc_int4_at(a, k) * (int64_t)orc_int4_at(b, k)",
+                              "orc_int4_at(a, k) * (int64_t)orc_int4_at(a, k)"),
+    "s8s4_k_reversed": ("acc += (int64_t)a[k] * (int64_t)orc_int4_at(b, k);",
+                        "acc += (int64_t)a[k] * (int64_t)orc_int4_at(b, K - 1 - k);"),
+    "s4_row_stride_in_bytes": ("(const uint8_t *)A + m * (lda / 2)", "(const uint8_t *)A + m * lda"),
+    "requant_shift_per_tensor": ("dot_any(ka, A, lda, m, kb, B, ldb, n, K);\n"
+                                 "            if (acc < INT32_MIN || acc > INT32_MAX)\n"
+                                 "                status |= ORC_E_RANGE;\n            int8_t y = 0;\n"
+                                 "            status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[n]",
+                                 "dot_any(ka, A, lda, m, kb, B, ldb, n, K);\n"
+                                 "            if (acc < INT32_MIN || acc > INT32_MAX)\n"
+                                 "                status |= ORC_E_RANGE;\n            int8_t y = 0;\n"
+                                 "            status |= orc_requant(acc, bias ? bias[n] : 0, mult[n], shift[0]"),
+    "gemm_range_check_dropped": ("dot_any(ka, A, lda, m, kb, B, ldb, n, K);\n"
+                                 "            if (acc < INT32_MIN || acc > INT32_MAX)\n"
+                                 "                status |= ORC_E_RANGE;\n            int8_t y = 0;",
+                                 "dot_any(ka, A, lda, m, kb, B, ldb, n, K);\n            int8_t y = 0;"),
+    "msb_range_check_dropped": ("(int64_t)a[k] * (int64_t)orc_int4_at_msb(b, k);\n            if (acc < INT32_MIN || acc > INT32_MAX)\n"
+                                "                status |= ORC_E_RANGE;\n",
+                                "(int64_t)a[k] * (int64_t)orc_int4_at_msb(b, k);\n"),
+    "conv_stride_axes_swapped": ("int64_t ih = oh * sh - ph + kh;", "int64_t ih = oh * sw - ph + kh;"),
+    "conv_pixel_row_index": ("int64_t oh = (p / Wo) % Ho;\n        int64_t ow = p % Wo;\n"
+                             "        for (int64_t oc = 0; oc < C_out; ++oc) {\n"
+                             "            int64_t acc = conv_acc_at(",
+                             "int64_t oh = (p / Ho) % Ho;\n        int64_t ow = p % Wo;\n"
+                             "        for (int64_t oc = 0; oc < C_out; ++oc) {\n"
+                             "            int64_t acc = conv_acc_at("),
+    "f16_subnormal_shift": ("shift = -e - 1;", "shift = -e - 2;"),
+    "f16_underflow_threshold": ("if (e < -25)", "if (e < -24)"),
+    "f16_nan_as_infinity": ("(a > 0x7F800000u ? 0x7E00u : 0x7C00u)", "(0x7C00u)"),
+    "f16_scale_a_by_position": ("t = t * scale_a[m];", "t = t * scale_a[r];"),
+    "f16_decode_subnormal_unit": ("v = (float)m * (1.0f / 16777216.0f);", "v = (float)m * (1.0f / 8388608.0f);"),
+    "f16_decode_bias": ("((uint32_t)(e - 15 + 127) << 23)", "((uint32_t)(e - 14 + 127) << 23)"),
+    "bf16_decode_shift": ("{(uint32_t)b << 16}", "{(uint32_t)b << 15}"),
+    "quant_low_clamp": ("q = -(int64_t)qmax;", "q = -(int64_t)qmax - 1;"),
+    "quant_scale_stored_inverse": ("scale[m] = sc;", "scale[m] = sc > 0.0f ? 1.0f / sc : 0.0f;"),
+    "quant_int4_row_stride": ("(uint8_t *)Q + m * (ldq / 2) + k / 2", "(uint8_t *)Q + m * (ldq / 4) + k / 2"),
+    "quant_int8_row_stride": ("((int8_t *)Q)[m * ldq + k]", "((int8_t *)Q)[m * (ldq / 2) + k]"),
     "dw_tap_dropped": ("for (int64_t kw = 0; kw < KW; ++kw) {\n            const int64_t iw",
                        "for (int64_t kw = 0; kw + 1 < KW; ++kw) {\n            const int64_t iw"),
 }
