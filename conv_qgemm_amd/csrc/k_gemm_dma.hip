@@ -11,24 +11,30 @@
 // next block's transfer with the current block's compute through ping-pong
 // buffers; here the same idea runs as a 4-deep ring in LDS.
 //
-// Per workgroup (4 waves, 2x2, each owning 128x128 = 4x4 sub-tiles of
-// v_mfma_i32_32x32x32_i8, 256 accumulators in AGPRs):
+// Per workgroup (4 waves, 2x2, each owning 128x128 = 8x8 tiles of
+// v_mfma_i32_16x16x64_i8, 256 accumulators): the 16x16x64 shape, not
+// 32x32x32, because under the board's power limit a stream of it runs at a
+// higher engine clock (measured: 4.08 against 3.38 POP/s, 2045 against
+// 1700 MHz, on random operands with the same 256 accumulators);
 //   * a stage holds 64 bytes of K for the 256 A rows and 256 B rows (32 KB);
 //     each wave fills a quarter of it with 8 direct-to-LDS loads.  A load
 //     writes 64 lanes x 16 bytes contiguously, so the swizzle is chosen on
 //     the source side: LDS slot (row, p) receives logical chunk
-//     p ^ ((row >> 2) & 3) of that row, which spreads the 16 rows read in
-//     one LDS cycle of an MFMA operand fetch over all banks.  The loads go
+//     p ^ swz(row) of that row, which puts the 16 lanes of each LDS read
+//     cycle of a fragment fetch (16 rows, one 16-byte chunk each) on 16
+//     different bank groups.  The loads go
 //     through buffer resources: a lane's offset inside a tile is one VGPR,
 //     fixed for the whole walk, and the tile and stage enter as the scalar
 //     offset, so the loop forms no per-lane addresses (a flat 64-bit address
 //     per load cost about 2.5% of the s8s8 8192^3 time);
-//   * three stages are in flight while one is multiplied.  Each stage is
-//     read as two groups of 16-byte fragments; the second group's reads
-//     overlap the first group's MFMAs, and the next stage's first group is
-//     read behind the last MFMAs of this one.  The one barrier per stage
-//     sits between MFMAs, after this wave's loads of the next stage have
-//     landed (counted with vmcnt);
+//   * three stages are in flight while one is multiplied.  A wave's
+//     fragments of a stage are 8 A and 8 B row blocks of 16 rows; read
+//     group 0 is A and B blocks 0..3, group 1 blocks 4..7.  The quadrants
+//     (0,0), (0,1), (1,0) of the wave's 8x8 tiles multiply before the
+//     stage's one barrier, (1,1) after it: group 1 streams in behind (0,0),
+//     and the next stage's group 0 lands in the registers that (0,1) and
+//     (1,0) freed, behind (1,1).  The barrier sits after this wave's loads
+//     of the next stage have landed (counted with vmcnt);
 //   * a stage's 8 loads are spread over two iterations (2 right after the
 //     barrier that frees their slot, 6 between the next iteration's MFMAs),
 //     so the four waves never queue 32 loads at once;
@@ -38,10 +44,12 @@
 //     ring runs across tile boundaries (a tile's last stages issue the next
 //     tile's first), and per-tile parameters come in by direct-to-LDS loads
 //     into a double buffer, so a tile starts with its operands in LDS;
-//   * the epilogue works from registers: the int8 results of each 32x32
-//     sub-tile row are regrouped across the two half-waves with
-//     v_permlane32_swap into 16-byte stores, a 32-row band at a time so that
-//     each output line fills from consecutive stores.
+//   * the epilogue works from registers: a lane holds 4 adjacent columns
+//     of one row per 16x16 tile; for four tiles side by side a 4x4
+//     transpose over the 16-lane rows (v_permlane32_swap, then
+//     v_permlane16_swap) gives it 16 adjacent int8 results, one 16-byte
+//     store, a 16-row band at a time so that each output line fills from
+//     consecutive stores.
 #include <type_traits>
 
 #include "dev_common.hpp"
@@ -65,10 +73,6 @@ constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
 constexpr int kEarlyLoads = 2;                // issued right after the barrier
-#ifndef QG_DMA_PRE_J1
-#define QG_DMA_PRE_J1 2
-#endif
-constexpr int kPreJ1 = QG_DMA_PRE_J1;          // read group 1 sub-tile columns before the barrier
 #ifndef QG_DMA_GROUP_M
 #define QG_DMA_GROUP_M 4
 #endif
@@ -123,15 +127,19 @@ struct DmaArgs {
     const float *scale_b;  // EPI_F16: per-column scales, or null
 };
 
-// A 16-byte LDS read is served 16 lanes per cycle over 64 4-byte banks; the
-// 16 lanes of one phase read 16 consecutive rows (64 bytes apart) at the
-// same logical chunk.  XOR-ing the chunk with row bits 2..3 puts those 16
-// reads on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
-// 128-byte rows (int8 A facing int4 B): row r starts at bank group
-// 8 * (r & 1); XOR-ing the chunk (0..7) with row bits 1..3 spreads 16
-// consecutive rows over all 16 groups.
-__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+// A 16-byte LDS read is served 16 lanes per cycle over 64 4-byte banks
+// (16 bank groups of 16 bytes); the lanes of one cycle share lane bit 5 and
+// the parity of lane bits 2..4 (measured).  A fragment read gives lane L row
+// L & 15 of a 16-row block and logical chunk L >> 4, so one cycle holds
+// rows 0-3 and 12-15 at one chunk and rows 4-11 at the chunk next to it.
+// With 64-byte rows a row's bank groups are 4 (r & 3) + chunk; XOR-ing the
+// chunk with 3 * (row bit 3) makes the 16 (row, chunk) pairs of every cycle
+// land on 16 different groups.
+__device__ __forceinline__ int swz(int row) { return 3 * ((row >> 3) & 1); }
+// 128-byte rows (int8 A facing int4 B, chunk 2 (L >> 4) + h for K step h):
+// a row's groups are 8 (r & 1) + chunk, and XOR-ing the chunk (0..7) with
+// row bit 1 and 4 * row bit 3 does the same for both steps.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 1) & 1) | (((row >> 3) & 1) << 2); }
 
 // Wait until at most N of this wave's direct-to-LDS loads are in flight and
 // all of its LDS reads have returned, then meet the other waves.  After it,
@@ -172,18 +180,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     constexpr int kStageA = G::kStageA;
     constexpr int kRowA = G::kRowA;
     constexpr int kLoadsPerStage = G::kLoads;
-    // int8: a 16-byte fragment is one 32-value K step; int4: two steps
-    // (int8 A facing int4 B reads two A fragments per B fragment)
+    // int8: a lane's 16-byte fragment is its 16 values of one 64-value K
+    // step; int4: of two steps (int8 A facing int4 B reads two A fragments
+    // per B fragment)
     constexpr int STEPS_PER_READ = KIND == OP_S8 ? 1 : 2;
     constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : (MIX ? 4 : 0);
-    constexpr int MG = 16 * STEPS_PER_READ;  // MFMAs per read group
+    constexpr int MQ = 16 * STEPS_PER_READ;  // MFMAs per quadrant of 4x4 tiles
     constexpr int DSG = G::kDsPerGroup;
-    // MFMAs of a stage before its barrier (read group 0, and the first
-    // kPreJ1 sub-tile columns of group 1) and after it (the rest of group 1,
-    // which covers the reads of the next stage's group 0)
-    constexpr int kMfmaPerJ = 4 * STEPS_PER_READ;
-    constexpr int kMfmaPre = MG + kPreJ1 * kMfmaPerJ;
-    constexpr int kMfmaPost = (4 - kPreJ1) * kMfmaPerJ;
+    // MFMAs of a stage before its barrier (quadrants (0,0), (0,1), (1,0))
+    // and after it (quadrant (1,1), which covers the reads of the next
+    // stage's group 0)
+    constexpr int kMfmaPre = 3 * MQ;
+    constexpr int kMfmaPost = MQ;
     constexpr int kPreMfmaPerLoad = (kMfmaPre - DSG) / (G::kLoads - kEarlyLoads);
     static_assert(kPreMfmaPerLoad >= 1 && kMfmaPost >= DSG / 2, "stage schedule");
     constexpr bool RQ = EPI == EPI_REQUANT || EPI == EPI_REQUANT_ZP;
@@ -322,51 +330,66 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                           isb ? p.b_bytes : p.a_bytes, src[l], (uint32_t)off, dst);
     };
 
-    // ---- fragment addresses inside a stage: read group g covers chunk
-    //      2g + (lane >> 5) of rows (lane & 31) + 32 * sub-tile.  The swizzle
-    //      only sees row bits 2..3, so sub-tile i is a fixed offset i*2048 ----
-    //      With 128-byte A rows the K values of B chunk c (16 bytes = 32
-    //      int4 values) are A chunks 2c and 2c + 1; the swizzle sees row bits
-    //      1..3, so sub-tile i is again a fixed offset (i*4096) ----
-    int a_rd[2][2], b_rd[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int ra = wm * 128 + (lane & 31);
-        const int rb = wn * 128 + (lane & 31);
-        const int c = 2 * g + (lane >> 5);
+    // ---- fragment addresses inside a stage: lane L reads row L & 15 of a
+    //      16-row block at logical chunk L >> 4 (with 128-byte A rows, chunks
+    //      2 (L >> 4) and 2 (L >> 4) + 1, one per K step of the int4 B
+    //      fragment).  The swizzles see row bits 1..3 only, so A block i is
+    //      a fixed offset i * 16 * kRowA and B block j one of j * 16 * kRowB ----
+    int a_rd[2], b_rd;
+    {
+        const int ra = wm * 128 + (lane & 15);
+        const int rb = wn * 128 + (lane & 15);
+        const int c = lane >> 4;
         if constexpr (MIX) {
-            a_rd[g][0] = ra * kRowA + (((2 * c) ^ swz8(ra)) << 4);
-            a_rd[g][1] = ra * kRowA + (((2 * c + 1) ^ swz8(ra)) << 4);
+            a_rd[0] = ra * kRowA + (((2 * c) ^ swz8(ra)) << 4);
+            a_rd[1] = ra * kRowA + (((2 * c + 1) ^ swz8(ra)) << 4);
         } else {
-            a_rd[g][0] = a_rd[g][1] = ra * kRowA + ((c ^ swz(ra)) << 4);
+            a_rd[0] = a_rd[1] = ra * kRowA + ((c ^ swz(ra)) << 4);
         }
-        b_rd[g] = kStageA + rb * kRowB + ((c ^ swz(rb)) << 4);
+        b_rd = kStageA + rb * kRowB + ((c ^ swz(rb)) << 4);
     }
 
-    v16i acc[16];
+    // tile (i, j) of the wave's 8x8: rows wm*128 + 16i .., columns
+    // wn*128 + 16j ..
+    v4i acc[64];
 
-    // raw fragments of read groups 0 and 1 (int8 A facing int4 B: two A
-    // fragments per sub-tile, [i] and [4 + i])
+    // raw fragments of read groups 0 and 1: A blocks 4g .. 4g+3 (int8 A
+    // facing int4 B: the second K step's in [4 + ..]) and B blocks 4g .. 4g+3
     constexpr int NA = MIX ? 8 : 4;
     v4i fa[2][NA], fb[2][4];
 
+    // in the order the MFMAs consume them: group 0 feeds quadrant (0,0)
+    // first, group 1 quadrant (0,1) (its B blocks) before (1,0) (its A)
     auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[4]) __attribute__((always_inline)) {
         const uint8_t *st = lds + slot * kStage;
+        auto rd_a = [&](int ii) __attribute__((always_inline)) {
+            ra[ii] = *(const v4i *)(st + a_rd[0] + (4 * g + ii) * 16 * kRowA);
+            if constexpr (MIX)
+                ra[4 + ii] = *(const v4i *)(st + a_rd[1] + (4 * g + ii) * 16 * kRowA);
+        };
+        auto rd_b = [&](int jj) __attribute__((always_inline)) {
+            rb[jj] = *(const v4i *)(st + b_rd + (4 * g + jj) * 16 * kRowB);
+        };
+        if (g == 0) {
+            rd_b(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ra[i] = *(const v4i *)(st + a_rd[g][0] + i * 32 * kRowA);
-        if constexpr (MIX) {
+            for (int ii = 0; ii < 4; ++ii)
+                rd_a(ii);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ra[4 + i] = *(const v4i *)(st + a_rd[g][1] + i * 32 * kRowA);
+            for (int jj = 1; jj < 4; ++jj)
+                rd_b(jj);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                rd_b(jj);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                rd_a(ii);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rb[i] = *(const v4i *)(st + b_rd[g] + i * 32 * kRowB);
     };
 
-    // MFMAs of one read group over sub-tiles (j, i) in [j0, j1) x [0, 4)
-    auto mma_group = [&](const v4i(&ra)[NA], const v4i(&rb)[4], int j0, int j1) __attribute__((always_inline)) {
+    // the 4x4 tiles of quadrant (qa, qb) from one A group and one B group
+    auto mma_quad = [&](const v4i(&ra)[NA], const v4i(&rb)[4], int qa, int qb) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < STEPS_PER_READ; ++h) {
             // int8 A facing int4 B: K step h of this group is A fragment
@@ -374,31 +397,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             v4i as[MIX ? 4 : 1];
             if constexpr (MIX) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    as[i] = even_odd_split<MSB>(ra[4 * h + i]);
+                for (int ii = 0; ii < 4; ++ii)
+                    as[ii] = even_odd_split<MSB>(ra[4 * h + ii]);
             }
 #pragma unroll
-            for (int j = j0; j < j1; ++j) {
+            for (int jj = 0; jj < 4; ++jj) {
                 v4i bq;
                 if constexpr (KIND == OP_S8) {
-                    bq = rb[j];
+                    bq = rb[jj];
                 } else {
-                    v2u w = {(unsigned)rb[j][2 * h], (unsigned)rb[j][2 * h + 1]};
+                    v2u w = {(unsigned)rb[jj][2 * h], (unsigned)rb[jj][2 * h + 1]};
                     bq = widen_int4_x16(w);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int ii = 0; ii < 4; ++ii) {
                     v4i aq;
                     if constexpr (KIND == OP_S8) {
-                        aq = ra[i];
+                        aq = ra[ii];
                     } else if constexpr (MIX) {
-                        aq = as[i];
+                        aq = as[ii];
                     } else {
-                        v2u w = {(unsigned)ra[i][2 * h], (unsigned)ra[i][2 * h + 1]};
+                        v2u w = {(unsigned)ra[ii][2 * h], (unsigned)ra[ii][2 * h + 1]};
                         aq = widen_int4_x16(w);
                     }
-                    acc[j * 4 + i] =
-                        __builtin_amdgcn_mfma_i32_32x32x32_i8(bq, aq, acc[j * 4 + i], 0, 0, 0);
+                    const int t = (4 * qa + ii) * 8 + 4 * qb + jj;
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bq, aq, acc[t], 0, 0, 0);
                 }
             }
         }
@@ -424,25 +447,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 
     for (int k = 0;; ++k) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            for (int e = 0; e < 16; ++e)
-                acc[i][e] = 0;
+        for (int t = 0; t < 64; ++t)
+            acc[t] = (v4i){0, 0, 0, 0};
         // the last kStages - 1 stages issue the next tile's first loads (the
         // ring is never deeper than a tile: nkt >= kStages)
         for (int kt = 0; kt < nkt; ++kt) {
             // slots of stages kt + kStages - 1 (the one before rs) and kt + 1
             const int ps = rs == 0 ? kStages - 1 : rs - 1;
             const int ns = rs == kStages - 1 ? 0 : rs + 1;
-            // group 1 of this stage streams in behind group 0's MFMAs, and
+            // group 1 of this stage streams in behind quadrant (0,0), and
             // the rest of stage kt+kStages-1 (its slot was freed at the last
             // barrier)
             read_group(rs, 1, fa[1], fb[1]);
 #pragma unroll
             for (int l = kEarlyLoads; l < kLoadsPerStage; ++l)
                 issue(kt + kStages - 1, ps, l);
-            mma_group(fa[0], fb[0], 0, 4);
-            if constexpr (kPreJ1 > 0)
-                mma_group(fa[1], fb[1], 0, kPreJ1);
+            mma_quad(fa[0], fb[0], 0, 0);
+            mma_quad(fa[0], fb[1], 0, 1);
+            mma_quad(fa[1], fb[0], 1, 0);
 #pragma unroll
             for (int i = 0; i < DSG; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -469,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             // after the last stage this reads the next tile's first
             // fragments, which are read again once the epilogue is done
             read_group(ns, 0, fa[0], fb[0]);
-            mma_group(fa[1], fb[1], kPreJ1, 4);
+            mma_quad(fa[1], fb[1], 1, 1);
 #pragma unroll
             for (int i = 0; i < kEarlyLoads; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -485,22 +507,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             rs = ns;
         }
 
-        // ---- epilogue: lane holds rows ml = wm*128 + i*32 + lane%32 and
-        //      columns nl = wn*128 + j*32 + q*8 + (lane/32)*4 + e of the
-        //      tile in accumulator registers 4q + e of sub-tile (j, i).  Its
-        //      parameters landed before the last stage's barrier; the ring
-        //      already holds the next tile's first stages ----
+        // ---- epilogue: for tile (i, j) a lane holds row
+        //      ml = wm*128 + 16i + lane%16 and columns
+        //      nl = wn*128 + 16j + 4 (lane/16) + e, e = 0..3, of the tile in
+        //      acc[i*8 + j][e].  Its parameters landed before the last
+        //      stage's barrier; the ring already holds the next tile's first
+        //      stages ----
         int(*prm)[kBN] = prm_buf[k & 1];
         const int lane = fresh_lane();
-        const int khalf = lane >> 5;
+        const int lg = lane >> 4;
         if constexpr (RQ) {
             // requantize with the cheapest exact form that every shift of
             // the tile allows (chosen once, so the accumulator indices stay
-            // compile-time constants).  For each 32x32 sub-tile a lane
-            // packs its 16 results of one row into 4 dwords (q = 0..3, 4
-            // columns each); one v_permlane32_swap per dword pair gives the
-            // lower half-wave columns 0..15 and the upper columns 16..31 of
-            // that row, stored as one 16-byte write.
+            // compile-time constants).  A lane packs the 4 results of each
+            // tile into a dword; over four tiles side by side a 4x4
+            // transpose across the 16-lane rows gives lane row g the 16
+            // adjacent results of tile 4J + g, stored as one 16-byte write.
             const v4i sh4 = *(const v4i *)&prm[2][lane * 4];
             bool s33 = true, s31 = true;
             for (int e = 0; e < 4; ++e) {
@@ -514,30 +536,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             const bool vec_ok = ((p.ldc | n0) & 15) == 0;
             auto requant_tile = [&](auto tier_tag) __attribute__((always_inline)) {
                 constexpr int TIER = decltype(tier_tag)::value;
-                // one 32-row band at a time, its four sub-tiles back to back,
+                // one 16-row band at a time, its 128 columns back to back,
                 // so that each 128-byte line of a row is written by
                 // consecutive stores (a line left partly written in L2 for
                 // long is written back in pieces)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ml = wm * 128 + i * 32 + (lane & 31);
+                for (int i = 0; i < 8; ++i) {
+                    const int ml = wm * 128 + i * 16 + (lane & 15);
                     const int rt = ZP ? prm[3][ml] : 0;
                     const int zo = ZP ? p.out_zero : 0;
                     const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
-                    int8_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128 + khalf * 16;
+                    int8_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int J = 0; J < 2; ++J) {
                         unsigned d[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
+                            const int j = 4 * J + q;
+                            const int nl = wn * 128 + j * 16 + lg * 4;
                             const v4i b4 = *(const v4i *)&prm[0][nl];
                             const v4i m4 = *(const v4i *)&prm[1][nl];
                             const v4i s4 = *(const v4i *)&prm[2][nl];
                             int y[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                int a = acc[j * 4 + i][4 * q + e] >> ACC_SHIFT;
+                                int a = acc[i * 8 + j][e] >> ACC_SHIFT;
                                 if constexpr (ZP)
                                     a = wrap_sub(a, rt);
                                 if constexpr (TIER == 2)
@@ -553,22 +576,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                             // int8 x int4: 4 values at a time, or
                             // accumulators spill, and each reload's wait
                             // holds the epilogue until the next tile's stages
-                            // have landed (W4A8 prefill 426.6 -> 416.3 us).
-                            // The int8 x int8 forms are no faster with it.
+                            // have landed.  The int8 x int8 forms are no
+                            // faster with it.
                             if constexpr (MIX)
                                 __builtin_amdgcn_sched_barrier(0);
                         }
+                        // 4x4 transpose over the lane rows: row g receives
+                        // dword g of rows 0..3, i.e. the 16 columns of tile
+                        // 4J + g in order
                         const auto r02 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
                         const auto r13 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-                        const v4i out = {(int)r02[0], (int)r02[1], (int)r13[0], (int)r13[1]};
-                        int8_t *dst = row + j * 32;
+                        const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+                        const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+                        const v4i out = {(int)r01[0], (int)r01[1], (int)r23[0], (int)r23[1]};
+                        int8_t *dst = row + (4 * J + lg) * 16;
                         if (vec_ok) {
                             *(v4i *)dst = out;
                         } else {
                             for (int b = 0; b < 16; ++b)
                                 dst[b] = (int8_t)(out[b >> 2] >> (8 * (b & 3)));
                         }
-                        // one sub-tile's parameters in registers at a time:
+                        // four tiles' parameters in registers at a time:
                         // hoisting a whole band's would spill
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -581,67 +609,59 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             else
                 requant_tile(std::integral_constant<int, 0>{});
         } else if constexpr (F16) {
-            // binary16: 4 adjacent columns of one row per 8-byte store, a
-            // 32-row band at a time so that each row's lines fill from
-            // consecutive stores
+            // binary16: a tile's 4 adjacent columns of one row per 8-byte
+            // store, a 16-row band at a time so that each row's lines fill
+            // from consecutive stores
             uint16_t *C = (uint16_t *)p.C;
             const bool vec = ((p.ldc | n0) & 3) == 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ml = wm * 128 + i * 32 + (lane & 31);
+            for (int i = 0; i < 8; ++i) {
+                const int ml = wm * 128 + i * 16 + (lane & 15);
                 const float sa = __int_as_float(prm[3][ml]);
                 uint16_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v16i &a = acc[j * 4 + i];
+                for (int j = 0; j < 8; ++j) {
+                    const int nl = wn * 128 + j * 16 + lg * 4;
+                    const v4i sb4 = *(const v4i *)&prm[0][nl];
+                    unsigned short h[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                        const v4i sb4 = *(const v4i *)&prm[0][nl];
-                        unsigned short h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float t = (float)(a[4 * q + e] >> ACC_SHIFT) * sa;
-                            h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
-                        }
-                        uint16_t *dst = row + nl;
-                        if (vec) {
-                            v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
-                                     (unsigned)h[2] | ((unsigned)h[3] << 16)};
-                            *(v2u *)dst = w;
-                        } else {
-                            for (int e = 0; e < 4; ++e)
-                                dst[e] = h[e];
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        const float t = (float)(acc[i * 8 + j][e] >> ACC_SHIFT) * sa;
+                        h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
+                    }
+                    uint16_t *dst = row + nl;
+                    if (vec) {
+                        v2u w = {(unsigned)h[0] | ((unsigned)h[1] << 16),
+                                 (unsigned)h[2] | ((unsigned)h[3] << 16)};
+                        *(v2u *)dst = w;
+                    } else {
+                        for (int e = 0; e < 4; ++e)
+                            dst[e] = h[e];
                     }
                 }
             }
         } else {
-            // raw int32: 4 adjacent columns of one row per 16-byte store, a
-            // 32-row band at a time so that each row's lines fill from
-            // consecutive stores
+            // raw int32: a tile's 4 adjacent columns of one row per 16-byte
+            // store, a 16-row band at a time so that each row's lines fill
+            // from consecutive stores
             int32_t *C = (int32_t *)p.C;
             const bool vec = ((p.ldc | n0) & 3) == 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ml = wm * 128 + i * 32 + (lane & 31);
+            for (int i = 0; i < 8; ++i) {
+                const int ml = wm * 128 + i * 16 + (lane & 15);
                 int32_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v16i &a = acc[j * 4 + i];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int nl = wn * 128 + j * 32 + q * 8 + khalf * 4;
-                        v4i y;
+                for (int j = 0; j < 8; ++j) {
+                    const int nl = wn * 128 + j * 16 + lg * 4;
+                    v4i y;
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = acc[i * 8 + j][e] >> ACC_SHIFT;
+                    int32_t *dst = row + nl;
+                    if (vec) {
+                        *(v4i *)dst = y;
+                    } else {
                         for (int e = 0; e < 4; ++e)
-                            y[e] = a[4 * q + e] >> ACC_SHIFT;
-                        int32_t *dst = row + nl;
-                        if (vec) {
-                            *(v4i *)dst = y;
-                        } else {
-                            for (int e = 0; e < 4; ++e)
-                                dst[e] = y[e];
-                        }
+                            dst[e] = y[e];
                     }
                 }
             }

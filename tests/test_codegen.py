@@ -18,7 +18,7 @@ SRC = os.path.join(ROOT, "conv_qgemm_amd", "csrc", "k_gemm_dma.hip")
 def asm(tmp_path_factory):
     out = tmp_path_factory.mktemp("asm") / "k_gemm_dma.s"
     from conv_qgemm_amd import build
-    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    cmd = [build.HIPCC, *build.flags_for(SRC), "--cuda-device-only", "-S", SRC, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
 
@@ -72,7 +72,12 @@ def test_main_loop_shape(asm):
         # no per-lane address arithmetic for the loads: the loop's only
         # 64-bit VALU ops would be address adds
         assert not any(ln.startswith(("v_lshl_add_u64", "v_add_co_u32")) for ln in loop), name
-        assert sum("v_mfma_i32_32x32x32_i8" in ln for ln in loop) == (32 if kind == 8 else 64), name
+        # a stage is 8x8 tiles of 16x16x64 per wave: 64 MFMAs for int8, two
+        # K steps (128) when a 64-byte fragment row holds packed int4
+        assert sum("v_mfma_i32_16x16x64_i8" in ln for ln in loop) == (64 if kind == 8 else 128), name
+        assert not any("v_mfma_i32_32x32" in ln for ln in loop), name
+        # every MFMA accumulates in place: no accumulator copies in the loop
+        assert not any(ln.startswith("v_accvgpr") for ln in loop), name
 
 
 def test_accumulators_not_spilled(asm):
@@ -90,7 +95,7 @@ def test_binary16_output_rounds_twice(tmp_path, src):
     once and differ from the definition in rare cases."""
     from conv_qgemm_amd import build
     out = tmp_path / (src + ".s")
-    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S",
+    cmd = [build.HIPCC, *build.flags_for(src), "--cuda-device-only", "-S",
            os.path.join(ROOT, "conv_qgemm_amd", "csrc", src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
@@ -107,7 +112,7 @@ def test_skinny_staged_readback_waits_for_the_copies_only(tmp_path):
     one-chunk kernels, one and two token blocks, both nibble orders."""
     from conv_qgemm_amd import build
     out = tmp_path / "k_skinny_w4a8.s"
-    cmd = [build.HIPCC, *build.CFLAGS, "--cuda-device-only", "-S",
+    cmd = [build.HIPCC, *build.flags_for("k_skinny_w4a8.hip"), "--cuda-device-only", "-S",
            os.path.join(ROOT, "conv_qgemm_amd", "csrc", "k_skinny_w4a8.hip"), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
