@@ -323,7 +323,7 @@ def _calib_lib():
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.qgc_stream_read.argtypes = [P, I64, P, I32, I32, P]
     lib.qgc_stream_read.restype = I32
-    lib.qgc_mfma_stream.argtypes = [P, I32, P, P, I32, P]
+    lib.qgc_mfma_stream.argtypes = [P, I32, P, P, I32, I32, P]
     lib.qgc_mfma_stream.restype = I32
     lib.qgc_wall_clock_khz.argtypes = []
     lib.qgc_wall_clock_khz.restype = I32
@@ -373,44 +373,57 @@ def read_calibration(torch, reps=5):
 
 
 def mfma_calibration(torch, cus, iters=20000, reps=5, seed=99):
-    """int8 matrix-core ceiling on random operands: v_mfma_i32_32x32x32_i8
-    back to back, 16 accumulators per wave, 4 waves per CU, one workgroup
-    per CU; the median of `reps` launches of ~5 ms.  The clock it ran at is
-    the shader-clock counter over the constant-rate counter around the loop
-    (s_memtime / s_memrealtime), times the latter's rate."""
+    """int8 matrix-core ceiling on random operands, 256 accumulator registers
+    per wave, 4 waves per CU, one workgroup per CU, for two MFMA shapes:
+    v_mfma_i32_32x32x32_i8 over 4x4 tiles and v_mfma_i32_16x16x64_i8 over 8x8
+    tiles (the same MACs per round: `iters` rounds of the first, iters/2 of
+    the second); the median of `reps` launches of ~5 ms each.  Under the
+    power limit the two run at different clocks; the faster is the ceiling.
+    The clock is the shader-clock counter over the constant-rate counter
+    around the loop (s_memtime / s_memrealtime), times the latter's rate."""
     import numpy as np
     lib = _calib_lib()
     g = np.random.default_rng(seed)
-    ops = torch.from_numpy(g.integers(-128, 127, size=cus * 4 * 8 * 64 * 16, endpoint=True,
+    ops = torch.from_numpy(g.integers(-128, 127, size=cus * 4 * 16 * 64 * 16, endpoint=True,
                                       dtype=np.int8)).cuda()
     clk = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
     sink = torch.zeros(cus * 256, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     wall_khz = lib.qgc_wall_clock_khz()
-    res = []
-    for r in range(reps + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        rc = lib.qgc_mfma_stream(ops.data_ptr(), iters, clk.data_ptr(), sink.data_ptr(), cus,
-                                 ctypes_stream(st))
-        e1.record(st)
-        if rc != 0:
-            raise RuntimeError(f"qgc_mfma_stream: hip error {rc}")
-        torch.cuda.synchronize()
-        if r == 0:
-            continue  # warm-up launch
-        t = e0.elapsed_time(e1) * 1e-3
-        c = clk.cpu().numpy().reshape(cus, 4).astype(np.float64)
-        ratio = (c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1)
-        res.append((cus * 4 * iters * 16 * 65536 / t / 1e12, float(np.median(ratio))))
-    res.sort()
-    tops, ratio = res[len(res) // 2]
-    return {"mfma_random_tops": round(tops, 1),
-            "mfma_random_frac_of_peak": round(tops / PEAK_INT8_TOPS, 4),
-            "mfma_clock_mhz": round(ratio * wall_khz / 1e3, 1) if wall_khz else None,
+    shapes = {}
+    for shape, name, it, macs in ((0, "32x32x32", iters, 16 * 32768),
+                                  (1, "16x16x64", iters // 2, 64 * 16384)):
+        res = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = lib.qgc_mfma_stream(ops.data_ptr(), it, clk.data_ptr(), sink.data_ptr(), cus,
+                                     shape, ctypes_stream(st))
+            e1.record(st)
+            if rc != 0:
+                raise RuntimeError(f"qgc_mfma_stream: hip error {rc}")
+            torch.cuda.synchronize()
+            if r == 0:
+                continue  # warm-up launch
+            t = e0.elapsed_time(e1) * 1e-3
+            c = clk.cpu().numpy().reshape(cus, 4).astype(np.float64)
+            ratio = (c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1)
+            res.append((cus * 4 * it * macs * 2 / t / 1e12, float(np.median(ratio))))
+        res.sort()
+        tops, ratio = res[len(res) // 2]
+        shapes[name] = {"tops": round(tops, 1),
+                        "clock_mhz": round(ratio * wall_khz / 1e3, 1) if wall_khz else None,
+                        "rounds": it}
+    best = max(shapes, key=lambda k: shapes[k]["tops"])
+    return {"mfma_random_tops": shapes[best]["tops"],
+            "mfma_random_frac_of_peak": round(shapes[best]["tops"] / PEAK_INT8_TOPS, 4),
+            "mfma_clock_mhz": shapes[best]["clock_mhz"],
+            "mfma_shape": best,
+            "mfma_shapes": shapes,
             "wall_clock_khz": wall_khz,
-            "shape": f"{cus} workgroups x 4 waves x {iters} x 16 MFMA 32x32x32 i8, "
-                     f"random int8 operands, median of {reps} launches"}
+            "shape": f"{cus} workgroups x 4 waves, 256 accumulator registers per wave, "
+                     f"random int8 operands, median of {reps} launches per MFMA shape; "
+                     f"the faster shape is the ceiling"}
 
 
 def ctypes_stream(st):

@@ -7,12 +7,14 @@
 //     U loads in flight per thread.  The bandwidth-bound kernels (the skinny
 //     W4A8 weight stream, the activation quantizer) read far more than they
 //     write, so this, not a device copy, is their practical ceiling;
-//   * a matrix-core stream: v_mfma_i32_32x32x32_i8 back to back on random
-//     int8 operands held in registers, 16 independent accumulators per wave,
-//     4 waves per CU, one workgroup per CU.  The board's power limit pulls
-//     the engine clock down when the multiplier arrays toggle, so this is the
-//     practical int8 ceiling; the shader-clock and constant-rate counters
-//     read around the loop give the clock it ran at.
+//   * a matrix-core stream on random int8 operands held in registers, 256
+//     accumulator registers per wave, 4 waves per CU, one workgroup per CU:
+//     v_mfma_i32_32x32x32_i8 over 4x4 tiles, or v_mfma_i32_16x16x64_i8 over
+//     8x8 tiles.  The board's power limit pulls the engine clock down when
+//     the multiplier arrays toggle, and by how much depends on the shape
+//     (the 16x16x64 stream runs at a higher clock), so the faster of the two
+//     is the practical int8 ceiling; the shader-clock and constant-rate
+//     counters read around the loop give the clock it ran at.
 //
 // The bandwidth and the MAC count are the figures of merit the INT4 GEMM
 // article (www.cf-1.com/news/6060138) and the MCU conv front-end article
@@ -51,42 +53,65 @@ __global__ __launch_bounds__(256) void k_stream_read(const v4i *__restrict__ src
         sink[blockIdx.x] = r;
 }
 
-// ops: [grid * 4 waves][8 fragments][64 lanes] x 16 bytes of int8 operands.
-// clk[4 * block] = {shader clock at start, at end, constant-rate clock at
-// start, at end}, read by the first lane of wave 0 after the operands landed.
+// ops: [grid * 4 waves][16 fragments][64 lanes] x 16 bytes of int8
+// operands.  clk[4 * block] = {shader clock at start, at end, constant-rate
+// clock at start, at end}, read by the first lane of wave 0 after the
+// operands landed.  SHAPE 0: 32x32x32 over 4x4 tiles (fragments 0..7);
+// SHAPE 1: 16x16x64 over 8x8 tiles (fragments 0..15).
+template <int SHAPE>
 __global__ __launch_bounds__(256, 1) void k_mfma_stream(const v4i *__restrict__ ops, int iters,
                                                         long long *clk, int *sink)
 {
+    constexpr int NF = SHAPE == 0 ? 4 : 8;  // A and B fragments each
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    v4i a[4], b[4];
+    v4i a[NF], b[NF];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = ops[(gw * 8 + i) * 64 + lane];
-        b[i] = ops[(gw * 8 + 4 + i) * 64 + lane];
+    for (int i = 0; i < NF; ++i) {
+        a[i] = ops[(gw * 16 + i) * 64 + lane];
+        b[i] = ops[(gw * 16 + NF + i) * 64 + lane];
     }
-    v16i acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        for (int e = 0; e < 16; ++e)
-            acc[i][e] = 0;
+    int r = 0;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const long long t0 = __builtin_amdgcn_s_memtime();
     const long long r0 = __builtin_amdgcn_s_memrealtime();
-    for (int it = 0; it < iters; ++it) {
+    if constexpr (SHAPE == 0) {
+        v16i acc[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 16; ++i)
+            for (int e = 0; e < 16; ++e)
+                acc[i][e] = 0;
+        for (int it = 0; it < iters; ++it) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[j * 4 + i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j * 4 + i],
-                                                                       0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[j * 4 + i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[j * 4 + i],
+                                                                           0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            for (int e = 0; e < 16; ++e)
+                r ^= acc[i][e];
+    } else {
+        v4i acc[64];
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+            acc[i] = (v4i){0, 0, 0, 0};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[j * 8 + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b[j], a[i], acc[j * 8 + i],
+                                                                           0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+            for (int e = 0; e < 4; ++e)
+                r ^= acc[i][e];
     }
-    int r = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        for (int e = 0; e < 16; ++e)
-            r ^= acc[i][e];
     __syncthreads();
     const long long t1 = __builtin_amdgcn_s_memtime();
     const long long r1 = __builtin_amdgcn_s_memrealtime();
@@ -125,16 +150,21 @@ int qgc_stream_read(const void *src, int64_t bytes, unsigned *sink, int grid, in
     return (int)hipGetLastError();
 }
 
-// Run `iters` rounds of 16 int8 MFMAs (32x32x32 each) per wave on `grid`
-// workgroups of 4 waves.  ops: device memory of grid * 4 * 8 * 64 * 16
-// bytes; clk: device memory of 4 * grid int64; sink: grid * 256 int32.
-int qgc_mfma_stream(const void *ops, int iters, long long *clk, int *sink, int grid,
+// Run `iters` rounds per wave on `grid` workgroups of 4 waves: shape 0, 16
+// int8 MFMAs of 32x32x32 (524,288 MACs); shape 1, 64 of 16x16x64 (1,048,576
+// MACs).  ops: device memory of grid * 4 * 16 * 64 * 16 bytes; clk: device
+// memory of 4 * grid int64; sink: grid * 256 int32.
+int qgc_mfma_stream(const void *ops, int iters, long long *clk, int *sink, int grid, int shape,
                     void *stream)
 {
-    if (!ops || !clk || !sink || iters < 1 || grid < 1)
+    if (!ops || !clk || !sink || iters < 1 || grid < 1 || (shape != 0 && shape != 1))
         return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_mfma_stream, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                       (const v4i *)ops, iters, clk, sink);
+    if (shape == 0)
+        hipLaunchKernelGGL(k_mfma_stream<0>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                           (const v4i *)ops, iters, clk, sink);
+    else
+        hipLaunchKernelGGL(k_mfma_stream<1>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                           (const v4i *)ops, iters, clk, sink);
     return (int)hipGetLastError();
 }
 
