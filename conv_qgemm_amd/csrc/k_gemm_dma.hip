@@ -73,6 +73,17 @@ constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
 constexpr int kEarlyLoads = 2;                // issued right after the barrier
+#ifndef QG_DMA_WAVES
+#define QG_DMA_WAVES 4
+#endif
+// waves per workgroup, 2 along M x kWaves/2 along N; every wave owns 128
+// rows and kTN columns of the tile and loads kRPW of its A and B rows
+constexpr int kWaves = QG_DMA_WAVES;
+static_assert(kWaves == 4 || kWaves == 8, "2x2 or 2x4 waves");
+constexpr int kWN = kWaves / 2;
+constexpr int kTN = kBN / kWN;                 // 128 or 64
+constexpr int kNBJ = kTN / 16;                 // 16-column tiles per wave
+constexpr int kRPW = kBM / kWaves;             // rows per wave per operand per stage
 #ifndef QG_DMA_GROUP_M
 #define QG_DMA_GROUP_M 4
 #endif
@@ -93,9 +104,12 @@ struct Geo {
     static constexpr int kStageA = kBM * kRowA;
     static constexpr int kStage = kStageA + kBN * kRowB;
     static constexpr int kStages = kMix ? 3 : QG_DMA_STAGES;
-    static constexpr int kLoadsA = 64 * kRowA / 1024;  // per wave: 64 rows
-    static constexpr int kLoads = kLoadsA + 4;
-    static constexpr int kDsPerGroup = kMix ? 12 : 8;  // LDS fragment reads per read group
+    static constexpr int kLoadsA = kRPW * kRowA / 1024;  // per wave: kRPW rows
+    static constexpr int kLoadsB = kRPW * kRowB / 1024;
+    static constexpr int kLoads = kLoadsA + kLoadsB;
+    // LDS fragment reads per read group: 4 A blocks (two K steps each with
+    // 128-byte A rows) and half the wave's B blocks
+    static constexpr int kDsPerGroup = (kMix ? 8 : 4) + kNBJ / 2;
 };
 // EPI_REQUANT_ZP: the asymmetric form.  `bias` then holds the per-column
 // term bias - za * sum_k B + K * za * zb, `rterm` the per-row zb * sum_k A
@@ -170,7 +184,7 @@ __device__ __forceinline__ void dma_dword(const void *src, void *dst)
 }
 
 template <int KIND, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
+__global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
 {
     using G = Geo<KIND>;
     constexpr bool MIX = G::kMix;
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     // per B fragment)
     constexpr int STEPS_PER_READ = KIND == OP_S8 ? 1 : 2;
     constexpr int ACC_SHIFT = KIND == OP_S4 ? 8 : (MIX ? 4 : 0);
-    constexpr int MQ = 16 * STEPS_PER_READ;  // MFMAs per quadrant of 4x4 tiles
+    constexpr int MQ = 4 * (kNBJ / 2) * STEPS_PER_READ;  // MFMAs per quadrant of the wave's tiles
     constexpr int DSG = G::kDsPerGroup;
     // MFMAs of a stage before its barrier (quadrants (0,0), (0,1), (1,0))
     // and after it (quadrant (1,1), which covers the reads of the next
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWN, wn = wave % kWN;
 
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nkt = (KIND == OP_S8 ? p.K : p.K / 2) / kRowB;  // B bytes per row / 64
@@ -240,18 +254,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
         if constexpr (MIX) {
-            const int r = wave * 64 + i * 8 + (lane >> 3);
+            const int r = wave * kRPW + i * 8 + (lane >> 3);
             const int c = (lane & 7) ^ swz8(r);
             src[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
         } else {
-            const int r = wave * 64 + i * 16 + (lane >> 2);
+            const int r = wave * kRPW + i * 16 + (lane >> 2);
             const int c = (lane & 3) ^ swz(r);
             src[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wave * 64 + i * 16 + (lane >> 2);
+    for (int i = 0; i < G::kLoadsB; ++i) {
+        const int r = wave * kRPW + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
         src[LA + i] = (uint32_t)r * (uint32_t)p.ldb_b + c * 16;
     }
@@ -260,6 +274,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     //      tile, one 4-byte direct-to-LDS load per array; absent arrays are
     //      constants written once ----
     auto load_prm = [&](int buf, int m0, int n0) __attribute__((always_inline)) {
+        // waves 0..3 cover the tile's 256 columns (and rows), 64 each
+        if (kWaves > 4 && wave >= 4)
+            return;
         const int ln = fresh_lane();
         const int n = n0 + wave * 64 + ln;
         const int m = m0 + wave * 64 + ln;
@@ -281,6 +298,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     };
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+        if (tid >= kBN)
+            break;
         if (RQ && !p.bias)
             prm_buf[b][0][tid] = 0;
         if (ZP && !p.rterm)
@@ -322,8 +341,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         const bool nxt = s >= nkt;
         const bool isb = l >= LA;
         uint8_t *dst = lds + slot * kStage +
-                       (isb ? kStageA + wave * 4096 + (l - LA) * 1024
-                            : wave * (64 * kRowA) + l * 1024);
+                       (isb ? kStageA + wave * (kRPW * kRowB) + (l - LA) * 1024
+                            : wave * (kRPW * kRowA) + l * 1024);
         const int64_t off = isb ? (nxt ? b_nxt : b_cur) + (int64_t)s * kRowB
                                 : (nxt ? a_nxt : a_cur) + (int64_t)s * kRowA;
         buffer_load_lds16(isb ? (const void *)p.B : (const void *)p.A,
@@ -338,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     int a_rd[2], b_rd;
     {
         const int ra = wm * 128 + (lane & 15);
-        const int rb = wn * 128 + (lane & 15);
+        const int rb = wn * kTN + (lane & 15);
         const int c = lane >> 4;
         if constexpr (MIX) {
             a_rd[0] = ra * kRowA + (((2 * c) ^ swz8(ra)) << 4);
@@ -349,18 +368,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
         b_rd = kStageA + rb * kRowB + ((c ^ swz(rb)) << 4);
     }
 
-    // tile (i, j) of the wave's 8x8: rows wm*128 + 16i .., columns
-    // wn*128 + 16j ..
-    v4i acc[64];
+    // tile (i, j) of the wave's 8 x kNBJ: rows wm*128 + 16i .., columns
+    // wn*kTN + 16j ..
+    v4i acc[8 * kNBJ];
 
     // raw fragments of read groups 0 and 1: A blocks 4g .. 4g+3 (int8 A
-    // facing int4 B: the second K step's in [4 + ..]) and B blocks 4g .. 4g+3
+    // facing int4 B: the second K step's in [4 + ..]) and the wave's B
+    // blocks NB g .. NB g + NB - 1 (NB = kNBJ / 2)
     constexpr int NA = MIX ? 8 : 4;
-    v4i fa[2][NA], fb[2][4];
+    constexpr int NB = kNBJ / 2;
+    v4i fa[2][NA], fb[2][NB];
 
     // in the order the MFMAs consume them: group 0 feeds quadrant (0,0)
     // first, group 1 quadrant (0,1) (its B blocks) before (1,0) (its A)
-    auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[4]) __attribute__((always_inline)) {
+    auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[NB]) __attribute__((always_inline)) {
         const uint8_t *st = lds + slot * kStage;
         auto rd_a = [&](int ii) __attribute__((always_inline)) {
             ra[ii] = *(const v4i *)(st + a_rd[0] + (4 * g + ii) * 16 * kRowA);
@@ -368,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 ra[4 + ii] = *(const v4i *)(st + a_rd[1] + (4 * g + ii) * 16 * kRowA);
         };
         auto rd_b = [&](int jj) __attribute__((always_inline)) {
-            rb[jj] = *(const v4i *)(st + b_rd + (4 * g + jj) * 16 * kRowB);
+            rb[jj] = *(const v4i *)(st + b_rd + (NB * g + jj) * 16 * kRowB);
         };
         if (g == 0) {
             rd_b(0);
@@ -376,11 +397,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
             for (int ii = 0; ii < 4; ++ii)
                 rd_a(ii);
 #pragma unroll
-            for (int jj = 1; jj < 4; ++jj)
+            for (int jj = 1; jj < NB; ++jj)
                 rd_b(jj);
         } else {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
+            for (int jj = 0; jj < NB; ++jj)
                 rd_b(jj);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
     };
 
     // the 4x4 tiles of quadrant (qa, qb) from one A group and one B group
-    auto mma_quad = [&](const v4i(&ra)[NA], const v4i(&rb)[4], int qa, int qb) __attribute__((always_inline)) {
+    auto mma_quad = [&](const v4i(&ra)[NA], const v4i(&rb)[NB], int qa, int qb) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < STEPS_PER_READ; ++h) {
             // int8 A facing int4 B: K step h of this group is A fragment
@@ -401,7 +422,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                     as[ii] = even_odd_split<MSB>(ra[4 * h + ii]);
             }
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int jj = 0; jj < NB; ++jj) {
                 v4i bq;
                 if constexpr (KIND == OP_S8) {
                     bq = rb[jj];
@@ -420,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                         v2u w = {(unsigned)ra[ii][2 * h], (unsigned)ra[ii][2 * h + 1]};
                         aq = widen_int4_x16(w);
                     }
-                    const int t = (4 * qa + ii) * 8 + 4 * qb + jj;
+                    const int t = (4 * qa + ii) * kNBJ + NB * qb + jj;
                     acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bq, aq, acc[t], 0, 0, 0);
                 }
             }
@@ -447,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
 
     for (int k = 0;; ++k) {
 #pragma unroll
-        for (int t = 0; t < 64; ++t)
+        for (int t = 0; t < 8 * kNBJ; ++t)
             acc[t] = (v4i){0, 0, 0, 0};
         // the last kStages - 1 stages issue the next tile's first loads (the
         // ring is never deeper than a tile: nkt >= kStages)
@@ -546,21 +567,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                     const int rt = ZP ? prm[3][ml] : 0;
                     const int zo = ZP ? p.out_zero : 0;
                     const int lo = ZP ? p.act_min : -128, hi = ZP ? p.act_max : 127;
-                    int8_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * 128;
+                    int8_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0 + wn * kTN;
 #pragma unroll
-                    for (int J = 0; J < 2; ++J) {
+                    for (int J = 0; J < kNBJ / 4; ++J) {
                         unsigned d[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int j = 4 * J + q;
-                            const int nl = wn * 128 + j * 16 + lg * 4;
+                            const int nl = wn * kTN + j * 16 + lg * 4;
                             const v4i b4 = *(const v4i *)&prm[0][nl];
                             const v4i m4 = *(const v4i *)&prm[1][nl];
                             const v4i s4 = *(const v4i *)&prm[2][nl];
                             int y[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                int a = acc[i * 8 + j][e] >> ACC_SHIFT;
+                                int a = acc[i * kNBJ + j][e] >> ACC_SHIFT;
                                 if constexpr (ZP)
                                     a = wrap_sub(a, rt);
                                 if constexpr (TIER == 2)
@@ -620,13 +641,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 const float sa = __int_as_float(prm[3][ml]);
                 uint16_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int nl = wn * 128 + j * 16 + lg * 4;
+                for (int j = 0; j < kNBJ; ++j) {
+                    const int nl = wn * kTN + j * 16 + lg * 4;
                     const v4i sb4 = *(const v4i *)&prm[0][nl];
                     unsigned short h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float t = (float)(acc[i * 8 + j][e] >> ACC_SHIFT) * sa;
+                        const float t = (float)(acc[i * kNBJ + j][e] >> ACC_SHIFT) * sa;
                         h[e] = f32_to_f16_bits(t * __int_as_float(sb4[e]));
                     }
                     uint16_t *dst = row + nl;
@@ -651,11 +672,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_dma(DmaArgs p)
                 const int ml = wm * 128 + i * 16 + (lane & 15);
                 int32_t *row = C + (int64_t)(m0 + ml) * p.ldc + n0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int nl = wn * 128 + j * 16 + lg * 4;
+                for (int j = 0; j < kNBJ; ++j) {
+                    const int nl = wn * kTN + j * 16 + lg * 4;
                     v4i y;
                     for (int e = 0; e < 4; ++e)
-                        y[e] = acc[i * 8 + j][e] >> ACC_SHIFT;
+                        y[e] = acc[i * kNBJ + j][e] >> ACC_SHIFT;
                     int32_t *dst = row + nl;
                     if (vec) {
                         *(v4i *)dst = y;
@@ -716,7 +737,7 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     // one persistent workgroup per CU (the LDS ring allows no second)
     const int ntiles = a.tiles_m * a.tiles_n;
     const int grid = ntiles < d.cus ? ntiles : d.cus;
-    hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(grid), dim3(kWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 
