@@ -330,6 +330,50 @@ def _calib_lib():
     return lib
 
 
+def vendor_comparison(torch, M=8192, N=8192, K=8192, reps=10, seed=7):
+    """AMD's hipBLASLt int8 GEMM (int8 operands, int32 output, no requantize)
+    on the s8s8 workload's shape, every solution the library offers for it
+    timed (libqgvendor.so: 2 untimed calls, then the median of `reps` eager
+    calls between HIP events per solution), and 16 elements of the best
+    solution's output checked exactly."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "conv_qgemm_amd", "libqgvendor.so"))
+    P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+    lib.qgv_int8_gemm_search.argtypes = [P, P, P, I64, I64, I64, P, I64, I32, P,
+                                         ctypes.POINTER(D), ctypes.POINTER(D),
+                                         ctypes.POINTER(I32), ctypes.c_char_p, I32,
+                                         ctypes.c_char_p, I32]
+    lib.qgv_int8_gemm_search.restype = I32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    A = torch.randint(-128, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    B = torch.randint(-128, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    heur, best, n = D(-1), D(-1), I32(0)
+    bname, hname = ctypes.create_string_buffer(512), ctypes.create_string_buffer(512)
+    st = torch.cuda.current_stream()
+    rc = lib.qgv_int8_gemm_search(A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                                  ws.data_ptr(), ws.numel(), reps, ctypes_stream(st),
+                                  ctypes.byref(heur), ctypes.byref(best), ctypes.byref(n),
+                                  bname, 512, hname, 512)
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise RuntimeError(f"qgv_int8_gemm_search: {rc}")
+    rows = torch.randint(0, M, (16,), generator=g, device="cuda")
+    cols = torch.randint(0, N, (16,), generator=g, device="cuda")
+    want = (A[rows].to(torch.int64) * B[cols].to(torch.int64)).sum(dim=1)
+    ok = int((C[rows, cols].to(torch.int64) == want).sum())
+    ops = 2.0 * M * N * K
+    return {"library": "hipBLASLt", "problem": f"int8 {M}x{N}x{K}, int32 out, no requantize",
+            "heuristic_us": round(heur.value, 2),
+            "best_us": round(best.value, 2), "best_tops": round(ops / best.value / 1e6, 1),
+            "solutions_timed": n.value, "best_kernel": bname.value.decode()[:160],
+            "heuristic_kernel": hname.value.decode()[:160],
+            "checked": f"{ok} of 16 elements exact",
+            "timing": f"median of {reps} eager calls per solution between HIP events"}
+
+
 def read_calibration(torch, reps=5):
     """Best read-only streaming rates (GB/s) over a few launch shapes, with
     16-byte loads, grid-stride, `unroll` loads in flight per thread:
@@ -631,6 +675,8 @@ def main():
     ap.add_argument("--config", default="all", help="all, or a comma list of " + ",".join(ORDER))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration legs")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the hipBLASLt comparison on the s8s8 shape")
     ap.add_argument("--cpu-frac", type=int, default=2)
     args = ap.parse_args()
 
@@ -728,6 +774,12 @@ def main():
         copy_gbs = round(hbm_copy_gbs(torch), 1)
     except RuntimeError:
         copy_gbs = None
+    vendor = None
+    if not args.no_vendor and "s8s8" in names:
+        try:
+            vendor = vendor_comparison(torch)
+        except (OSError, RuntimeError) as e:
+            vendor = {"error": str(e)}
     clock.close()
 
     per = {}
@@ -817,6 +869,10 @@ def main():
         "calibration": calib,
         "hbm_copy_gb_s": copy_gbs,
     }
+    if vendor is not None:
+        if "best_us" in vendor:
+            vendor["this_kernel_us"] = per["s8s8"]["us_median"]
+        out["vendor_int8_gemm"] = vendor
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(step, args.cpu_frac)
     print(json.dumps(out))

@@ -20,6 +20,10 @@ OBJ = os.path.join(ROOT, "_build", "qgemm")
 LIB = os.path.join(PKG, "libqgemm.so")
 CALIB_LIB = os.path.join(PKG, "libqgcalib.so")
 CALIB_SOURCES = ["calib.hip"]
+# the benchmark's comparison with AMD's hipBLASLt int8 GEMM (its own library,
+# so that libqgemm.so does not depend on hipBLASLt)
+VENDOR_LIB = os.path.join(PKG, "libqgvendor.so")
+VENDOR_SOURCES = ["vendor_hipblaslt.cpp"]
 SOURCES = ["api.cpp", "k_tile_gemm.hip", "k_gemm_dma.hip", "k_skinny_w4a8.hip", "k_conv_halo.hip", "k_dwconv.hip",
            "k_quant.hip", "k_zp.hip"]
 
@@ -58,10 +62,10 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, lib, verbose):
+def _link(objs, lib, verbose, libs=()):
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
-           "-Wl,-rpath,/opt/rocm/lib"]
+           "-Wl,-rpath,/opt/rocm/lib", *libs]
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(tmp, lib)
     if verbose:
@@ -70,11 +74,13 @@ def _link(objs, lib, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    srcs = SOURCES + CALIB_SOURCES
+    srcs = SOURCES + CALIB_SOURCES + VENDOR_SOURCES
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
         objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB, verbose)
-    _link(objs[len(SOURCES):], CALIB_LIB, verbose)
+    n, c = len(SOURCES), len(CALIB_SOURCES)
+    _link(objs[:n], LIB, verbose)
+    _link(objs[n:n + c], CALIB_LIB, verbose)
+    _link(objs[n + c:], VENDOR_LIB, verbose, libs=["-L/opt/rocm/lib", "-lhipblaslt"])
     return LIB
 
 
