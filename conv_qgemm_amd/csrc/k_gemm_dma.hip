@@ -73,6 +73,12 @@ constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
 constexpr int kEarlyLoads = 2;                // issued right after the barrier
+#ifndef QG_DMA_PAIRS
+#define QG_DMA_PAIRS 1                        // paired stages for int8 / int4 operands
+#endif
+#ifndef QG_DMA_PAIR_FIRST
+#define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
+#endif
 #ifndef QG_DMA_WAVES
 #define QG_DMA_WAVES 4
 #endif
@@ -154,6 +160,11 @@ __device__ __forceinline__ int swz(int row) { return 3 * ((row >> 3) & 1); }
 // a row's groups are 8 (r & 1) + chunk, and XOR-ing the chunk (0..7) with
 // row bit 1 and 4 * row bit 3 does the same for both steps.
 __device__ __forceinline__ int swz8(int row) { return ((row >> 1) & 1) | (((row >> 3) & 1) << 2); }
+// Paired stages (int8 and int4 operands): stages 2j and 2j+1 share a slot
+// with 128-byte rows, stage 2j+h in chunks 4h .. 4h+3, read as chunk
+// 4h + (L >> 4).  XOR-ing the chunk with row bits 1..3 spreads both halves'
+// 16 reads of a cycle over the 16 bank groups.
+__device__ __forceinline__ int swzp(int row) { return (row >> 1) & 7; }
 
 // Wait until at most N of this wave's direct-to-LDS loads are in flight and
 // all of its LDS reads have returned, then meet the other waves.  After it,
@@ -183,11 +194,21 @@ __device__ __forceinline__ void dma_dword(const void *src, void *dst)
     __builtin_amdgcn_global_load_lds((const glb_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
 }
 
-template <int KIND, int EPI>
+template <int KIND, int EPI, bool PAIRS>
 __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
 {
     using G = Geo<KIND>;
     constexpr bool MIX = G::kMix;
+    static_assert(!(PAIRS && MIX), "paired stages take 64-byte rows of both operands");
+    // paired stages: slot of two stages, 128-byte rows, kLP loads per wave
+    // per pair (8 rows x 128 bytes each), kLP1 of them in the pair's first
+    // stage
+    constexpr int kRowP = 2 * kRowB;
+    constexpr int kPairA = kBM * kRowP;
+    constexpr int kPair = kPairA + kBN * kRowP;
+    constexpr int kLP = 2 * kRPW * kRowP / 1024;
+    constexpr int kLP1 = kLP * QG_DMA_PAIR_FIRST / 4;
+    static_assert(!PAIRS || 2 * kPair == G::kStages * G::kStage, "same LDS ring");
     constexpr bool MSB = KIND == OP_MIXM;
     constexpr int kStages = G::kStages;
     constexpr int kStage = G::kStage;
@@ -250,7 +271,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
     //      for the int8 A facing int4 B).  The per-lane offsets inside a
     //      tile are the same for every tile; a tile adds a scalar base ----
     constexpr int LA = G::kLoadsA;
-    uint32_t src[kLoadsPerStage];
+    constexpr int NSRC = PAIRS ? kLP : kLoadsPerStage;
+    uint32_t src[NSRC];
+    if constexpr (PAIRS) {
+        // load i: A rows (i < kLP/2) or B rows, 8 rows of 128 bytes each;
+        // lane L fetches logical chunk (L & 7) ^ swzp(row) of its row
+#pragma unroll
+        for (int i = 0; i < kLP; ++i) {
+            const bool isb = i >= kLP / 2;
+            const int r = wave * kRPW + (isb ? i - kLP / 2 : i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swzp(r);
+            src[i] = (uint32_t)r * (uint32_t)(isb ? p.ldb_b : p.lda_b) + c * 16;
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
         if constexpr (MIX) {
@@ -268,6 +301,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
         const int r = wave * kRPW + i * 16 + (lane >> 2);
         const int c = (lane & 3) ^ swz(r);
         src[LA + i] = (uint32_t)r * (uint32_t)p.ldb_b + c * 16;
+    }
     }
 
     // ---- per-tile parameters: this wave's 64 columns (and rows) of the
@@ -348,6 +382,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
         buffer_load_lds16(isb ? (const void *)p.B : (const void *)p.A,
                           isb ? p.b_bytes : p.a_bytes, src[l], (uint32_t)off, dst);
     };
+    // paired stages: load l (0..kLP/2-1: A, the rest B) of pair jp (stages
+    // 2jp, 2jp+1; jp >= nkt/2: the next tile's pair jp - nkt/2) into pair
+    // slot `slot`
+    auto issue_pair = [&](int jp, int slot, int l) __attribute__((always_inline)) {
+        const bool nxt = 2 * jp >= nkt;
+        const bool isb = l >= kLP / 2;
+        uint8_t *dst = lds + slot * kPair +
+                       (isb ? kPairA + wave * (kRPW * kRowP) + (l - kLP / 2) * 1024
+                            : wave * (kRPW * kRowP) + l * 1024);
+        const int64_t off = (isb ? (nxt ? b_nxt : b_cur) : (nxt ? a_nxt : a_cur)) +
+                            (int64_t)jp * kRowP;
+        buffer_load_lds16(isb ? (const void *)p.B : (const void *)p.A,
+                          isb ? p.b_bytes : p.a_bytes, src[l], (uint32_t)off, dst);
+    };
 
     // ---- fragment addresses inside a stage: lane L reads row L & 15 of a
     //      16-row block at logical chunk L >> 4 (with 128-byte A rows, chunks
@@ -355,10 +403,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
     //      fragment).  The swizzles see row bits 1..3 only, so A block i is
     //      a fixed offset i * 16 * kRowA and B block j one of j * 16 * kRowB ----
     int a_rd[2], b_rd;
+    // paired stages: A and B fragment addresses of stage half h
+    int ap_rd[2], bp_rd[2];
     {
         const int ra = wm * 128 + (lane & 15);
         const int rb = wn * kTN + (lane & 15);
         const int c = lane >> 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ap_rd[h] = ra * kRowP + (((4 * h + c) ^ swzp(ra)) << 4);
+            bp_rd[h] = kPairA + rb * kRowP + (((4 * h + c) ^ swzp(rb)) << 4);
+        }
         if constexpr (MIX) {
             a_rd[0] = ra * kRowA + (((2 * c) ^ swz8(ra)) << 4);
             a_rd[1] = ra * kRowA + (((2 * c + 1) ^ swz8(ra)) << 4);
@@ -381,15 +436,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
 
     // in the order the MFMAs consume them: group 0 feeds quadrant (0,0)
     // first, group 1 quadrant (0,1) (its B blocks) before (1,0) (its A)
-    auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[NB]) __attribute__((always_inline)) {
-        const uint8_t *st = lds + slot * kStage;
+    // (paired stages: h is the stage's half of its pair slot)
+    auto read_group = [&](int slot, int g, v4i(&ra)[NA], v4i(&rb)[NB], int h = 0) __attribute__((always_inline)) {
+        const uint8_t *st = lds + slot * (PAIRS ? kPair : kStage);
+        constexpr int pa = PAIRS ? kRowP : kRowA, pb = PAIRS ? kRowP : kRowB;
+        const int ard = PAIRS ? ap_rd[h] : a_rd[0], brd = PAIRS ? bp_rd[h] : b_rd;
         auto rd_a = [&](int ii) __attribute__((always_inline)) {
-            ra[ii] = *(const v4i *)(st + a_rd[0] + (4 * g + ii) * 16 * kRowA);
+            ra[ii] = *(const v4i *)(st + ard + (4 * g + ii) * 16 * pa);
             if constexpr (MIX)
                 ra[4 + ii] = *(const v4i *)(st + a_rd[1] + (4 * g + ii) * 16 * kRowA);
         };
         auto rd_b = [&](int jj) __attribute__((always_inline)) {
-            rb[jj] = *(const v4i *)(st + b_rd + (NB * g + jj) * 16 * kRowB);
+            rb[jj] = *(const v4i *)(st + brd + (NB * g + jj) * 16 * pb);
         };
         if (g == 0) {
             rd_b(0);
@@ -454,25 +512,103 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
     //      whole stages when it is waited for ----
     if constexpr (RQ || F16)
         load_prm(0, m0, n0);
+    if constexpr (PAIRS) {
+        // paired stages: pair 0 in slot 0; pair 1 follows during pair 0
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
+        for (int l = 0; l < kLP; ++l)
+            issue_pair(0, 0, l);
+        wait_loads_and_barrier<0>();
+    } else {
 #pragma unroll
-        for (int l = 0; l < kLoadsPerStage; ++l)
-            issue(s, s, l);
+        for (int s = 0; s < kStages - 1; ++s)
 #pragma unroll
-    for (int l = 0; l < kEarlyLoads; ++l)
-        issue(kStages - 1, kStages - 1, l);
-    wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage + kEarlyLoads>();
+            for (int l = 0; l < kLoadsPerStage; ++l)
+                issue(s, s, l);
+#pragma unroll
+        for (int l = 0; l < kEarlyLoads; ++l)
+            issue(kStages - 1, kStages - 1, l);
+        wait_loads_and_barrier<(kStages - 2) * kLoadsPerStage + kEarlyLoads>();
+    }
     read_group(0, 0, fa[0], fb[0]);
-    int rs = 0;  // ring slot of the stage being multiplied
+    int rs = 0;  // ring slot (paired stages: pair slot) of the stage being multiplied
+
+    // paired stages: the MFMA / LDS-read / load interleave of one stage,
+    // NL loads before the stage's last quadrant
+    auto pre_hints = [&]<int NL>() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < DSG; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        if constexpr (NL > 0) {
+            constexpr int per = (kMfmaPre - DSG) / NL;
+            static_assert(per >= 1, "stage schedule");
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPre - DSG - per * NL, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPre - DSG, 0);
+        }
+    };
+    auto post_hints = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < DSG / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPost - DSG / 2, 0);
+    };
 
     for (int k = 0;; ++k) {
 #pragma unroll
         for (int t = 0; t < 8 * kNBJ; ++t)
             acc[t] = (v4i){0, 0, 0, 0};
+        // paired stages: pair j multiplies from slot rs while pair j+1
+        // streams into the other slot (freed at the last barrier); one
+        // barrier per pair, after which pair j+1 has landed for every wave
+        // and no wave reads pair j any more.  The last pair issues the next
+        // tile's first.
+        if constexpr (PAIRS) {
+            for (int j = 0; j < nkt / 2; ++j) {
+                const int ns = rs ^ 1;
+                // stage 2j (first half of the slot)
+                read_group(rs, 1, fa[1], fb[1], 0);
+#pragma unroll
+                for (int l = 0; l < kLP1; ++l)
+                    issue_pair(j + 1, ns, l);
+                mma_quad(fa[0], fb[0], 0, 0);
+                mma_quad(fa[0], fb[1], 0, 1);
+                mma_quad(fa[1], fb[0], 1, 0);
+                pre_hints.template operator()<kLP1>();
+                __builtin_amdgcn_sched_barrier(0);
+                read_group(rs, 0, fa[0], fb[0], 1);
+                mma_quad(fa[1], fb[1], 1, 1);
+                post_hints();
+                __builtin_amdgcn_sched_barrier(0);
+                // stage 2j + 1 (second half)
+                read_group(rs, 1, fa[1], fb[1], 1);
+#pragma unroll
+                for (int l = kLP1; l < kLP; ++l)
+                    issue_pair(j + 1, ns, l);
+                mma_quad(fa[0], fb[0], 0, 0);
+                mma_quad(fa[0], fb[1], 0, 1);
+                mma_quad(fa[1], fb[0], 1, 0);
+                pre_hints.template operator()<kLP - kLP1>();
+                __builtin_amdgcn_sched_barrier(0);
+                wait_loads_and_barrier<0>();
+                __builtin_amdgcn_sched_barrier(0);
+                read_group(ns, 0, fa[0], fb[0], 0);
+                mma_quad(fa[1], fb[1], 1, 1);
+                post_hints();
+                rs = ns;
+            }
+        }
         // the last kStages - 1 stages issue the next tile's first loads (the
         // ring is never deeper than a tile: nkt >= kStages)
-        for (int kt = 0; kt < nkt; ++kt) {
+        for (int kt = 0; kt < (PAIRS ? 0 : nkt); ++kt) {
             // slots of stages kt + kStages - 1 (the one before rs) and kt + 1
             const int ps = rs == 0 ? kStages - 1 : rs - 1;
             const int ns = rs == kStages - 1 ? 0 : rs + 1;
@@ -737,7 +873,14 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     // one persistent workgroup per CU (the LDS ring allows no second)
     const int ntiles = a.tiles_m * a.tiles_n;
     const int grid = ntiles < d.cus ? ntiles : d.cus;
-    hipLaunchKernelGGL((k_gemm_dma<KIND, EPI>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    // paired stages for int8 and int4 operands whenever the stages pair up
+    // (the ring then holds this tile's pair and the next one: >= 2 pairs)
+    constexpr bool kCanPair = !Geo<KIND>::kMix && QG_DMA_PAIRS;
+    const int64_t nkt = (KIND == OP_S8 ? d.K : d.K / 2) / kRowB;
+    if (kCanPair && nkt % 2 == 0 && nkt >= 4)
+        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, kCanPair>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, false>), dim3(grid), dim3(kWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 

@@ -32,9 +32,10 @@ def _kernels(asm):
     return out
 
 
-# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize, s4s4 binary16,
-# w4a8 requantize (int4 weights low or high nibble first)
-N_INSTANTIATIONS = 6
+# s8s8 requantize, s4s4 raw int32, s8s8 asymmetric requantize, s4s4 binary16
+# (each stage by stage and in pairs of stages), w4a8 requantize (int4
+# weights low or high nibble first; stage by stage only)
+N_INSTANTIATIONS = 10
 
 
 def _nonempty(ks):
@@ -62,11 +63,19 @@ def test_main_loop_shape(asm):
     for name, body in _nonempty(_kernels(asm)).items():
         loop = _main_loop(body)
         waits = [ln for ln in loop if ln.startswith("s_waitcnt")]
-        assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (name, waits)
         assert sum("s_barrier" in ln for ln in loop) == 1, name
-        # operand kind: 8 int8 x int8, 4 int4 x int4, 3 / 5 int8 x int4
+        # operand kind: 8 int8 x int8, 4 int4 x int4, 3 / 5 int8 x int4;
+        # pairs: one loop iteration multiplies two 64-byte K stages
         kind = int(re.search(r"k_gemm_dmaILi(\d)E", name).group(1))
-        loads = 12 if kind in (3, 5) else 8
+        pairs = re.search(r"k_gemm_dmaILi\dELi\dELb1E", name) is not None
+        vm = [w for w in waits if "vmcnt" in w]
+        if pairs:
+            # the pair's loads are waited for once, at its barrier
+            assert len(vm) == 1 and re.search(r"vmcnt\(0\)", vm[0]), (name, waits)
+        else:
+            # the ring keeps the later stages' loads in flight at the barrier
+            assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (name, waits)
+        loads = 16 if pairs else 12 if kind in (3, 5) else 8
         assert sum(re.search(r"buffer_load_dwordx4 .* offen lds", ln) is not None
                    for ln in loop) == loads, name
         # no per-lane address arithmetic for the loads: the loop's only
@@ -74,7 +83,8 @@ def test_main_loop_shape(asm):
         assert not any(ln.startswith(("v_lshl_add_u64", "v_add_co_u32")) for ln in loop), name
         # a stage is 8x8 tiles of 16x16x64 per wave: 64 MFMAs for int8, two
         # K steps (128) when a 64-byte fragment row holds packed int4
-        assert sum("v_mfma_i32_16x16x64_i8" in ln for ln in loop) == (64 if kind == 8 else 128), name
+        per_stage = 64 if kind == 8 else 128
+        assert sum("v_mfma_i32_16x16x64_i8" in ln for ln in loop) == per_stage * (2 if pairs else 1), name
         assert not any("v_mfma_i32_32x32" in ln for ln in loop), name
         # every MFMA accumulates in place: no accumulator copies in the loop
         assert not any(ln.startswith("v_accvgpr") for ln in loop), name

@@ -431,6 +431,29 @@ def test_w4a8_ring_kernel(qg, M, N, K, msb):
     assert np.array_equal(C[rows], want)
 
 
+RING_STAGES = [(2048, 4096, 4), (2048, 4096, 5), (2000, 4100, 6), (1025, 8200, 7)]
+
+
+@pytest.mark.parametrize("M,N,stages", RING_STAGES)
+def test_ring_kernel_stage_parity(qg, M, N, stages):
+    """The ring kernel multiplies int8 and packed int4 operands in pairs of
+    64-byte K stages when the stage count is even (one slot of 128-byte rows
+    per pair) and stage by stage otherwise: 4 to 7 stages, ragged M and N,
+    every output of s8s8 (requantize) and s4s4 (raw int32) compared."""
+    _say("ring stages", M, N, stages)
+    K = 64 * stages
+    d = datagen.gemm_s8s8(M, N, K, seed=stages, shift=(37, 43))
+    C = host(qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    want = oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"], d["shift"])
+    assert np.array_equal(C, want)
+    K4 = 128 * stages  # 64 packed bytes per stage
+    d4 = datagen.gemm_s4s4(M, N, K4, seed=stages + 10)
+    C4 = host(qg.qgemm_s4s4_i32(dev(d4["A"]), dev(d4["B"])))
+    rows = _sample_rows(M, 64, seed=stages)
+    assert np.array_equal(C4[rows], oracle.gemm_s4s4_i32(d4["A"], d4["B"], rows=rows))
+
+
 def test_w4a8_ring_kernel_max_k(qg):
     """The largest K of whole 128-value stages under the int4 bound, with
     operands at the ends of their ranges, so that the x16 widened sums sit at
