@@ -568,17 +568,21 @@ def summarize_trace(stats_csv, title, cmd):
 def summarize_pmc(name, fetch_dir, write_dir, copy_bytes=1 << 30):
     """One traffic line for `name` from two rocprofv3 --pmc runs of
     `bench.py --config name` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
-    Every dispatch that is not a copy kernel belongs to the workload; the
+    The dispatches of the workload's kernel (KERNEL_NAMES) are averaged; the
     1 GiB device copy of hbm_copy_gbs() in the same run calibrates the
     counter (factor = known bytes / what the counter reads for that copy)."""
     out = {}
+    kn = KERNEL_NAMES[name]
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         work, copies = [], []
         for r in _csv_rows(d):
             if r.get("Counter_Name") != counter:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
-            (copies if "copy" in r["Kernel_Name"].lower() else work).append(v)
+            if "copy" in r["Kernel_Name"].lower():
+                copies.append(v)
+            elif kn in r["Kernel_Name"]:
+                work.append(v)
         if not work or not copies:
             raise SystemExit(f"no {counter} rows for the workload or the copy kernel in {d}")
         calib = copy_bytes / max(copies)
@@ -601,8 +605,8 @@ LABELS = {"pointwise": "pointwise s8s8 320x64x64", "s4s4": "s4s4 4096^3 -> i32",
 
 
 # kernel of each workload, as it appears in a rocprofv3 kernel name
-KERNEL_NAMES = {"s8s8": "k_gemm_dma<8, 0>", "s8s8_zp": "k_gemm_dma<8, 2>",
-                "w4a8_prefill": "k_gemm_dma<3, 0>", "s4s4": "k_gemm_dma<4, 1>",
+KERNEL_NAMES = {"s8s8": "k_gemm_dma<8, 0,", "s8s8_zp": "k_gemm_dma<8, 2,",
+                "w4a8_prefill": "k_gemm_dma<3, 0,", "s4s4": "k_gemm_dma<4, 1,",
                 "conv3x3": "k_conv_halo<3, 3, false>", "conv3x3_zp": "k_conv_halo<3, 3, true>",
                 "w4a8": "k_skinny_w4a8", "w4a8_m64": "k_skinny_w4a8",
                 "dw3x3": "k_dwconv3x3<1, false>", "quant_a8": "k_quant", "pointwise": "k_tile"}

@@ -79,17 +79,24 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #ifndef QG_DMA_PAIR_FIRST
 #define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
 #endif
+// waves per workgroup: int4 x int4 runs fastest with 8, the other operand
+// kinds with 4 (measured)
 #ifndef QG_DMA_WAVES
 #define QG_DMA_WAVES 4
 #endif
-// waves per workgroup, 2 along M x kWaves/2 along N; every wave owns 128
+#ifndef QG_DMA_WAVES_S4
+#define QG_DMA_WAVES_S4 8
+#endif
+// NW waves per workgroup, 2 along M x NW/2 along N; every wave owns 128
 // rows and kTN columns of the tile and loads kRPW of its A and B rows
-constexpr int kWaves = QG_DMA_WAVES;
-static_assert(kWaves == 4 || kWaves == 8, "2x2 or 2x4 waves");
-constexpr int kWN = kWaves / 2;
-constexpr int kTN = kBN / kWN;                 // 128 or 64
-constexpr int kNBJ = kTN / 16;                 // 16-column tiles per wave
-constexpr int kRPW = kBM / kWaves;             // rows per wave per operand per stage
+template <int NW>
+struct Waves {
+    static_assert(NW == 4 || NW == 8, "2x2 or 2x4 waves");
+    static constexpr int kWN = NW / 2;
+    static constexpr int kTN = kBN / kWN;      // 128 or 64
+    static constexpr int kNBJ = kTN / 16;      // 16-column tiles per wave
+    static constexpr int kRPW = kBM / NW;      // rows per wave per operand per stage
+};
 #ifndef QG_DMA_GROUP_M
 #define QG_DMA_GROUP_M 4
 #endif
@@ -103,8 +110,10 @@ enum { OP_S8 = 8, OP_S4 = 4, OP_MIX = 3, OP_MIXM = 5 };
 // loads per wave per stage.  A stage always covers 64 bytes of each B row;
 // with int8 A facing int4 B that is 128 K values, so A rows take 128 bytes
 // and the ring drops to three 48 KB stages.
-template <int KIND>
+template <int KIND, int NW>
 struct Geo {
+    static constexpr int kRPW = Waves<NW>::kRPW;
+    static constexpr int kNBJ = Waves<NW>::kNBJ;
     static constexpr bool kMix = KIND == OP_MIX || KIND == OP_MIXM;
     static constexpr int kRowA = kMix ? 128 : kRowB;
     static constexpr int kStageA = kBM * kRowA;
@@ -194,10 +203,13 @@ __device__ __forceinline__ void dma_dword(const void *src, void *dst)
     __builtin_amdgcn_global_load_lds((const glb_void_t *)src, (lds_void_t *)dst, 4, 0, 0);
 }
 
-template <int KIND, int EPI, bool PAIRS>
-__global__ __launch_bounds__(kWaves * 64, 1) void k_gemm_dma(DmaArgs p)
+template <int KIND, int EPI, bool PAIRS, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
 {
-    using G = Geo<KIND>;
+    using G = Geo<KIND, NW>;
+    constexpr int kWaves = NW;
+    constexpr int kWN = Waves<NW>::kWN, kTN = Waves<NW>::kTN;
+    constexpr int kNBJ = Waves<NW>::kNBJ, kRPW = Waves<NW>::kRPW;
     constexpr bool MIX = G::kMix;
     static_assert(!(PAIRS && MIX), "paired stages take 64-byte rows of both operands");
     // paired stages: slot of two stages, 128-byte rows, kLP loads per wave
@@ -875,12 +887,13 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     const int grid = ntiles < d.cus ? ntiles : d.cus;
     // paired stages for int8 and int4 operands whenever the stages pair up
     // (the ring then holds this tile's pair and the next one: >= 2 pairs)
-    constexpr bool kCanPair = !Geo<KIND>::kMix && QG_DMA_PAIRS;
+    constexpr int NW = KIND == OP_S4 ? QG_DMA_WAVES_S4 : QG_DMA_WAVES;
+    constexpr bool kCanPair = !Geo<KIND, NW>::kMix && QG_DMA_PAIRS;
     const int64_t nkt = (KIND == OP_S8 ? d.K : d.K / 2) / kRowB;
     if (kCanPair && nkt % 2 == 0 && nkt >= 4)
-        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, kCanPair>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, kCanPair, NW>), dim3(grid), dim3(NW * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, false>), dim3(grid), dim3(kWaves * 64), 0, s, a);
+        hipLaunchKernelGGL((k_gemm_dma<KIND, EPI, false, NW>), dim3(grid), dim3(NW * 64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -893,7 +906,7 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
 bool dma_gemm_fits(const GemmDesc &d, bool int4)
 {
     const int64_t kb = int4 ? d.K / 2 : d.K;
-    if (kb % kRowB != 0 || kb / kRowB < (int4 ? Geo<OP_S4>::kStages : Geo<OP_S8>::kStages))
+    if (kb % kRowB != 0 || kb / kRowB < (int4 ? Geo<OP_S4, QG_DMA_WAVES_S4>::kStages : Geo<OP_S8, QG_DMA_WAVES>::kStages))
         return false;
     if (d.M < kBM || d.N < kBN)
         return false;
@@ -929,7 +942,7 @@ hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
 // least one whole tile each way, and operands of under 4 GiB
 bool dma_w4a8_fits(const GemmDesc &d)
 {
-    if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX>::kStages)
+    if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX, QG_DMA_WAVES>::kStages)
         return false;
     if (d.M < kBM || d.N < kBN)
         return false;

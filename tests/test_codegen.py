@@ -66,8 +66,9 @@ def test_main_loop_shape(asm):
         assert sum("s_barrier" in ln for ln in loop) == 1, name
         # operand kind: 8 int8 x int8, 4 int4 x int4, 3 / 5 int8 x int4;
         # pairs: one loop iteration multiplies two 64-byte K stages
-        kind = int(re.search(r"k_gemm_dmaILi(\d)E", name).group(1))
-        pairs = re.search(r"k_gemm_dmaILi\dELi\dELb1E", name) is not None
+        kind, epi, pairs, nw = re.search(r"k_gemm_dmaILi(\d)ELi(\d)ELb(\d)ELi(\d)E", name).groups()
+        kind, pairs, nw = int(kind), pairs == "1", int(nw)
+        rows = 256 // nw  # A and B rows each wave loads per stage
         vm = [w for w in waits if "vmcnt" in w]
         if pairs:
             # the pair's loads are waited for once, at its barrier
@@ -75,7 +76,8 @@ def test_main_loop_shape(asm):
         else:
             # the ring keeps the later stages' loads in flight at the barrier
             assert not any(re.search(r"vmcnt\(0\)", w) for w in waits), (name, waits)
-        loads = 16 if pairs else 12 if kind in (3, 5) else 8
+        row_a = 128 if kind in (3, 5) else 64
+        loads = 2 * rows * 128 // 1024 if pairs else rows * (row_a + 64) // 1024
         assert sum(re.search(r"buffer_load_dwordx4 .* offen lds", ln) is not None
                    for ln in loop) == loads, name
         # no per-lane address arithmetic for the loads: the loop's only
@@ -83,7 +85,9 @@ def test_main_loop_shape(asm):
         assert not any(ln.startswith(("v_lshl_add_u64", "v_add_co_u32")) for ln in loop), name
         # a stage is 8x8 tiles of 16x16x64 per wave: 64 MFMAs for int8, two
         # K steps (128) when a 64-byte fragment row holds packed int4
-        per_stage = 64 if kind == 8 else 128
+        # a wave owns 128 x (512 / nw) outputs: 8 x (32 / nw) tiles, one
+        # MFMA each per K step, one step per stage for int8, two for int4
+        per_stage = 8 * (32 // nw) * (1 if kind == 8 else 2)
         assert sum("v_mfma_i32_16x16x64_i8" in ln for ln in loop) == per_stage * (2 if pairs else 1), name
         assert not any("v_mfma_i32_32x32" in ln for ln in loop), name
         # every MFMA accumulates in place: no accumulator copies in the loop
