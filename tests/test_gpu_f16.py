@@ -35,7 +35,7 @@ def _scales(g, n):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (7, 5, 64), (33, 17, 96), (129, 65, 288),
-                                   (300, 260, 512), (4096, 4096, 4096)])
+                                   (300, 260, 512), (2048, 4096, 640), (4096, 4096, 4096)])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_s4s4_f16(qg, orc, M, N, K, scaled):
     print("s4s4 f16", M, N, K, scaled, flush=True)
@@ -45,7 +45,12 @@ def test_s4s4_f16(qg, orc, M, N, K, scaled):
     sb = _scales(g, N) if scaled else None
     C = qg.qgemm_s4s4_f16(dev(d["A"]), dev(d["B"]), None if sa is None else dev(sa),
                           None if sb is None else dev(sb))
-    rows = None if M <= 512 else np.array([0, 1, 255, 256, 2049, 4095])
+    # large shapes take the ring kernel (K = 640: five 64-byte stages, one at
+    # a time; K = 4096: paired stages): 64 rows, every offset inside a 16-row
+    # block and both row halves of a 256-row tile, the last row included
+    rows = None if M <= 512 else np.unique(np.concatenate([
+        np.arange(16) * 17 % 256 + 256 * np.arange(16) % M,
+        np.random.default_rng(K).integers(0, M, 47), [M - 1]]))
     want = orc.gemm_s4s4_f16(d["A"], d["B"], sa, sb, rows=rows)
     got = C.cpu().numpy()
     got = got if rows is None else got[rows]
