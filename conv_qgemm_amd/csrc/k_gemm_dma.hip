@@ -76,6 +76,9 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #ifndef QG_DMA_PAIRS
 #define QG_DMA_PAIRS 1                        // paired stages for int8 / int4 operands
 #endif
+#ifndef QG_DMA_PAIR_EARLY
+#define QG_DMA_PAIR_EARLY 1                   // 4-wave pairs: a second barrier, the next pair's loads earlier
+#endif
 #ifndef QG_DMA_PAIR_FIRST
 #define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
 #endif
@@ -221,6 +224,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
     constexpr int kLP = 2 * kRPW * kRowP / 1024;
     constexpr int kLP1 = kLP * QG_DMA_PAIR_FIRST / 4;
     static_assert(!PAIRS || 2 * kPair == G::kStages * G::kStage, "same LDS ring");
+    // paired stages, early form: a second barrier in the middle of a pair's
+    // second stage frees its slot for the pair after next, whose loads then
+    // have two and a half stages to land instead of two.  Four waves gain
+    // (their barrier waits were the longer); with eight, the int4 kind, the
+    // extra barrier costs more than the earlier loads save.
+    constexpr bool kPairEarly = PAIRS && QG_DMA_PAIR_EARLY && NW == 4;
     constexpr bool MSB = KIND == OP_MIXM;
     constexpr int kStages = G::kStages;
     constexpr int kStage = G::kStage;
@@ -524,7 +533,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
     //      whole stages when it is waited for ----
     if constexpr (RQ || F16)
         load_prm(0, m0, n0);
-    if constexpr (PAIRS) {
+    if constexpr (kPairEarly) {
+        // pairs 0 and 1 in slots 0 and 1; pair j+2 streams in from the
+        // middle of pair j's second stage
+#pragma unroll
+        for (int l = 0; l < kLP; ++l)
+            issue_pair(0, 0, l);
+#pragma unroll
+        for (int l = 0; l < kLP; ++l)
+            issue_pair(1, 1, l);
+        wait_loads_and_barrier<kLP>();
+    } else if constexpr (PAIRS) {
         // paired stages: pair 0 in slot 0; pair 1 follows during pair 0
 #pragma unroll
         for (int l = 0; l < kLP; ++l)
@@ -579,11 +598,69 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
         for (int t = 0; t < 8 * kNBJ; ++t)
             acc[t] = (v4i){0, 0, 0, 0};
         // paired stages: pair j multiplies from slot rs while pair j+1
-        // streams into the other slot (freed at the last barrier); one
-        // barrier per pair, after which pair j+1 has landed for every wave
-        // and no wave reads pair j any more.  The last pair issues the next
-        // tile's first.
-        if constexpr (PAIRS) {
+        // lands in the other slot; pairs past the tile's last are the next
+        // tile's first
+        if constexpr (kPairEarly) {
+            // two barriers per pair: once every wave has read its last
+            // fragments of pair j (the middle of stage 2j+1), pair j+2
+            // streams into slot rs; the pair's last barrier waits for pair
+            // j+1 with pair j+2 still in flight
+            for (int j = 0; j < nkt / 2; ++j) {
+                const int ns = rs ^ 1;
+                // stage 2j
+                read_group(rs, 1, fa[1], fb[1], 0);
+                mma_quad(fa[0], fb[0], 0, 0);
+                mma_quad(fa[0], fb[1], 0, 1);
+                mma_quad(fa[1], fb[0], 1, 0);
+                pre_hints.template operator()<0>();
+                __builtin_amdgcn_sched_barrier(0);
+                read_group(rs, 0, fa[0], fb[0], 1);
+                mma_quad(fa[1], fb[1], 1, 1);
+                post_hints();
+                __builtin_amdgcn_sched_barrier(0);
+                // stage 2j + 1
+                read_group(rs, 1, fa[1], fb[1], 1);
+                mma_quad(fa[0], fb[0], 0, 0);
+#pragma unroll
+                for (int i = 0; i < DSG; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MQ - DSG, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                // this wave's reads of slot rs are back; after the barrier,
+                // every wave's
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int l = 0; l < kLP; ++l)
+                    issue_pair(j + 2, rs, l);
+                mma_quad(fa[0], fb[1], 0, 1);
+                mma_quad(fa[1], fb[0], 1, 0);
+                {
+                    constexpr int per = 2 * MQ / kLP;
+                    static_assert(per >= 1, "stage schedule");
+#pragma unroll
+                    for (int i = 0; i < kLP; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+                        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MQ - per * kLP, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // all but pair j+2's loads have landed for this wave (a new
+                // tile's parameters are issued before its pair 2), pair
+                // j+1's among them; after the barrier, for every wave
+                wait_loads_and_barrier<kLP>();
+                __builtin_amdgcn_sched_barrier(0);
+                read_group(ns, 0, fa[0], fb[0], 0);
+                mma_quad(fa[1], fb[1], 1, 1);
+                post_hints();
+                rs = ns;
+            }
+        } else if constexpr (PAIRS) {
+            // one barrier per pair, after which pair j+1 has landed for
+            // every wave and no wave reads pair j any more
             for (int j = 0; j < nkt / 2; ++j) {
                 const int ns = rs ^ 1;
                 // stage 2j (first half of the slot)
