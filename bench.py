@@ -113,11 +113,40 @@ def ops_and_bytes(name):
     return 2 * macs, by
 
 
+def code_text(src):
+    """C++ source with its comments removed and each run of whitespace made
+    one space: what the compiler sees, so that a comment-only edit keeps the
+    counters taken on the kernel.  String and character literals are kept
+    whole (an asm string may hold '//')."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def src_sha(path):
+    """Fingerprint of a kernel's code (its source and the shared device
+    header, comments and layout aside)."""
     h = hashlib.sha256()
     for p in (path, "conv_qgemm_amd/csrc/dev_common.hpp"):
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,6 +38,15 @@
 //   * a stage's 8 loads are spread over two iterations (2 right after the
 //     barrier that frees their slot, 6 between the next iteration's MFMAs),
 //     so the four waves never queue 32 loads at once;
+//   * int8 x int8 and int4 x int4, when K gives an even number (>= 4) of
+//     stages, pair them instead: stages 2j and 2j+1 share one 64 KB slot of
+//     128-byte rows, each load fetches 8 whole 128-byte lines, and the ring
+//     is two such slots.  With 4 waves a second barrier, in the middle of a
+//     pair's second stage, frees the slot for the pair after next, whose
+//     loads then have two and a half stages to land; the int4 x int4 kernel
+//     (8 waves, 2x4, each 128x64) keeps one barrier per pair.  int8 A facing
+//     int4 B, whose A rows already take 128 bytes per stage, keeps a
+//     3-stage ring of single stages;
 //   * int4 operands are widened in registers (dev_common.hpp): a 16-byte
 //     fragment read of packed data covers two MFMA K steps;
 //   * the grid is one workgroup per compute unit, walking its tiles; the

@@ -97,3 +97,16 @@ def test_helper_libraries_export(lib, symbols):
     so = ctypes.CDLL(path)
     for s in symbols:
         assert hasattr(so, s), s
+
+
+def test_code_fingerprint_ignores_comments_only():
+    """The counters stay attached to a kernel through comment and layout
+    edits, and detach on any change of code, string literals included."""
+    src = 'int f(int x) {  // add one\n  return x + 1; /* done */ }\nconst char *s = "a // b";\n'
+    same = '/* header */\nint f(int x)\n{\n    return x + 1;\n}\nconst char *s = "a // b";  // literal\n'
+    assert bench.code_text(src) == bench.code_text(same)
+    for changed in (src.replace("x + 1", "x + 2"), src.replace('"a // b"', '"a // c"'),
+                    src.replace("return", "return -")):
+        assert bench.code_text(changed) != bench.code_text(src)
+    assert "add one" not in bench.code_text(src) and "// b" in bench.code_text(src)
+
