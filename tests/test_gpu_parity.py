@@ -454,6 +454,27 @@ def test_ring_kernel_stage_parity(qg, M, N, stages):
     assert np.array_equal(C4[rows], oracle.gemm_s4s4_i32(d4["A"], d4["B"], rows=rows))
 
 
+
+RING_SHORT_K_TILES = [(4096, 8192, 4), (4096, 8192, 5), (4000, 8200, 6)]
+
+
+@pytest.mark.parametrize("M,N,stages", RING_SHORT_K_TILES)
+def test_ring_kernel_short_k_several_tiles(qg, M, N, stages):
+    """512 and more 256x256 tiles, so that a workgroup walks two or three
+    of them: with 4 and 6 stages (2 and 3 pairs) the last pairs of a tile
+    load the next tile's first two, into slots that tile then multiplies
+    from; every output of s8s8 and of s4s4 compared."""
+    _say("ring short K, several tiles", M, N, stages)
+    K = 64 * stages
+    d = datagen.gemm_s8s8(M, N, K, seed=20 + stages, shift=(37, 43))
+    C = host(qg.qgemm_s8s8_requant(dev(d["A"]), dev(d["B"]), dev(d["bias"]), dev(d["mult"]),
+                                   dev(d["shift"])))
+    assert np.array_equal(C, oracle.gemm_s8s8_requant(d["A"], d["B"], d["bias"], d["mult"],
+                                                      d["shift"]))
+    d4 = datagen.gemm_s4s4(M, N, 128 * stages, seed=30 + stages)
+    C4 = host(qg.qgemm_s4s4_i32(dev(d4["A"]), dev(d4["B"])))
+    assert np.array_equal(C4, oracle.gemm_s4s4_i32(d4["A"], d4["B"]))
+
 def test_w4a8_ring_kernel_max_k(qg):
     """The largest K of whole 128-value stages under the int4 bound, with
     operands at the ends of their ranges, so that the x16 widened sums sit at
