@@ -20,7 +20,15 @@
 //     in 80 bytes (the slice's 64 channels + 16 unused) with columns and
 //     rows of the padding value (the input zero point, 0 when symmetric), so
 //     a tap is a fixed LDS offset and 16 consecutive pixels fall in 16
-//     different bank groups;
+//     different bank groups.  With stride 1 the LDS row holds a pixel count
+//     congruent to Wo mod 16, so that this stays true across a row end;
+//   * a 16-byte LDS read serves 16 lanes per cycle: lane rows 0 and 1 (and
+//     2 and 3) share cycles, each with 8 of the 16 pixels.  Their two taps
+//     then fall on 16 distinct bank groups when their LDS offsets differ by
+//     a multiple of 16 pixels.  With stride 1 and Wo a multiple of 8 the
+//     taps are placed so: kernel rows 0 and 2 pair up (two row pitches
+//     apart), and each tap of kernel row 1 shares its cycles with a
+//     zero-weight copy of itself;
 //   * the diagonal weight operands live in registers (12 per lane);
 //   * the requantize takes the cheapest exact form all 64 shifts of the
 //     slice allow; a 4 x 4 lane transpose (permlane swaps) gives each lane
@@ -56,7 +64,9 @@ struct DwArgs {
     int8_t *Y;
     int H, Wd, C, KH, KW, sh, sw, ph, pw, Ho, Wo;
     int tiles_per_img;
-    int in_bytes;  // LDS bytes of the staged input rows
+    int in_bytes;   // LDS bytes of the staged input rows
+    int colsL;      // LDS pixels per staged row (>= Wd + 2 pw)
+    int tap_pairs;  // taps placed in bank-conflict-free pairs (stride 1, Wo % 8 == 0)
     // asymmetric form: the padding byte x4 and the zero points; the 3x3 path
     // takes zb = 0 with `bias` holding bias - za * sum_t w[t][c]
     int pad4, a_zero, b_zero, out_zero;
@@ -98,8 +108,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     const int ih0 = oh_first * S - p.ph;  // input row of LDS row 0
     const int nrow_in = (oh_last - oh_first) * S + KH;
     const int ih_lo = max(ih0, 0), ih_hi = min(ih0 + nrow_in - 1, p.H - 1);
-    const int colsL = p.Wd + 2 * p.pw;
-    const int rowL = colsL * kPixL;
+    const int colsR = p.Wd + 2 * p.pw;  // staged columns, padding included
+    const int rowL = p.colsL * kPixL;
 
     // ---- per-channel parameters and this lane's weight bytes, loaded
     //      behind the input rows (issued first, the compiler waited for
@@ -108,6 +118,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     // Unconditional loads at clamped indices, the raw values kept untouched
     // until after the barrier (a load under a branch, or a value used at
     // once, makes the compiler wait for the input loads issued before it).
+    // K slot (slice s, lane row g) -> tap, and whether it carries the tap's
+    // weights or zeros.  Plain order: tap 4s + g, zeros past the ninth.
+    // Paired order (4 bits a slot): slice 0 taps 0 6 1 7, slice 1 2 8 3 3,
+    // slice 2 4 4 5 5, the second 3, 4 and 5 with zero weights.
+    constexpr int kPairTaps[kSlices] = {0x7160, 0x3382, 0x5544};
+    constexpr int kPairReal[kSlices] = {0xF, 0x7, 0x5};
+    const bool pairs = S == 1 && p.tap_pairs;
+    auto slot_tap = [&](int s) {
+        return pairs ? (kPairTaps[s] >> (4 * g)) & 15 : min(4 * s + g, KK - 1);
+    };
+    auto slot_real = [&](int s) { return pairs ? ((kPairReal[s] >> g) & 1) != 0 : 4 * s + g < KK; };
     int bv, mv, sv;
     int wb[kSlices][4];
     auto load_params = [&]() {
@@ -119,8 +140,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
         for (int s = 0; s < kSlices; ++s)
 #pragma unroll
             for (int n = 0; n < 4; ++n)
-                wb[s][n] = (uint8_t)p.W[(int64_t)min(4 * s + g, KK - 1) * p.C + c0 +
-                                        min(16 * n, cs - 16) + col];
+                wb[s][n] = (uint8_t)p.W[(int64_t)slot_tap(s) * p.C + c0 + min(16 * n, cs - 16) +
+                                        col];
     };
 
     // ---- input rows (the slice's channels) -> LDS, the padding value
@@ -140,8 +161,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
         *(v4i *)(IN + r * rowL + (iw + p.pw) * kPixL + 16 * q) = v;
     };
     auto pad_rows = [&]() {
-        for (int e = tid; e < nrow_in * colsL; e += kWaves * 64) {
-            const int r = e / colsL, c = e - r * colsL;
+        for (int e = tid; e < nrow_in * colsR; e += kWaves * 64) {
+            const int r = e / colsR, c = e - r * colsR;
             const int ih = ih0 + r;
             if (ih < 0 || ih >= p.H || c < p.pw || c >= p.pw + p.Wd) {
                 v4i *z = (v4i *)(IN + r * rowL + c * kPixL);
@@ -195,16 +216,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     }
     __syncthreads();
 
-    // ---- diagonal weight operands: slice s (taps 4s..4s+3), group n; the
-    //      lane (column col = output channel 16n + col, K group g = tap
-    //      4s + g) holds w[4s + g][c0 + 16n + col] at byte col of 16 ----
+    // ---- diagonal weight operands: slice s, group n; the lane (column
+    //      col = output channel 16n + col, K group g = tap t of slot (s, g))
+    //      holds w[t][c0 + 16n + col] at byte col of 16, or 0 ----
     v4i wd[kSlices][4];
 #pragma unroll
     for (int s = 0; s < kSlices; ++s)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             v4i v = {0, 0, 0, 0};
-            const int w = 4 * s + g < KK && 16 * n < cs ? wb[s][n] : 0;
+            const int w = slot_real(s) && 16 * n < cs ? wb[s][n] : 0;
 #pragma unroll
             for (int d = 0; d < 4; ++d)
                 v[d] = (col >> 2) == d ? (w << (8 * (col & 3))) : 0;
@@ -225,7 +246,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     int toff[kSlices];
 #pragma unroll
     for (int s = 0; s < kSlices; ++s) {
-        const int t = 4 * s + g < KK ? 4 * s + g : 0;  // taps past the last have zero weights
+        const int t = slot_tap(s);
         toff[s] = (t / KW) * rowL + (t % KW) * kPixL;
     }
 
@@ -353,20 +374,35 @@ __global__ __launch_bounds__(256) void k_dwconv_direct(DwArgs p, int64_t nitems)
     *(unsigned *)(p.Y + pix * p.C + c) = pack4_i8(y[0], y[1], y[2], y[3]);
 }
 
-// LDS bytes of the staged input rows for a 3x3 conv with stride S: the
-// output rows a tile of kTP consecutive pixels touches (never more than the
-// image has), times S, plus the halo; rounded to 1 KB.
-int64_t dw_in_bytes(const ConvDesc &d)
+// LDS bytes of the staged input rows for a 3x3 conv with stride S and
+// `cols` pixels per LDS row: the output rows a tile of kTP consecutive
+// pixels touches (never more than the image has), times S, plus the halo;
+// rounded to 1 KB.
+int64_t dw_in_bytes(const ConvDesc &d, int64_t cols)
 {
     const int64_t span = std::min<int64_t>((kTP - 1) / d.Wo + 1, d.Ho - 1);
     const int64_t rows = span * d.sh + d.KH;
-    int64_t in = rows * (d.Wd + 2 * d.pw) * kPixL;
+    int64_t in = rows * cols * kPixL;
     return (in + 1023) & ~(int64_t)1023;
+}
+
+// LDS pixels per staged row: the padded width, or with stride 1 the next
+// count congruent to Wo mod 16 (when that still fits), so that 16
+// consecutive output pixels take 16 bank groups across a row end too
+int64_t dw_cols(const ConvDesc &d)
+{
+    const int64_t base = d.Wd + 2 * d.pw;
+    if (d.sh == 1) {
+        const int64_t cols = base + (((d.Wo - base) % 16) + 16) % 16;
+        if (dw_in_bytes(d, cols) + 3 * kCS * 4 <= kMaxLds)
+            return cols;
+    }
+    return base;
 }
 
 int64_t dw_lds_bytes(const ConvDesc &d)
 {
-    return dw_in_bytes(d) + 3 * kCS * 4;
+    return dw_in_bytes(d, dw_cols(d)) + 3 * kCS * 4;
 }
 
 bool dw_mfma_fits(const ConvDesc &d)
@@ -439,7 +475,11 @@ hipError_t launch_dwconv_nhwc(const ConvDesc &d, hipStream_t s)
     }
     if (dw_takes_mfma(d)) {
         a.tiles_per_img = (d.Ho * d.Wo + kTP - 1) / kTP;
-        a.in_bytes = (int)dw_in_bytes(d);
+        a.colsL = (int)dw_cols(d);
+        a.in_bytes = (int)dw_in_bytes(d, a.colsL);
+        // the paired tap order needs taps two row pitches apart on one
+        // bank group: stride 1, a pitch congruent to Wo, and 2 Wo = 0 mod 16
+        a.tap_pairs = d.sh == 1 && d.Wo % 8 == 0 && (a.colsL - d.Wo) % 16 == 0;
         const int lds = (int)dw_lds_bytes(d);
         if (d.asym)
             return d.sh == 1 ? run_dw3x3<1, true>(a, d.batch, lds, s)

@@ -315,6 +315,11 @@ DW_GEOMS = [
     (2, 6, 11, 32, 1, 3, (1, 2), (0, 1)),     # direct kernel: 1x3, unequal strides
     (1, 9, 9, 48, 3, 3, (2, 1), (1, 1)),      # direct kernel: unequal strides
     (1, 3, 200, 16, 3, 3, (2, 2), (1, 1)),    # wide rows at stride 2
+    # stride 1, Wo a multiple of 8: LDS rows padded to Wo mod 16, paired taps
+    (1, 12, 8, 32, 3, 3, (1, 1), (1, 1)),     # Wo 8
+    (2, 30, 24, 64, 3, 3, (1, 1), (1, 1)),    # Wo 24, bands starting mid-row
+    (1, 12, 112, 64, 3, 3, (1, 1), (1, 1)),   # Wo 112: a band is 3.5 rows
+    (1, 14, 18, 32, 3, 3, (1, 1), (1, 0)),    # Wo 16 with no column padding
 ]
 
 

@@ -201,6 +201,7 @@ DW_GEOMS = [
     (1, 7, 7, 80, 3, 3, (1, 1), (1, 1)),
     (1, 9, 8, 16, 5, 5, (1, 1), (2, 2)),
     (2, 6, 9, 48, 3, 3, (1, 2), (1, 1)),
+    (2, 30, 24, 64, 3, 3, (1, 1), (1, 1)),  # Wo 24: paired taps, zero-point padding
 ]
 
 
