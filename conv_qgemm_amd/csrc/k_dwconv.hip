@@ -111,13 +111,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
     const int colsR = p.Wd + 2 * p.pw;  // staged columns, padding included
     const int rowL = p.colsL * kPixL;
 
-    // ---- per-channel parameters and this lane's weight bytes, loaded
-    //      behind the input rows (issued first, the compiler waited for
-    //      them before the input loads could go); the diagonal operands are
-    //      built from the bytes after the barrier ----
-    // Unconditional loads at clamped indices, the raw values kept untouched
-    // until after the barrier (a load under a branch, or a value used at
-    // once, makes the compiler wait for the input loads issued before it).
     // K slot (slice s, lane row g) -> tap, and whether it carries the tap's
     // weights or zeros.  Plain order: tap 4s + g, zeros past the ninth.
     // Paired order (4 bits a slot): slice 0 taps 0 6 1 7, slice 1 2 8 3 3,
@@ -129,6 +122,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void k_dwconv3x3(DwArgs p)
         return pairs ? (kPairTaps[s] >> (4 * g)) & 15 : min(4 * s + g, KK - 1);
     };
     auto slot_real = [&](int s) { return pairs ? ((kPairReal[s] >> g) & 1) != 0 : 4 * s + g < KK; };
+
+    // ---- per-channel parameters and this lane's weight bytes, loaded
+    //      behind the input rows (issued first, the compiler waited for
+    //      them before the input loads could go); the diagonal operands are
+    //      built from the bytes after the barrier ----
+    // Unconditional loads at clamped indices, the raw values kept untouched
+    // until after the barrier (a load under a branch, or a value used at
+    // once, makes the compiler wait for the input loads issued before it).
     int bv, mv, sv;
     int wb[kSlices][4];
     auto load_params = [&]() {
