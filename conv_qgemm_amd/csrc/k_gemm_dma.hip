@@ -42,8 +42,11 @@
 //     stages, pair them instead: stages 2j and 2j+1 share one 64 KB slot of
 //     128-byte rows, each load fetches 8 whole 128-byte lines, and the ring
 //     is two such slots.  With 4 waves a second barrier, in the middle of a
-//     pair's second stage, frees the slot for the pair after next, whose
-//     loads then have two and a half stages to land; the int4 x int4 kernel
+//     pair's second stage, frees the slot for the pair after next: half of
+//     that pair's loads go out there (two and a half stages to land), the
+//     other half in the next pair's first stage, so that the four waves'
+//     loads, issued at the same points of the same schedule, never queue
+//     all at once at the CU's address unit; the int4 x int4 kernel
 //     (8 waves, 2x4, each 128x64) keeps one barrier per pair.  int8 A facing
 //     int4 B, whose A rows already take 128 bytes per stage, keeps a
 //     3-stage ring of single stages;
@@ -87,6 +90,9 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #endif
 #ifndef QG_DMA_PAIR_EARLY
 #define QG_DMA_PAIR_EARLY 1                   // 4-wave pairs: a second barrier, the next pair's loads earlier
+#endif
+#ifndef QG_DMA_PAIR_DEFER
+#define QG_DMA_PAIR_DEFER 8                   // early form: a pair's loads issued in the stage after the rest
 #endif
 #ifndef QG_DMA_PAIR_FIRST
 #define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
@@ -239,6 +245,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
     // (their barrier waits were the longer); with eight, the int4 kind, the
     // extra barrier costs more than the earlier loads save.
     constexpr bool kPairEarly = PAIRS && QG_DMA_PAIR_EARLY && NW == 4;
+    // early form: the first kEarly of pair j+2's loads go out after the
+    // middle barrier of pair j, the other kDefer in the first stage of pair
+    // j+1, so that the four waves' loads do not all queue in one window
+    constexpr int kDefer = kPairEarly ? QG_DMA_PAIR_DEFER : 0;
+    constexpr int kEarly = kLP - kDefer;
+    static_assert(kDefer >= 0 && kEarly >= 1, "pair load split");
     constexpr bool MSB = KIND == OP_MIXM;
     constexpr int kStages = G::kStages;
     constexpr int kStage = G::kStage;
@@ -549,9 +561,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
         for (int l = 0; l < kLP; ++l)
             issue_pair(0, 0, l);
 #pragma unroll
-        for (int l = 0; l < kLP; ++l)
+        for (int l = 0; l < kEarly; ++l)
             issue_pair(1, 1, l);
-        wait_loads_and_barrier<kLP>();
+        wait_loads_and_barrier<kEarly>();
     } else if constexpr (PAIRS) {
         // paired stages: pair 0 in slot 0; pair 1 follows during pair 0
 #pragma unroll
@@ -616,12 +628,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
             // j+1 with pair j+2 still in flight
             for (int j = 0; j < nkt / 2; ++j) {
                 const int ns = rs ^ 1;
-                // stage 2j
+                // stage 2j; the deferred loads of pair j+1 (slot ns has had
+                // no reader since the middle of pair j-1)
                 read_group(rs, 1, fa[1], fb[1], 0);
+#pragma unroll
+                for (int l = kEarly; l < kLP; ++l)
+                    issue_pair(j + 1, ns, l);
                 mma_quad(fa[0], fb[0], 0, 0);
                 mma_quad(fa[0], fb[1], 0, 1);
                 mma_quad(fa[1], fb[0], 1, 0);
-                pre_hints.template operator()<0>();
+                pre_hints.template operator()<kDefer>();
                 __builtin_amdgcn_sched_barrier(0);
                 read_group(rs, 0, fa[0], fb[0], 1);
                 mma_quad(fa[1], fb[1], 1, 1);
@@ -642,25 +658,26 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int l = 0; l < kLP; ++l)
+                for (int l = 0; l < kEarly; ++l)
                     issue_pair(j + 2, rs, l);
                 mma_quad(fa[0], fb[1], 0, 1);
                 mma_quad(fa[1], fb[0], 1, 0);
                 {
-                    constexpr int per = 2 * MQ / kLP;
+                    constexpr int per = 2 * MQ / kEarly;
                     static_assert(per >= 1, "stage schedule");
 #pragma unroll
-                    for (int i = 0; i < kLP; ++i) {
+                    for (int i = 0; i < kEarly; ++i) {
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
                         __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MQ - per * kLP, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MQ - per * kEarly, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // all but pair j+2's loads have landed for this wave (a new
-                // tile's parameters are issued before its pair 2), pair
-                // j+1's among them; after the barrier, for every wave
-                wait_loads_and_barrier<kLP>();
+                // all but pair j+2's first kEarly loads have landed for this
+                // wave (a new tile's parameters are issued before its pair
+                // 2), pair j+1's among them; after the barrier, for every
+                // wave
+                wait_loads_and_barrier<kEarly>();
                 __builtin_amdgcn_sched_barrier(0);
                 read_group(ns, 0, fa[0], fb[0], 0);
                 mma_quad(fa[1], fb[1], 1, 1);
