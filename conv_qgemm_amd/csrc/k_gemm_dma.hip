@@ -92,7 +92,10 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #define QG_DMA_PAIR_EARLY 1                   // 4-wave pairs: a second barrier, the next pair's loads earlier
 #endif
 #ifndef QG_DMA_PAIR_DEFER
-#define QG_DMA_PAIR_DEFER 8                   // early form: a pair's loads issued in the stage after the rest
+#define QG_DMA_PAIR_DEFER 2                   // early form: quarters of a pair's loads issued in the stage after the rest
+#endif
+#ifndef QG_DMA_PAIR_EARLY_WAVES
+#define QG_DMA_PAIR_EARLY_WAVES 4             // early form up to this many waves per workgroup
 #endif
 #ifndef QG_DMA_PAIR_FIRST
 #define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
@@ -244,11 +247,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
     // have two and a half stages to land instead of two.  Four waves gain
     // (their barrier waits were the longer); with eight, the int4 kind, the
     // extra barrier costs more than the earlier loads save.
-    constexpr bool kPairEarly = PAIRS && QG_DMA_PAIR_EARLY && NW == 4;
+    constexpr bool kPairEarly = PAIRS && QG_DMA_PAIR_EARLY && NW <= QG_DMA_PAIR_EARLY_WAVES;
     // early form: the first kEarly of pair j+2's loads go out after the
     // middle barrier of pair j, the other kDefer in the first stage of pair
     // j+1, so that the four waves' loads do not all queue in one window
-    constexpr int kDefer = kPairEarly ? QG_DMA_PAIR_DEFER : 0;
+    constexpr int kDefer = kPairEarly ? kLP * QG_DMA_PAIR_DEFER / 4 : 0;
     constexpr int kEarly = kLP - kDefer;
     static_assert(kDefer >= 0 && kEarly >= 1, "pair load split");
     constexpr bool MSB = KIND == OP_MIXM;
