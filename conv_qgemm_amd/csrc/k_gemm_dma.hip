@@ -11,8 +11,9 @@
 // next block's transfer with the current block's compute through ping-pong
 // buffers; here the same idea runs as a 4-deep ring in LDS.
 //
-// Per workgroup (4 waves, 2x2, each owning 128x128 = 8x8 tiles of
-// v_mfma_i32_16x16x64_i8, 256 accumulators): the 16x16x64 shape, not
+// Per workgroup (int8 x int8: 4 waves, 2x2, each owning 128x128 = 8x8 tiles
+// of v_mfma_i32_16x16x64_i8, 256 accumulators; the int4 kinds: 8 waves, 2x4,
+// each owning 128x64): the 16x16x64 shape, not
 // 32x32x32, because under the board's power limit a stream of it runs at a
 // higher engine clock (measured: 4.08 against 3.38 POP/s, 2045 against
 // 1700 MHz, on random operands with the same 256 accumulators);
@@ -100,10 +101,13 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #ifndef QG_DMA_PAIR_FIRST
 #define QG_DMA_PAIR_FIRST 4                   // quarters of a pair's loads issued in its first stage
 #endif
-// waves per workgroup: int4 x int4 runs fastest with 8, the other operand
-// kinds with 4 (measured)
+// waves per workgroup: int4 x int4 and int8 x int4 run fastest with 8,
+// int8 x int8 with 4 (measured)
 #ifndef QG_DMA_WAVES
 #define QG_DMA_WAVES 4
+#endif
+#ifndef QG_DMA_WAVES_MIX
+#define QG_DMA_WAVES_MIX 8
 #endif
 #ifndef QG_DMA_WAVES_S4
 #define QG_DMA_WAVES_S4 8
@@ -993,7 +997,9 @@ hipError_t run(const GemmDesc &d, hipStream_t s)
     const int grid = ntiles < d.cus ? ntiles : d.cus;
     // paired stages for int8 and int4 operands whenever the stages pair up
     // (the ring then holds this tile's pair and the next one: >= 2 pairs)
-    constexpr int NW = KIND == OP_S4 ? QG_DMA_WAVES_S4 : QG_DMA_WAVES;
+    constexpr int NW = KIND == OP_S4 ? QG_DMA_WAVES_S4
+                       : (KIND == OP_MIX || KIND == OP_MIXM) ? QG_DMA_WAVES_MIX
+                                                               : QG_DMA_WAVES;
     constexpr bool kCanPair = !Geo<KIND, NW>::kMix && QG_DMA_PAIRS;
     const int64_t nkt = (KIND == OP_S8 ? d.K : d.K / 2) / kRowB;
     if (kCanPair && nkt % 2 == 0 && nkt >= 4)
@@ -1048,7 +1054,7 @@ hipError_t launch_s4s4_f16_dma(const GemmDesc &d, hipStream_t s)
 // least one whole tile each way, and operands of under 4 GiB
 bool dma_w4a8_fits(const GemmDesc &d)
 {
-    if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX, QG_DMA_WAVES>::kStages)
+    if (d.K % 128 != 0 || d.K / 128 < Geo<OP_MIX, QG_DMA_WAVES_MIX>::kStages)
         return false;
     if (d.M < kBM || d.N < kBN)
         return false;
