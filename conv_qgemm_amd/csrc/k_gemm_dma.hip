@@ -51,8 +51,11 @@
 //     (8 waves, 2x4, each 128x64) keeps one barrier per pair.  int8 A facing
 //     int4 B, whose A rows already take 128 bytes per stage, keeps a
 //     3-stage ring of single stages;
-//   * int4 operands are widened in registers (dev_common.hpp): a 16-byte
-//     fragment read of packed data covers two MFMA K steps;
+//   * int4 operands are widened in registers: a 16-byte fragment read of
+//     packed data covers two MFMA K steps.  int4 x int4 widens both sides
+//     into the same even/odd order (dev_common.hpp); int8 A facing int4 B
+//     widens B into natural order, whose 8-wave layout (each wave 128 rows
+//     x 64 columns) reads twice as many A fragments as B ones;
 //   * the grid is one workgroup per compute unit, walking its tiles; the
 //     ring runs across tile boundaries (a tile's last stages issue the next
 //     tile's first), and per-tile parameters come in by direct-to-LDS loads
@@ -109,6 +112,9 @@ constexpr int kEarlyLoads = 2;                // issued right after the barrier
 #ifndef QG_DMA_WAVES_MIX
 #define QG_DMA_WAVES_MIX 8
 #endif
+#ifndef QG_DMA_MIX_NATURAL
+#define QG_DMA_MIX_NATURAL 1                  // int8 x int4: widen B into A's natural byte order
+#endif
 #ifndef QG_DMA_WAVES_S4
 #define QG_DMA_WAVES_S4 8
 #endif
@@ -126,6 +132,27 @@ struct Waves {
 #define QG_DMA_GROUP_M 4
 #endif
 constexpr int kGroupM = QG_DMA_GROUP_M;      // tile rows that share B panels in L2
+
+// 8 packed bytes (16 int4 values) -> 16 int8 bytes in natural order, each
+// value scaled by 16 (dev_common.hpp's widen_int4_x16 gives the even/odd
+// order): the low and high nibbles are masked in place as there, then
+// interleaved by v_perm_b32, 5 instructions per packed dword against 3, and
+// the int8 operand needs no permutation.  MSB: packed high nibble first, so
+// the even elements are the high nibbles.
+template <bool MSB>
+__device__ __forceinline__ v4i widen_int4_x16_natural(v2u p)
+{
+    const unsigned lx = (p.x << 4) & 0xF0F0F0F0u, hx = p.x & 0xF0F0F0F0u;
+    const unsigned ly = (p.y << 4) & 0xF0F0F0F0u, hy = p.y & 0xF0F0F0F0u;
+    const unsigned ex = MSB ? hx : lx, ox = MSB ? lx : hx;
+    const unsigned ey = MSB ? hy : ly, oy = MSB ? ly : hy;
+    v4i r;
+    r[0] = (int)__builtin_amdgcn_perm(ox, ex, 0x05010400u);
+    r[1] = (int)__builtin_amdgcn_perm(ox, ex, 0x07030602u);
+    r[2] = (int)__builtin_amdgcn_perm(oy, ey, 0x05010400u);
+    r[3] = (int)__builtin_amdgcn_perm(oy, ey, 0x07030602u);
+    return r;
+}
 
 // OP_MIX: int8 A x packed int4 B (W4A8); OP_MIXM: the same with B packed
 // high nibble first
@@ -521,12 +548,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
 #pragma unroll
         for (int h = 0; h < STEPS_PER_READ; ++h) {
             // int8 A facing int4 B: K step h of this group is A fragment
-            // [4h + i], byte-permuted to the widened-int4 order once
+            // [4h + i], byte-permuted to the widened-int4 order once (or
+            // taken as it is, with B widened into natural order)
             v4i as[MIX ? 4 : 1];
             if constexpr (MIX) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
-                    as[ii] = even_odd_split<MSB>(ra[4 * h + ii]);
+                    as[ii] = QG_DMA_MIX_NATURAL ? ra[4 * h + ii] : even_odd_split<MSB>(ra[4 * h + ii]);
             }
 #pragma unroll
             for (int jj = 0; jj < NB; ++jj) {
@@ -535,7 +563,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_dma(DmaArgs p)
                     bq = rb[jj];
                 } else {
                     v2u w = {(unsigned)rb[jj][2 * h], (unsigned)rb[jj][2 * h + 1]};
-                    bq = widen_int4_x16(w);
+                    if constexpr (MIX && QG_DMA_MIX_NATURAL)
+                        bq = widen_int4_x16_natural<MSB>(w);
+                    else
+                        bq = widen_int4_x16(w);
                 }
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
