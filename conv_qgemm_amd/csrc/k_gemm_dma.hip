@@ -88,7 +88,10 @@ constexpr int kStageA = kBM * kRowB;          // 16 KB
 constexpr int kStageB = kBN * kRowB;          // 16 KB
 constexpr int kStage = kStageA + kStageB;     // 32 KB
 constexpr int kLoadsPerStage = 8;             // per wave: 4 for A, 4 for B
-constexpr int kEarlyLoads = 2;                // issued right after the barrier
+#ifndef QG_DMA_EARLY_LOADS
+#define QG_DMA_EARLY_LOADS 2
+#endif
+constexpr int kEarlyLoads = QG_DMA_EARLY_LOADS;  // issued right after the barrier
 #ifndef QG_DMA_PAIRS
 #define QG_DMA_PAIRS 1                        // paired stages for int8 / int4 operands
 #endif
