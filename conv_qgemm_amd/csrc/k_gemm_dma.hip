@@ -36,9 +36,10 @@
 //     and the next stage's group 0 lands in the registers that (0,1) and
 //     (1,0) freed, behind (1,1).  The barrier sits after this wave's loads
 //     of the next stage have landed (counted with vmcnt);
-//   * a stage's 8 loads are spread over two iterations (2 right after the
-//     barrier that frees their slot, 6 between the next iteration's MFMAs),
-//     so the four waves never queue 32 loads at once;
+//   * stage by stage, a wave's loads of a stage (8 for int8 x int8 on 4
+//     waves, 6 for int8 x int4 on 8) are spread over two iterations (2
+//     right after the barrier that frees their slot, the rest between the
+//     next iteration's MFMAs), so the waves never queue all of them at once;
 //   * int8 x int8 and int4 x int4, when K gives an even number (>= 4) of
 //     stages, pair them instead: stages 2j and 2j+1 share one 64 KB slot of
 //     128-byte rows, each load fetches 8 whole 128-byte lines, and the ring
